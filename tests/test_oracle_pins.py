@@ -1,0 +1,440 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: a worked
+example derived by hand from the score equation, closed forms, brute-force
+enumeration, the literal heaps, or special cases that reduce to a simpler
+object. A plausible mistake (a dropped term, a wrong sign, a wrong row or
+index, a transposed operand) fails at least one of them; the mutation tests at
+the end plant such mistakes in the oracle and check that they are caught.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import dartree_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_problem(seed, V=40, L=4, K=5, r=6, scale_u=1.0, A_zero=False, E_zero=False, U_zero=False, ties=False):
+    rng = np.random.default_rng(seed)
+    logits = rng.normal(0, 2, (L, V))
+    if ties:
+        logits = np.round(logits * 2) / 2
+    A = np.zeros((r, r)) if A_zero else rng.normal(0, 1 / math.sqrt(r), (r, r))
+    E = np.zeros((V, r)) if E_zero else rng.normal(0, 1, (V, r))
+    U = np.zeros((V, r)) if U_zero else rng.normal(0, scale_u / math.sqrt(r), (V, r))
+    h = rng.normal(0, 1, (L, r))
+    return logits, h, A, E, U
+
+
+def cands(logits, K):
+    L = logits.shape[0]
+    ids = np.empty((L, K), np.int64)
+    vals = np.empty((L, K))
+    for i in range(L):
+        ids[i], vals[i] = O.topk_candidates(logits[i], K)
+    return ids, vals
+
+
+# --------------------------------------------------------------------------
+# hand-worked example (score equation of the blog's section 3.1)
+# --------------------------------------------------------------------------
+def test_hand_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_tiny.json")))
+    logits = np.array(g["logits"])
+    r, V = g["r"], g["V"]
+    A = np.ones((r, r)) * 0.3
+    E = np.arange(V * r, dtype=float).reshape(V, r) * 0.1
+    U = np.zeros((V, r))
+    h = np.ones((g["L"], r))
+    res = O.round_one_request(logits, h, A, E, U, g["K"], g["W"], g["B"], g["beta"])
+    ex = g["expected"]
+    assert res.cand_ids.tolist() == ex["cand_ids"]
+    ln = math.log
+    l1 = [ln(3 / 4) - 0.5, ln(1 / 4) - 0.5]
+    l2 = [ln(3 / 4) + ln(4 / 5) - 1, ln(1 / 4) + ln(4 / 5) - 1]
+    assert [n.tok for n in res.levels[1]] == ex["level1"]["tok"]
+    assert np.allclose([n.sbeta for n in res.levels[1]], l1, atol=1e-12)
+    paths = [[res.levels[1][n.parent_slot].tok, n.tok] for n in res.levels[2]]
+    assert paths == ex["level2"]["path"]
+    assert np.allclose([n.sbeta for n in res.levels[2]], l2, atol=1e-12)
+    em = res.emitted
+    assert em.n_sel == ex["n_sel"]
+    assert em.tok[:3].tolist() == ex["tok"]
+    assert em.depth[:3].tolist() == ex["depth"]
+    assert em.parent[:3].tolist() == ex["parent"]
+    assert np.allclose(em.score[:3], [l1[0], l1[1], ln(3 / 4) + ln(4 / 5) - 1], atol=1e-12)
+    assert [int(x) for x in res.mask[:3, 0]] == ex["mask_rows"]
+
+
+# --------------------------------------------------------------------------
+# top-K: rank-count definition on tie-heavy rows
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(30))
+def test_topk_matches_rank_count(seed):
+    rng = np.random.default_rng(seed)
+    V = int(rng.integers(1, 60))
+    K = int(rng.integers(1, V + 1))
+    row = rng.integers(-3, 4, V).astype(float) * 0.5   # many exact ties
+    if seed % 5 == 0:
+        row[rng.integers(0, V, max(1, V // 4))] = -0.0
+    ids, vals = O.topk_candidates(row, K)
+    # element i is selected iff fewer than K elements beat it, where j beats
+    # i when row[j] > row[i] or (row[j] == row[i] and j < i)
+    rank = [sum(1 for j in range(V) if row[j] > row[i] or (row[j] == row[i] and j < i)) for i in range(V)]
+    expect = sorted(range(V), key=lambda i: rank[i])[:K]
+    assert ids.tolist() == expect
+    assert vals.tolist() == [row[i] for i in expect]
+    assert sorted(rank) == list(range(V))
+
+
+# --------------------------------------------------------------------------
+# log-softmax closed form
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(10))
+def test_log_softmax_closed_form(seed):
+    rng = np.random.default_rng(seed)
+    z = rng.normal(0, 5, int(rng.integers(1, 100)))
+    lq = O.log_softmax(z)
+    assert np.all(lq <= 0)
+    assert abs(np.sum(np.exp(lq)) - 1) < 1e-12
+    # differences of log q equal differences of z (q proportional to e^z)
+    assert np.allclose(lq - lq[0], z - z[0], atol=1e-12)
+    # two candidates: q = sigmoid(z0 - z1)
+    a, b = rng.normal(0, 3, 2)
+    lq2 = O.log_softmax(np.array([a, b]))
+    assert abs(lq2[0] - (-math.log1p(math.exp(b - a)))) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# head input projection and the state recursion
+# --------------------------------------------------------------------------
+def test_head_states_onehot_and_linearity():
+    rng = np.random.default_rng(3)
+    D, r = 9, 5
+    Pt = rng.normal(0, 1, (r, D))           # Pt[j][i] = P[i][j]
+    H = np.eye(D)
+    h = O.head_states(H, Pt)
+    # H = e_i gives row i of P, i.e. column i of Pt
+    assert np.array_equal(h, Pt.T)
+    H1, H2 = rng.normal(0, 1, (4, D)), rng.normal(0, 1, (4, D))
+    assert np.allclose(O.head_states(2 * H1 - 3 * H2, Pt), 2 * O.head_states(H1, Pt) - 3 * O.head_states(H2, Pt))
+
+
+def test_state_is_tanh_h_when_A_and_E_vanish():
+    logits, h, A, E, U = rand_problem(5, A_zero=True, E_zero=True)
+    ids, vals = cands(logits, 5)
+    levels = O.build_supertree(ids, vals, h, A, E, U, W=3, beta=-0.1)
+    L = logits.shape[0]
+    assert np.array_equal(levels[0][0].state, h[0])
+    for d in range(1, L):
+        for nd in levels[d]:
+            assert np.allclose(nd.state, np.tanh(h[d]), atol=0, rtol=0)
+    assert all(nd.state is None for nd in levels[L])
+
+
+def test_state_recursion_chain_explicit():
+    # W = 1 makes a single chain; its states follow s_d = tanh(A s_{d-1} + E[u_d] + h_d)
+    logits, h, A, E, U = rand_problem(8)
+    ids, vals = cands(logits, 5)
+    levels = O.build_supertree(ids, vals, h, A, E, U, W=1, beta=-0.2)
+    s = h[0]
+    for d in range(1, logits.shape[0]):
+        nd = levels[d][0]
+        s = np.tanh(A.dot(s) + E[nd.tok] + h[d])
+        assert np.allclose(nd.state, s, atol=1e-14)
+
+
+def test_U_zero_logq_is_base_softmax():
+    logits, h, A, E, U = rand_problem(11, U_zero=True)
+    K = 5
+    ids, vals = cands(logits, K)
+    levels = O.build_supertree(ids, vals, h, A, E, U, W=50, beta=0.0)
+    for nd in levels[1]:
+        k = list(ids[0]).index(nd.tok)
+        p = np.exp(vals[0]) / np.exp(vals[0]).sum()
+        assert abs(nd.cum - math.log(p[k])) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# U = 0: the beam is exact, so level d is the top-W of all K^d sequences
+# --------------------------------------------------------------------------
+def brute_force_levels(logits, K, W, beta):
+    """Enumerate every sequence of candidates (U = 0: q_d does not depend on
+    the prefix) and take the W best per length under the comparator, with
+    ties broken by token and then recursively by the prefix."""
+    L = logits.shape[0]
+    cand = []
+    for i in range(L):
+        order = sorted(range(logits.shape[1]), key=lambda j: (-logits[i, j], j))[:K]
+        v = np.array([logits[i, j] for j in order])
+        q = np.exp(v - v.max()) / np.exp(v - v.max()).sum()
+        cand.append((order, np.log(q)))
+    out = {}
+    for d in range(1, L + 1):
+        seqs = []
+        for combo in itertools.product(range(K), repeat=d):
+            cum = 0.0
+            key_tail = ()
+            toks = []
+            for i, k in enumerate(combo):
+                cum = cum + cand[i][1][k]
+                toks.append(cand[i][0][k])
+            sb = cum + beta * d
+            # comparator key built from the last position outwards
+            key = ()
+            c2 = 0.0
+            partial = []
+            for i, k in enumerate(combo):
+                c2 = c2 + cand[i][1][k]
+                partial.append((-(c2 + beta * (i + 1)), cand[i][0][k]))
+            for item in partial:
+                key = (item[0], item[1], key)
+            seqs.append(((-sb, toks[-1], key), tuple(toks), cum, sb))
+        seqs.sort(key=lambda s: s[0])
+        out[d] = seqs[:W]
+    return out
+
+
+@pytest.mark.parametrize("seed,W,beta", [(s, w, b) for s in range(4) for w in (1, 2, 3, 7) for b in (0.0, -0.1, -5.0)])
+def test_U_zero_beam_equals_brute_force(seed, W, beta):
+    K, L = 4, 4
+    logits, h, A, E, U = rand_problem(100 + seed, V=12, L=L, K=K, U_zero=True)
+    ids, vals = cands(logits, K)
+    levels = O.build_supertree(ids, vals, h, A, E, U, W=W, beta=beta)
+    bf = brute_force_levels(logits, K, W, beta)
+
+    def path(d, nd):
+        toks = [nd.tok]
+        while d > 1:
+            nd = levels[d - 1][nd.parent_slot]
+            d -= 1
+            toks.append(nd.tok)
+        return tuple(reversed(toks))
+
+    for d in range(1, L + 1):
+        got = [(path(d, nd), nd.cum, nd.sbeta) for nd in levels[d]]
+        exp = [(s[1], s[2], s[3]) for s in bf[d]]
+        assert [g[0] for g in got] == [e[0] for e in exp], f"depth {d}"
+        assert np.allclose([g[1] for g in got], [e[1] for e in exp], atol=1e-12)
+        assert np.allclose([g[2] for g in got], [e[2] for e in exp], atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# W = 1: one greedy corrected chain (Domino's single chain)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(8))
+def test_W1_is_greedy_chain(seed):
+    logits, h, A, E, U = rand_problem(200 + seed, V=30, L=6, K=6)
+    K, B = 6, 4
+    res = O.round_one_request(logits, h, A, E, U, K, 1, B, -0.3)
+    s = h[0]
+    chain = []
+    cum = 0.0
+    for d in range(1, 7):
+        order = sorted(range(30), key=lambda j: (-logits[d - 1, j], j))[:K]
+        z = [logits[d - 1, j] + float(U[j].dot(s)) for j in order]
+        best = max(range(K), key=lambda k: (z[k], -order[k]))
+        m = max(z)
+        cum += z[best] - (m + math.log(sum(math.exp(x - m) for x in z)))
+        chain.append((order[best], cum))
+        if d < 6:
+            s = np.tanh(A.dot(s) + E[order[best]] + h[d])
+    assert [lv[0].tok for lv in res.levels[1:]] == [c[0] for c in chain]
+    assert np.allclose([lv[0].cum for lv in res.levels[1:]], [c[1] for c in chain], atol=1e-10)
+    assert res.emitted.n_sel == min(B, 6)
+    assert res.emitted.tok[:B].tolist() == [c[0] for c in chain[:B]]
+    assert res.emitted.parent[:B].tolist() == [-1] + list(range(B - 1))
+
+
+# --------------------------------------------------------------------------
+# Lemma 1: deferred top-B equals best-first heap pops on the supertree
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed,beta", [(s, b) for s in range(12) for b in (0.0, -0.1, -0.5, -5.0)])
+def test_lemma1_heap_equals_deferred(seed, beta):
+    rng = np.random.default_rng(seed)
+    W = int(rng.integers(1, 6))
+    B = int(rng.integers(1, 20))
+    logits, h, A, E, U = rand_problem(300 + seed, V=25, L=5, K=5, ties=(seed % 3 == 0))
+    ids, vals = cands(logits, 5)
+    levels = O.build_supertree(ids, vals, h, A, E, U, W=W, beta=beta)
+    deferred = O.select_topB(levels, B)
+    heap = O.heap_materialized(levels, B)
+    assert [(n.depth, n.slot) for n in heap] == [(n.depth, n.slot) for n in deferred]
+    sel = set((n.depth, n.slot) for n in deferred)
+    for n in deferred:
+        assert n.depth == 1 or (n.depth - 1, n.parent_slot) in sel     # prefix closed
+    assert len(deferred) == min(B, sum(len(l) for l in levels[1:])) <= B
+
+
+# --------------------------------------------------------------------------
+# W >= B: deferred construction equals the serial "pop then correct" heap
+# over the full tree (derived: a node of the full-tree top-B can only be
+# pruned at its depth if W >= B better nodes of that depth exist, all of them
+# in the top-B, which would make it more than B)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed,beta", [(s, b) for s in range(10) for b in (0.0, -0.15, -1.0)])
+def test_deferred_equals_serial_heap_when_W_ge_B(seed, beta):
+    K, L, B = 6, 6, 12
+    W = B + (seed % 3)
+    logits, h, A, E, U = rand_problem(400 + seed, V=20, L=L, K=K, scale_u=3.0)
+    ids, vals = cands(logits, K)
+    levels = O.build_supertree(ids, vals, h, A, E, U, W=W, beta=beta)
+    deferred = O.select_topB(levels, B)
+    serial = O.heap_serial_full(ids, vals, h, A, E, U, beta, B)
+
+    def path_st(n):
+        toks = []
+        d = n.depth
+        while d >= 1:
+            toks.append(n.tok)
+            n = levels[d - 1][n.parent_slot] if d > 1 else None
+            d -= 1
+        return tuple(reversed(toks))
+
+    def path_full(n):
+        toks = []
+        while n.depth >= 1:
+            toks.append(n.tok)
+            n = n.parent
+        return tuple(reversed(toks))
+
+    assert [path_st(n) for n in deferred] == [path_full(n) for n in serial]
+    assert np.allclose([n.sbeta for n in deferred], [n.sbeta for n in serial], atol=1e-12)
+
+
+def test_whole_supertree_selected_when_WL_le_B():
+    logits, h, A, E, U = rand_problem(77, V=30, L=5, K=6)
+    W, L = 3, 5
+    res = O.round_one_request(logits, h, A, E, U, 6, W, W * L + 2, -0.1)
+    assert res.emitted.n_sel == W * L
+    assert len(res.selected) == sum(len(l) for l in res.levels[1:])
+
+
+def test_very_negative_beta_is_depth_major():
+    logits, h, A, E, U = rand_problem(78, V=30, L=5, K=6)
+    res = O.round_one_request(logits, h, A, E, U, 6, 3, 8, -1e3)
+    assert [n.depth for n in res.selected] == [1, 1, 1, 2, 2, 2, 3, 3]
+
+
+# --------------------------------------------------------------------------
+# emission and mask
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(10))
+def test_emission_and_mask_invariants(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 130))
+    logits, h, A, E, U = rand_problem(500 + seed, V=40, L=8, K=6)
+    res = O.round_one_request(logits, h, A, E, U, 6, 20, B, -0.1)
+    em, m = res.emitted, res.mask
+    n = em.n_sel
+    words = (B + 63) // 64
+    assert m.shape == (B, words)
+    for i in range(n):
+        p = em.parent[i]
+        assert -1 <= p < i
+        assert em.depth[i] == (1 if p == -1 else em.depth[p] + 1)
+        bits = sum(bin(int(w)).count("1") for w in m[i])
+        assert bits == em.depth[i]
+        assert (int(m[i, i // 64]) >> (i % 64)) & 1
+        if p >= 0:
+            assert np.all((m[i] & m[p]) == m[p])
+        # lower triangular: no bit above the diagonal
+        for j in range(i + 1, B):
+            assert not (int(m[i, j // 64]) >> (j % 64)) & 1
+    assert np.all(m[n:] == 0)
+    assert np.all(em.tok[n:] == -1) and np.all(em.parent[n:] == -2) and np.all(np.isneginf(em.score[n:]))
+    # breadth-first: depth non-decreasing, then parent index, then token
+    keys = [(em.depth[i], em.parent[i], em.tok[i]) for i in range(n)]
+    assert keys == sorted(keys)
+    # the mask built row by row from parent rows equals the ancestor walk
+    m2 = np.zeros_like(m)
+    for i in range(n):
+        if em.parent[i] >= 0:
+            m2[i] = m2[em.parent[i]]
+        m2[i, i // 64] |= np.uint64(1) << np.uint64(i % 64)
+    assert np.array_equal(m, m2)
+
+
+# --------------------------------------------------------------------------
+# equal scores of a parent and its child: depth breaks the tie (prefix closure)
+# --------------------------------------------------------------------------
+def test_equal_parent_child_score_depth_tiebreak():
+    # base logits [0, -800] over K = 2 give log q = [0, -800] exactly in
+    # float64, so with beta = 0 the best child scores exactly as its parent
+    V, L, r = 4, 3, 2
+    logits = np.full((L, V), -900.0)
+    logits[:, 0] = 0.0
+    logits[:, 1] = -800.0
+    h = np.zeros((L, r)); A = np.zeros((r, r)); E = np.zeros((V, r)); U = np.zeros((V, r))
+    for B in (1, 2, 3):
+        res = O.round_one_request(logits, h, A, E, U, 2, 2, B, 0.0)
+        assert [n.depth for n in res.selected] == list(range(1, B + 1))
+        assert all(n.sbeta == 0.0 for n in res.selected)
+        assert res.emitted.parent[:B].tolist() == [-1] + list(range(B - 1))
+
+
+# --------------------------------------------------------------------------
+# planted mistakes must be caught by the pins above
+# --------------------------------------------------------------------------
+import importlib
+
+MUTANTS = {
+    "drop_lse": ("return z - (m + np.log(np.sum(np.exp(z - m))))", "return z - m"),
+    "beta_sign": ("sb = cum + beta * d", "sb = cum - beta * d"),
+    "drop_parent_cum": ("cum = p.cum + logq", "cum = logq"),
+    "wrong_h_row": ("child_state(A, p.state, E[tok], h[d])", "child_state(A, p.state, E[tok], h[d - 1])"),
+    "transposed_A": ("np.tanh(A @ s_parent + e_row + h_d)", "np.tanh(A.T @ s_parent + e_row + h_d)"),
+    "E_for_U": ("U_rows = U[C]", "U_rows = E[C]"),
+    "token_desc_tiebreak": ("order = np.lexsort((ids, -v))", "order = np.lexsort((-ids, -v))"),
+    "wrong_logits_row": ("cand_ids[d - 1], cand_vals[d - 1], h, A, E, U, W, beta, L)",
+                         "cand_ids[d % L], cand_vals[d % L], h, A, E, U, W, beta, L)"),
+    "keep_W_minus_1": ("children[:W]", "children[:max(W - 1, 1)]"),
+    "depth_desc_tiebreak": ("return (-sbeta, depth, tok, parent_slot)", "return (-sbeta, -depth, tok, parent_slot)"),
+    "emit_token_first": ("nodes.sort(key=lambda nd: (pidx(nd), nd.tok))", "nodes.sort(key=lambda nd: (nd.tok, pidx(nd)))"),
+    "mask_without_self": ("        j = i\n        while j >= 0:", "        j = int(parent[i])\n        while j >= 0:"),
+    "projection_untransposed": ("@ np.asarray(Pt, dtype=np.float64).T", "@ np.asarray(Pt, dtype=np.float64).T[::-1]"),
+}
+
+
+def _run_pins():
+    test_hand_worked_example()
+    test_equal_parent_child_score_depth_tiebreak()
+    test_head_states_onehot_and_linearity()
+    for s in range(5):
+        test_topk_matches_rank_count(s)
+    for s in range(2):
+        test_W1_is_greedy_chain(s)
+        for b in (0.0, -0.1):
+            test_deferred_equals_serial_heap_when_W_ge_B(s, b)
+        test_emission_and_mask_invariants(s)
+    test_U_zero_beam_equals_brute_force(0, 2, -0.1)
+    test_state_is_tanh_h_when_A_and_E_vanish()
+    test_state_recursion_chain_explicit()
+    test_U_zero_logq_is_base_softmax()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistakes_are_caught(name):
+    src = open(O.__file__).read()
+    old, new = MUTANTS[name]
+    assert old in src, f"mutation site for {name} not found"
+    try:
+        exec(compile(src.replace(old, new), O.__file__, "exec"), O.__dict__)
+        caught = False
+        try:
+            _run_pins()
+        except (AssertionError, KeyError, IndexError, ValueError):
+            caught = True
+        assert caught, f"mutant {name} survived the pins"
+    finally:
+        importlib.reload(O)
+
+
+def test_unmutated_oracle_passes_pin_set():
+    _run_pins()
