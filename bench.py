@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark: DARTree draft-tree construction rounds on one MI355X.
+
+A step is one whole round (head inputs, top-K candidates, depth-by-depth
+expansion, global top-B, emission and mask) over one synthetic round of the
+qwen3_4b workload (V=151936, L=16, K=64, W=12, B=64, r=256, D=2560, one
+request). Rounds run one after another, each on a distinct device-resident
+round from a ring larger than the 256 MB Infinity Cache, as in decoding where
+each round depends on the previous verification.
+
+Prints one JSON line (see the end of main()).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "draft-tree builds/sec and us/round at V=151936,L=16,K=64,W=12,B=64 (1 GPU)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--config", default="qwen3_4b")
+    ap.add_argument("--ring", type=int, default=128, help="distinct device-resident rounds")
+    ap.add_argument("--graph-rounds", type=int, default=16, help="rounds captured per HIP graph")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="if > 0: run only this many eager rounds (for rocprofv3) and exit")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(requests shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from diffusion_drafter_tree_amd import inputs as I
+    from diffusion_drafter_tree_amd import ops
+
+    torch.cuda.set_device(0)
+    cfg = I.CONFIGS[args.config]
+    t0 = time.time()
+    head = I.make_head(cfg, 0)
+    dhead = ops.DeviceHead(head)
+    R = max(1, args.ring)
+    logits, hin = [], []
+    for t in range(R):
+        rnd = I.make_round(cfg, 0, t)
+        logits.append(ops.to_device(rnd.logits))
+        hin.append(ops.to_device(rnd.H if cfg.D > 0 else rnd.h))
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready: {R} rounds ({R * logits[0].numel() * logits[0].element_size() / 1e6:.0f} MB of "
+          f"logits) in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    rb = ops.RoundBuffers(cfg)
+    dims = rb.dims
+    stream = torch.cuda.current_stream()
+
+    if args.profile_steps > 0:
+        for t in range(args.profile_steps):
+            ops.build_round(dims, dhead, logits[t % R], hin[t % R], rb)
+        torch.cuda.synchronize()
+        print(f"[bench] profiled {args.profile_steps} eager rounds", file=sys.stderr, flush=True)
+        return
+
+    # ---- warmup (eager) ------------------------------------------------------
+    for t in range(args.warmup):
+        ops.build_round(dims, dhead, logits[t % R], hin[t % R], rb)
+    torch.cuda.synchronize()
+
+    # ---- graphs of G consecutive ring rounds ---------------------------------
+    G = max(1, min(args.graph_rounds, R))
+    graphs = []
+    s_cap = torch.cuda.Stream()
+    s_cap.wait_stream(stream)
+    with torch.cuda.stream(s_cap):
+        for start in range(0, R, G):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s_cap):
+                for t in range(start, min(R, start + G)):
+                    ops.build_round(dims, dhead, logits[t], hin[t], rb)
+            graphs.append((g, min(R, start + G) - start))
+    stream.wait_stream(s_cap)
+    torch.cuda.synchronize()
+    # replay each graph once more as warmup
+    for g, _ in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K rounds ----------------------------------------
+    K = args.steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    done, gi = 0, 0
+    plan = []
+    while done < K:
+        g, n = graphs[gi % len(graphs)]
+        if done + n <= K:
+            plan.append(("g", g, n))
+            done += n
+        else:
+            plan.append(("e", (gi * G) % R, K - done))
+            done = K
+        gi += 1
+    torch.cuda.synchronize()
+    t_host0 = time.perf_counter()
+    ev0.record(stream)
+    for kind, obj, n in plan:
+        if kind == "g":
+            obj.replay()
+        else:
+            for t in range(n):
+                ops.build_round(dims, dhead, logits[(obj + t) % R], hin[(obj + t) % R], rb)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host0
+    ms = ev0.elapsed_time(ev1)
+    us_round = ms * 1000.0 / K
+    builds_per_s = K / (ms / 1000.0)
+
+    # ---- eager rate (host launches, no graph), for reference -------------------
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ne = min(K, 256)
+    e0.record(stream)
+    for t in range(ne):
+        ops.build_round(dims, dhead, logits[t % R], hin[t % R], rb)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_eager = e0.elapsed_time(e1) * 1000.0 / ne
+
+    # ---- per-kernel durations with HIP events (step entry points) ----------------
+    names = ["head_states", "topk_candidates", "expand_depth", "select_topB", "tree_mask"]
+    evs = {n: [] for n in names}
+    nk = min(K, 256)
+    torch.cuda.synchronize()
+    for t in range(nk):
+        s = t % R
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        marks[0].record(stream)
+        if cfg.D > 0:
+            ops.head_states(dims, hin[s], dhead.Pt, rb.h)
+        marks[1].record(stream)
+        ops.topk_candidates(dims, logits[s], rb.cand_ids, rb.cand_logit, rb.ws)
+        marks[2].record(stream)
+        rb.st.next_depth = 1
+        ops.expand_depth(dims, dhead, rb.cand_ids, rb.cand_logit, rb.h if cfg.D > 0 else hin[s], rb, 1, cfg.L)
+        marks[3].record(stream)
+        ops.select_topB(dims, rb)
+        marks[4].record(stream)
+        ops.tree_mask(dims, rb.n_sel, rb.parent, rb.mask)
+        marks[5].record(stream)
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            evs[n].append(marks[i].elapsed_time(marks[i + 1]) * 1000.0)
+    kern_us = {n: float(np.mean(v[4:])) if len(v) > 8 else float(np.mean(v)) for n, v in evs.items()}
+
+    # algorithmic bytes / flops per launch
+    n, L, V, Kc, W, B, r, D = cfg.n_req, cfg.L, cfg.V, cfg.K, cfg.W, cfg.B, cfg.r, cfg.D
+    lsz = 2 if cfg.logits_dtype == "bf16" else 4
+    wsz = 2 if cfg.weight_dtype == "bf16" else 4
+    alg = {
+        "topk_candidates": {"bytes": n * L * V * lsz + n * L * Kc * 8, "flops": 0},
+        "head_states": {"bytes": n * L * D * wsz + r * D * wsz + n * L * r * 4, "flops": 2 * n * L * D * r},
+        "expand_depth": {"bytes": n * L * Kc * (r * wsz + 8) + n * (L - 1) * W * r * wsz + r * r * wsz
+                         + n * L * r * 4 + n * L * W * 16,
+                         "flops": 2 * n * L * W * Kc * r + 2 * n * (L - 1) * W * r * r},
+        "select_topB": {"bytes": n * L * W * 16 + n * B * 20, "flops": 0},
+        "tree_mask": {"bytes": n * B * 4 + n * B * ((B + 63) // 64) * 8, "flops": 0},
+    }
+    HBM_PEAK = 8000.0   # GB/s
+    kernels = {}
+    for k in names:
+        if k == "head_states" and D == 0:
+            continue
+        us = kern_us[k]
+        gbs = alg[k]["bytes"] / (us * 1e-6) / 1e9
+        kernels[k] = {"us": round(us, 3), "alg_bytes": alg[k]["bytes"], "GB_s": round(gbs, 1),
+                      "hbm_frac": round(gbs / HBM_PEAK, 4), "alg_flops": alg[k]["flops"]}
+    dom = max(kernels, key=lambda k: kernels[k]["us"])
+    dk = kernels[dom]
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": dk["GB_s"], "peak": HBM_PEAK, "unit": "GB/s",
+                "frac": dk["hbm_frac"], "traffic": None}
+    scan = kernels["topk_candidates"]
+    roofline_scan = {"kernel": "topk_candidates", "bound": "hbm", "achieved": scan["GB_s"], "peak": HBM_PEAK,
+                     "unit": "GB/s", "frac": scan["hbm_frac"], "traffic": None}
+
+    # ---- CPU oracle baseline on a bounded sample -------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, head, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(builds_per_s, 1),
+        "unit": "builds/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / K, 6),
+        "us_per_round": round(us_round, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: n_req={n} V={V} L={L} K={Kc} W={W} B={B} beta={cfg.beta} r={r} D={D} "
+                               f"logits={cfg.logits_dtype} weights={cfg.weight_dtype}",
+                   "ring_rounds": R, "launch": f"hipGraph of {G} rounds per replay",
+                   "global_batch": n, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "roofline_scan": roofline_scan,
+        "kernels": kernels,
+        "us_per_round_eager": round(us_eager, 3),
+        "host_seconds_timed": round(t_host, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, head, budget_s):
+    """The oracle as it stands, on the same workload, for a bounded sample of
+    rounds; single-threaded BLAS."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    from diffusion_drafter_tree_amd import inputs as I
+    from oracle import dartree_oracle as O
+
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        rounds = [I.make_round(cfg, 0, t) for t in range(3)]
+        t0 = time.perf_counter()
+        done = 0
+        while True:
+            O.round_all(cfg, head, rounds[done % len(rounds)])
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or done >= 1000:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return {"value": round(done / el, 3), "unit": "builds/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} rounds of {cfg.name} (3 distinct seeded rounds cycled), numpy fp64, "
+                      f"{el:.1f} s wall on 1 host thread"}
+
+
+if __name__ == "__main__":
+    main()

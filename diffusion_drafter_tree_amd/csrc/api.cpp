@@ -1,0 +1,342 @@
+// C ABI of libdartree: argument validation, workspace layout and kernel
+// dispatch. Every entry point validates completely before it enqueues.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dartree.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dartree_status fail(dartree_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+dartree_status hip_fail(hipError_t e, const char* what) {
+  return fail(DARTREE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define REQ_PTR(p, a)                                                                          \
+  do {                                                                                         \
+    if ((p) == nullptr) return fail(DARTREE_ERR_INVALID_ARGUMENT, "%s is NULL", #p);           \
+    if (!aligned((p), (a)))                                                                    \
+      return fail(DARTREE_ERR_INVALID_ARGUMENT, "%s is not %d-byte aligned", #p, (int)(a));    \
+  } while (0)
+
+constexpr int kMaxL = 31, kMaxK = 1024, kMaxW = 64, kMaxB = 1024, kMaxR = 1024, kMaxV = 1 << 18;
+
+dartree_status check_dims(const dartree_dims* d) {
+  if (!d) return fail(DARTREE_ERR_INVALID_ARGUMENT, "dims is NULL");
+  if (d->n_req < 1 || d->L < 1 || d->V < 1 || d->K < 1 || d->W < 1 || d->B < 1 || d->r < 1 || d->D < 0)
+    return fail(DARTREE_ERR_INVALID_ARGUMENT, "sizes must be positive (n_req=%d L=%d V=%d K=%d W=%d B=%d r=%d D=%d)",
+                d->n_req, d->L, d->V, d->K, d->W, d->B, d->r, d->D);
+  if (d->K > d->V) return fail(DARTREE_ERR_INVALID_ARGUMENT, "K=%d exceeds V=%d", d->K, d->V);
+  if (!std::isfinite(d->beta)) return fail(DARTREE_ERR_INVALID_ARGUMENT, "beta is not finite");
+  if (d->beta > 0.f)
+    return fail(DARTREE_ERR_INVALID_ARGUMENT, "beta=%g > 0: prefix closure (Lemma 1) needs beta <= 0", d->beta);
+  if ((d->logits_dtype != DARTREE_F32 && d->logits_dtype != DARTREE_BF16) ||
+      (d->weight_dtype != DARTREE_F32 && d->weight_dtype != DARTREE_BF16))
+    return fail(DARTREE_ERR_UNSUPPORTED, "unknown dtype");
+  if (d->L > kMaxL || d->K > kMaxK || d->W > kMaxW || d->B > kMaxB || d->r > kMaxR || d->V > kMaxV ||
+      d->n_req > 65535 || d->D > (1 << 20))
+    return fail(DARTREE_ERR_UNSUPPORTED,
+                "limits: L<=%d K<=%d W<=%d B<=%d r<=%d V<=%d n_req<=65535 D<=2^20 (got L=%d K=%d W=%d B=%d r=%d V=%d)",
+                kMaxL, kMaxK, kMaxW, kMaxB, kMaxR, kMaxV, d->L, d->K, d->W, d->B, d->r, d->V);
+  if (d->W * d->r > 8192 || d->W * d->K > 8192)
+    return fail(DARTREE_ERR_UNSUPPORTED, "limits: W*r <= 8192 and W*K <= 8192 (got W*r=%d W*K=%d)", d->W * d->r,
+                d->W * d->K);
+  return DARTREE_OK;
+}
+
+struct WsLayout {
+  dartree::TopkPlan plan;
+  size_t tickets_off, lists_off, total;
+};
+
+WsLayout ws_layout(const dartree_dims* d) {
+  WsLayout w{};
+  const int rows = d->n_req * d->L;
+  w.plan = dartree::topk_plan(rows, d->V, d->K, d->logits_dtype == DARTREE_BF16);
+  w.tickets_off = 0;
+  w.lists_off = (w.plan.ticket_bytes + 255) & ~(size_t)255;
+  w.total = w.lists_off + w.plan.list_bytes;
+  if (w.total == 0) w.total = 256;
+  return w;
+}
+
+dartree_status check_ws(const dartree_dims* d, void* ws, size_t ws_bytes, WsLayout* out) {
+  *out = ws_layout(d);
+  if (out->plan.nv == 0) return fail(DARTREE_ERR_UNSUPPORTED, "no top-K plan for V=%d K=%d", d->V, d->K);
+  REQ_PTR(ws, 256);
+  if (ws_bytes < out->total)
+    return fail(DARTREE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", ws_bytes, out->total);
+  return DARTREE_OK;
+}
+
+dartree_status check_head(const dartree_dims* d, const dartree_head* h) {
+  if (!h) return fail(DARTREE_ERR_INVALID_ARGUMENT, "head is NULL");
+  REQ_PTR(h->A, 16);
+  REQ_PTR(h->E, 16);
+  REQ_PTR(h->U, 16);
+  (void)d;
+  return DARTREE_OK;
+}
+
+dartree_status check_supertree(const dartree_supertree* st) {
+  if (!st) return fail(DARTREE_ERR_INVALID_ARGUMENT, "supertree is NULL");
+  REQ_PTR(st->tok, 4);
+  REQ_PTR(st->parent_slot, 4);
+  REQ_PTR(st->cum, 4);
+  REQ_PTR(st->sbeta, 4);
+  REQ_PTR(st->count, 4);
+  REQ_PTR(st->state, 16);
+  return DARTREE_OK;
+}
+
+dartree_status check_tree_out(const int32_t* n_sel, const int32_t* tok, const int32_t* depth, const int32_t* parent,
+                              const float* score, const int32_t* slot) {
+  REQ_PTR(n_sel, 4);
+  REQ_PTR(tok, 4);
+  REQ_PTR(depth, 4);
+  REQ_PTR(parent, 4);
+  REQ_PTR(score, 4);
+  REQ_PTR(slot, 4);
+  return DARTREE_OK;
+}
+
+#define TRY(x)                                \
+  do {                                        \
+    dartree_status _s = (x);                  \
+    if (_s != DARTREE_OK) return _s;          \
+  } while (0)
+
+dartree::ExpandArgs expand_args(const dartree_dims* dims, const dartree_head* head, const int32_t* cand_ids,
+                                const float* cand_logit, const float* h, const dartree_supertree* st, int d0,
+                                int d1) {
+  dartree::ExpandArgs a{};
+  a.n_req = dims->n_req;
+  a.L = dims->L;
+  a.V = dims->V;
+  a.K = dims->K;
+  a.W = dims->W;
+  a.r = dims->r;
+  a.beta = dims->beta;
+  a.bf16 = dims->weight_dtype == DARTREE_BF16;
+  a.A = head->A;
+  a.E = head->E;
+  a.U = head->U;
+  a.cand_ids = cand_ids;
+  a.cand_logit = cand_logit;
+  a.h = h;
+  a.st_tok = st->tok;
+  a.st_parent = st->parent_slot;
+  a.st_cum = st->cum;
+  a.st_sbeta = st->sbeta;
+  a.st_count = st->count;
+  a.st_state = st->state;
+  a.d0 = d0;
+  a.d1 = d1;
+  return a;
+}
+
+dartree::SelectArgs select_args(const dartree_dims* dims, const dartree_supertree* st, int32_t* n_sel, int32_t* tok,
+                                int32_t* depth, int32_t* parent, float* score, int32_t* slot) {
+  dartree::SelectArgs a{};
+  a.n_req = dims->n_req;
+  a.L = dims->L;
+  a.W = dims->W;
+  a.B = dims->B;
+  a.st_tok = st->tok;
+  a.st_parent = st->parent_slot;
+  a.st_sbeta = st->sbeta;
+  a.st_count = st->count;
+  a.n_sel = n_sel;
+  a.tok = tok;
+  a.depth = depth;
+  a.parent = parent;
+  a.score = score;
+  a.slot = slot;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dartree_status_string(dartree_status s) {
+  switch (s) {
+    case DARTREE_OK: return "DARTREE_OK";
+    case DARTREE_ERR_INVALID_ARGUMENT: return "DARTREE_ERR_INVALID_ARGUMENT";
+    case DARTREE_ERR_UNSUPPORTED: return "DARTREE_ERR_UNSUPPORTED";
+    case DARTREE_ERR_WORKSPACE_TOO_SMALL: return "DARTREE_ERR_WORKSPACE_TOO_SMALL";
+    case DARTREE_ERR_HIP: return "DARTREE_ERR_HIP";
+  }
+  return "DARTREE_UNKNOWN_STATUS";
+}
+
+const char* dartree_last_error(void) { return g_err; }
+
+int32_t dartree_version(void) { return 1; }
+
+dartree_status dartree_workspace_size(const dartree_dims* dims, size_t* bytes) {
+  g_err[0] = 0;
+  TRY(check_dims(dims));
+  if (!bytes) return fail(DARTREE_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  WsLayout w = ws_layout(dims);
+  if (w.plan.nv == 0) return fail(DARTREE_ERR_UNSUPPORTED, "no top-K plan for V=%d K=%d", dims->V, dims->K);
+  *bytes = w.total;
+  return DARTREE_OK;
+}
+
+dartree_status dartree_workspace_init(const dartree_dims* dims, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  TRY(check_dims(dims));
+  WsLayout w;
+  TRY(check_ws(dims, ws, ws_bytes, &w));
+  hipError_t e = dartree::launch_fill_u32(static_cast<char*>(ws) + w.tickets_off, w.plan.ticket_bytes / 4, 0u,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "workspace_init");
+  return DARTREE_OK;
+}
+
+dartree_status dartree_head_states(const dartree_dims* dims, const void* H, const void* Pt, float* h, void* stream) {
+  g_err[0] = 0;
+  TRY(check_dims(dims));
+  if (dims->D < 1) return fail(DARTREE_ERR_INVALID_ARGUMENT, "head_states needs D >= 1");
+  REQ_PTR(H, 16);
+  REQ_PTR(Pt, 16);
+  REQ_PTR(h, 4);
+  hipError_t e = dartree::launch_head_states(dims->weight_dtype == DARTREE_BF16, H, Pt, h, dims->n_req * dims->L,
+                                             dims->D, dims->r, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "head_states launch");
+  return DARTREE_OK;
+}
+
+dartree_status dartree_topk_candidates(const dartree_dims* dims, const void* logits, int32_t* cand_ids,
+                                       float* cand_logit, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  TRY(check_dims(dims));
+  REQ_PTR(logits, 16);
+  REQ_PTR(cand_ids, 4);
+  REQ_PTR(cand_logit, 4);
+  WsLayout w;
+  TRY(check_ws(dims, ws, ws_bytes, &w));
+  char* wsb = static_cast<char*>(ws);
+  hipError_t e = dartree::launch_topk(w.plan, dims->logits_dtype == DARTREE_BF16, logits, dims->V, dims->K,
+                                      reinterpret_cast<uint64_t*>(wsb + w.lists_off),
+                                      reinterpret_cast<unsigned int*>(wsb + w.tickets_off), cand_ids, cand_logit,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "topk launch");
+  return DARTREE_OK;
+}
+
+dartree_status dartree_expand_depth(const dartree_dims* dims, const dartree_head* head, const int32_t* cand_ids,
+                                    const float* cand_logit, const float* h, dartree_supertree* st,
+                                    int32_t depth_begin, int32_t depth_end, void* stream) {
+  g_err[0] = 0;
+  TRY(check_dims(dims));
+  TRY(check_head(dims, head));
+  REQ_PTR(cand_ids, 4);
+  REQ_PTR(cand_logit, 4);
+  REQ_PTR(h, 4);
+  TRY(check_supertree(st));
+  if (depth_begin != st->next_depth)
+    return fail(DARTREE_ERR_INVALID_ARGUMENT, "depth_begin=%d but the supertree expects depth %d", depth_begin,
+                st->next_depth);
+  if (depth_begin < 1 || depth_end < depth_begin || depth_end > dims->L)
+    return fail(DARTREE_ERR_INVALID_ARGUMENT, "depth range [%d, %d] outside [1, %d]", depth_begin, depth_end, dims->L);
+  hipError_t e = dartree::launch_expand(expand_args(dims, head, cand_ids, cand_logit, h, st, depth_begin, depth_end),
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "expand launch");
+  st->next_depth = depth_end + 1;
+  return DARTREE_OK;
+}
+
+dartree_status dartree_select_topB(const dartree_dims* dims, const dartree_supertree* st, int32_t* n_sel,
+                                   int32_t* tok, int32_t* depth, int32_t* parent, float* score, int32_t* slot,
+                                   void* stream) {
+  g_err[0] = 0;
+  TRY(check_dims(dims));
+  TRY(check_supertree(st));
+  if (st->next_depth != dims->L + 1)
+    return fail(DARTREE_ERR_INVALID_ARGUMENT, "supertree incomplete: next_depth=%d, expected %d", st->next_depth,
+                dims->L + 1);
+  TRY(check_tree_out(n_sel, tok, depth, parent, score, slot));
+  hipError_t e = dartree::launch_select(select_args(dims, st, n_sel, tok, depth, parent, score, slot),
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return DARTREE_OK;
+}
+
+dartree_status dartree_tree_mask(const dartree_dims* dims, const int32_t* n_sel, const int32_t* parent,
+                                 uint64_t* mask, void* stream) {
+  g_err[0] = 0;
+  TRY(check_dims(dims));
+  REQ_PTR(n_sel, 4);
+  REQ_PTR(parent, 4);
+  REQ_PTR(mask, 8);
+  hipError_t e = dartree::launch_mask(dims->n_req, dims->B, n_sel, parent, mask, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mask launch");
+  return DARTREE_OK;
+}
+
+dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head* head, const void* logits,
+                                   const void* H_or_h, int32_t* cand_ids, float* cand_logit, float* h,
+                                   dartree_supertree* st, int32_t* n_sel, int32_t* tok, int32_t* depth,
+                                   int32_t* parent, float* score, int32_t* slot, uint64_t* mask, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  TRY(check_dims(dims));
+  TRY(check_head(dims, head));
+  REQ_PTR(logits, 16);
+  REQ_PTR(H_or_h, 16);
+  REQ_PTR(cand_ids, 4);
+  REQ_PTR(cand_logit, 4);
+  if (dims->D > 0) {
+    REQ_PTR(h, 4);
+    REQ_PTR(head->Pt, 16);
+  }
+  TRY(check_supertree(st));
+  if (st->next_depth != 1)
+    return fail(DARTREE_ERR_INVALID_ARGUMENT, "supertree next_depth=%d, a round starts at 1", st->next_depth);
+  TRY(check_tree_out(n_sel, tok, depth, parent, score, slot));
+  REQ_PTR(mask, 8);
+  WsLayout w;
+  TRY(check_ws(dims, ws, ws_bytes, &w));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float* hin = static_cast<const float*>(H_or_h);
+  hipError_t e;
+  if (dims->D > 0) {
+    e = dartree::launch_head_states(dims->weight_dtype == DARTREE_BF16, H_or_h, head->Pt, h, dims->n_req * dims->L,
+                                    dims->D, dims->r, s);
+    if (e != hipSuccess) return hip_fail(e, "head_states launch");
+    hin = h;
+  }
+  char* wsb = static_cast<char*>(ws);
+  e = dartree::launch_topk(w.plan, dims->logits_dtype == DARTREE_BF16, logits, dims->V, dims->K,
+                           reinterpret_cast<uint64_t*>(wsb + w.lists_off),
+                           reinterpret_cast<unsigned int*>(wsb + w.tickets_off), cand_ids, cand_logit, s);
+  if (e != hipSuccess) return hip_fail(e, "topk launch");
+  e = dartree::launch_expand(expand_args(dims, head, cand_ids, cand_logit, hin, st, 1, dims->L), s);
+  if (e != hipSuccess) return hip_fail(e, "expand launch");
+  st->next_depth = dims->L + 1;
+  e = dartree::launch_select(select_args(dims, st, n_sel, tok, depth, parent, score, slot), s);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  e = dartree::launch_mask(dims->n_req, dims->B, n_sel, parent, mask, s);
+  if (e != hipSuccess) return hip_fail(e, "mask launch");
+  return DARTREE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,176 @@
+"""Torch-facing binding of libdartree (argument marshalling only).
+
+PyTorch supplies device memory and the current stream; every step of the
+round runs in the library's HIP kernels. Each function mirrors one C entry
+point of include/dartree.h and raises DartreeError on a non-OK status.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import _lib as C
+from . import inputs as I
+
+
+class DartreeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {C.status_string(status)}: {C.last_error()}")
+
+
+def _check(status: int, where: str):
+    if status != C.OK:
+        raise DartreeError(status, where)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(None)
+
+
+def _stream(stream: Optional[torch.cuda.Stream] = None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_dims(cfg: I.Config) -> C.Dims:
+    return C.Dims(n_req=cfg.n_req, L=cfg.L, V=cfg.V, K=cfg.K, W=cfg.W, B=cfg.B, r=cfg.r, D=cfg.D,
+                  beta=cfg.beta, logits_dtype=C.BF16 if cfg.logits_dtype == I.BF16 else C.F32,
+                  weight_dtype=C.BF16 if cfg.weight_dtype == I.BF16 else C.F32)
+
+
+def to_device(arr: Optional[np.ndarray], device="cuda") -> Optional[torch.Tensor]:
+    """Upload a generator array (uint16 bf16 bits travel as int16)."""
+    if arr is None:
+        return None
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+class DeviceHead:
+    """Head weights resident on the GPU."""
+
+    def __init__(self, head: I.Head, device="cuda"):
+        self.A = to_device(head.A, device)
+        self.E = to_device(head.E, device)
+        self.U = to_device(head.U, device)
+        self.Pt = to_device(head.Pt, device)
+        self.c = C.Head(A=self.A.data_ptr(), E=self.E.data_ptr(), U=self.U.data_ptr(),
+                        Pt=self.Pt.data_ptr() if self.Pt is not None else None)
+
+
+def workspace_size(dims: C.Dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(C.load().dartree_workspace_size(ctypes.byref(dims), ctypes.byref(n)), "workspace_size")
+    return int(n.value)
+
+
+class RoundBuffers:
+    """Every device output of a round for one config, plus the workspace."""
+
+    def __init__(self, cfg: I.Config, device="cuda"):
+        self.cfg = cfg
+        self.dims = make_dims(cfg)
+        n, L, K, W, B, r = cfg.n_req, cfg.L, cfg.K, cfg.W, cfg.B, cfg.r
+        i32, f32 = torch.int32, torch.float32
+        z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
+        self.cand_ids = z((n, L, K), i32)
+        self.cand_logit = z((n, L, K), f32)
+        self.h = z((n, L, r), f32)
+        self.st_tok = z((n, L, W), i32)
+        self.st_parent = z((n, L, W), i32)
+        self.st_cum = z((n, L, W), f32)
+        self.st_sbeta = z((n, L, W), f32)
+        self.st_count = z((n, L), i32)
+        self.st_state = z((n, W, r), f32)
+        self.n_sel = z((n,), i32)
+        self.tok = z((n, B), i32)
+        self.depth = z((n, B), i32)
+        self.parent = z((n, B), i32)
+        self.score = z((n, B), f32)
+        self.slot = z((n, B), i32)
+        self.mask = z((n, B, (B + 63) // 64), torch.int64)
+        self.ws_bytes = workspace_size(self.dims)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.st = C.Supertree(tok=self.st_tok.data_ptr(), parent_slot=self.st_parent.data_ptr(),
+                              cum=self.st_cum.data_ptr(), sbeta=self.st_sbeta.data_ptr(),
+                              count=self.st_count.data_ptr(), state=self.st_state.data_ptr(), next_depth=1)
+        workspace_init(self.dims, self.ws)
+
+    def numpy(self) -> Dict[str, np.ndarray]:
+        """Host copies laid out as the parity checker expects."""
+        g = lambda t: t.detach().cpu().numpy()
+        return {"cand_ids": g(self.cand_ids), "cand_logit": g(self.cand_logit), "h": g(self.h),
+                "st_tok": g(self.st_tok), "st_parent": g(self.st_parent), "st_cum": g(self.st_cum),
+                "st_sbeta": g(self.st_sbeta), "st_count": g(self.st_count), "n_sel": g(self.n_sel),
+                "tok": g(self.tok), "depth": g(self.depth), "parent": g(self.parent), "score": g(self.score),
+                "slot": g(self.slot), "mask": g(self.mask).view(np.uint64)}
+
+
+def workspace_init(dims: C.Dims, ws: torch.Tensor, stream=None):
+    _check(C.load().dartree_workspace_init(ctypes.byref(dims), _p(ws), ws.numel(), _stream(stream)),
+           "workspace_init")
+
+
+def head_states(dims: C.Dims, H: torch.Tensor, Pt: torch.Tensor, h: torch.Tensor, stream=None):
+    _check(C.load().dartree_head_states(ctypes.byref(dims), _p(H), _p(Pt), _p(h), _stream(stream)), "head_states")
+
+
+def topk_candidates(dims: C.Dims, logits: torch.Tensor, cand_ids: torch.Tensor, cand_logit: torch.Tensor,
+                    ws: torch.Tensor, stream=None):
+    _check(C.load().dartree_topk_candidates(ctypes.byref(dims), _p(logits), _p(cand_ids), _p(cand_logit), _p(ws),
+                                            ws.numel(), _stream(stream)), "topk_candidates")
+
+
+def expand_depth(dims: C.Dims, head: DeviceHead, cand_ids: torch.Tensor, cand_logit: torch.Tensor,
+                 h: torch.Tensor, rb: RoundBuffers, depth_begin: int, depth_end: int, stream=None):
+    _check(C.load().dartree_expand_depth(ctypes.byref(dims), ctypes.byref(head.c), _p(cand_ids), _p(cand_logit),
+                                         _p(h), ctypes.byref(rb.st), depth_begin, depth_end, _stream(stream)),
+           "expand_depth")
+
+
+def select_topB(dims: C.Dims, rb: RoundBuffers, stream=None):
+    _check(C.load().dartree_select_topB(ctypes.byref(dims), ctypes.byref(rb.st), _p(rb.n_sel), _p(rb.tok),
+                                        _p(rb.depth), _p(rb.parent), _p(rb.score), _p(rb.slot), _stream(stream)),
+           "select_topB")
+
+
+def tree_mask(dims: C.Dims, n_sel: torch.Tensor, parent: torch.Tensor, mask: torch.Tensor, stream=None):
+    _check(C.load().dartree_tree_mask(ctypes.byref(dims), _p(n_sel), _p(parent), _p(mask), _stream(stream)),
+           "tree_mask")
+
+
+def build_round(dims: C.Dims, head: DeviceHead, logits: torch.Tensor, H_or_h: torch.Tensor, rb: RoundBuffers,
+                stream=None):
+    """The whole round (a0..a5) through dartree_build_round."""
+    rb.st.next_depth = 1
+    _check(C.load().dartree_build_round(ctypes.byref(dims), ctypes.byref(head.c), _p(logits), _p(H_or_h),
+                                        _p(rb.cand_ids), _p(rb.cand_logit), _p(rb.h), ctypes.byref(rb.st),
+                                        _p(rb.n_sel), _p(rb.tok), _p(rb.depth), _p(rb.parent), _p(rb.score),
+                                        _p(rb.slot), _p(rb.mask), _p(rb.ws), rb.ws_bytes, _stream(stream)),
+           "build_round")
+
+
+def run_steps(dims: C.Dims, head: DeviceHead, logits: torch.Tensor, H_or_h: torch.Tensor, rb: RoundBuffers,
+              depth_chunks=None, stream=None):
+    """The round through the individual entry points: head_states (D > 0),
+    topk_candidates, expand_depth over ``depth_chunks`` ranges (default: one
+    call per depth), select_topB and tree_mask."""
+    cfg = rb.cfg
+    h = H_or_h
+    if cfg.D > 0:
+        head_states(dims, H_or_h, head.Pt, rb.h, stream)
+        h = rb.h
+    topk_candidates(dims, logits, rb.cand_ids, rb.cand_logit, rb.ws, stream)
+    rb.st.next_depth = 1
+    ranges = depth_chunks or [(d, d) for d in range(1, cfg.L + 1)]
+    for d0, d1 in ranges:
+        expand_depth(dims, head, rb.cand_ids, rb.cand_logit, h, rb, d0, d1, stream)
+    select_topB(dims, rb, stream)
+    tree_mask(dims, rb.n_sel, rb.parent, rb.mask, stream)

@@ -1,0 +1,202 @@
+/*
+ * dartree.h — C ABI of the MI355X (gfx950) draft-tree construction round.
+ *
+ * The method is DARTree's tree construction for a diffusion block drafter
+ * (marsggbo blog "DARTree: give a diffusion drafter an AR tree", sections
+ * 3.1-3.2; AINews summary "DARTree builds trees in batches before pruning").
+ * One round takes the drafter's base logits and shared representations for a
+ * block of L positions and produces a draft tree of at most B nodes that a
+ * target model verifies in one tree-attention pass:
+ *
+ *   a0  h_d = P^T H_d                        dartree_head_states
+ *   a1  top-K candidates per position        dartree_topk_candidates
+ *   a2  batched correction scoring per depth dartree_expand_depth
+ *   a3  s_beta and per-depth top-W           (same call)
+ *   a4  deferred global top-B                dartree_select_topB
+ *   a5  parent pointers + ancestor mask      dartree_select_topB, dartree_tree_mask
+ *   all of the above in one launch           dartree_build_round
+ *
+ * Conventions (every call):
+ *   - Every array argument is a DEVICE pointer allocated by the caller, row
+ *     major and contiguous, 16-byte aligned. The library never allocates,
+ *     frees or copies to the host (dartree_workspace_size tells the caller
+ *     how much scratch to allocate).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Each
+ *     call validates its arguments on the host, then enqueues its kernels and
+ *     returns without synchronising. Results are valid once the stream
+ *     reaches that point.
+ *   - On any error nothing is enqueued and outputs are untouched; the status
+ *     says why and dartree_last_error() (thread-local) gives detail.
+ *   - Device-side faults surface at the caller's next synchronisation.
+ *   - Calls are re-entrant; concurrent calls must use distinct workspaces and
+ *     distinct outputs.
+ *   - bf16 data is passed as raw 16-bit patterns.
+ *
+ * Scores (marsggbo blog, section 3.1, the score equation):
+ *   s_beta(u_1..u_d) = sum_{i<=d} log q_i(u_i) + beta * d,   beta <= 0,
+ * q_i is the corrected probability of the token among the K candidates of
+ * position i. One comparator orders nodes everywhere: s_beta descending, then
+ * depth ascending, then token id ascending, then the parent's rank (its slot
+ * in its level) ascending.
+ */
+#ifndef DARTREE_H
+#define DARTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DARTREE_OK = 0,
+  DARTREE_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, beta > 0, depth out of order */
+  DARTREE_ERR_UNSUPPORTED = 2,      /* beyond the implementation limits below, unknown dtype */
+  DARTREE_ERR_WORKSPACE_TOO_SMALL = 3,
+  DARTREE_ERR_HIP = 4               /* a HIP call failed; detail in dartree_last_error() */
+} dartree_status;
+
+typedef enum { DARTREE_F32 = 0, DARTREE_BF16 = 1 } dartree_dtype;
+
+/* Problem sizes.
+ *   n_req  requests batched in one call (>= 1)
+ *   L      block length = tree depth (1..31)
+ *   V      vocabulary size (K..262144)
+ *   K      candidates per position (1..1024), marsggbo section 3.1 (default 64)
+ *   W      nodes kept per depth (1..64), marsggbo section 3.1 (12 or 4)
+ *   B      verification-tree budget (1..1024), marsggbo section 3.1 (64)
+ *   r      head rank (1..1024); W*r <= 8192 and W*K <= 8192
+ *   D      drafter hidden size for dartree_head_states (0 = h supplied directly)
+ *   beta   depth term of s_beta; must be finite and <= 0 (Lemma 1)
+ *   logits_dtype, weight_dtype: dartree_dtype of the base logits and of the
+ *          head weights (A, E, U, Pt) and H. */
+typedef struct {
+  int32_t n_req, L, V, K, W, B, r, D;
+  float beta;
+  int32_t logits_dtype;
+  int32_t weight_dtype;
+} dartree_dims;
+
+/* Correction head (a declared low-rank stand-in; the pages do not define the
+ * head's architecture). Row-major, weight_dtype:
+ *   A  [r][r]  state transition, (A s)[j] = sum_m A[j][m] s[m]
+ *   E  [V][r]  token embeddings
+ *   U  [V][r]  output rows: corrected logit z_c = Lbase[c] + <s_parent, U[c]>
+ *   Pt [r][D]  input projection stored output-major, Pt[j][i] = P[i][j]
+ *              (may be NULL when D == 0)
+ * Child state: s = tanh(A s_parent + E[u] + h_d); the root state is h_0. */
+typedef struct {
+  const void* A;
+  const void* E;
+  const void* U;
+  const void* Pt;
+} dartree_head;
+
+/* The supertree: W slots per depth, kept in rank order (slot 0 best).
+ *   tok         [n][L][W] int32  token id (pad -1)
+ *   parent_slot [n][L][W] int32  slot of the parent in depth d-1 (depth 1: 0)
+ *   cum         [n][L][W] float  sum of log q along the path (pad -inf)
+ *   sbeta       [n][L][W] float  cum + beta * d (pad -inf)
+ *   count       [n][L]    int32  kept nodes per depth
+ *   state       [n][W][r] float  head states of the deepest expanded level,
+ *                                read back by the next dartree_expand_depth
+ *   next_depth  HOST field: the next depth dartree_expand_depth expects; set
+ *               it to 1 before a round; each successful call advances it. */
+typedef struct {
+  int32_t* tok;
+  int32_t* parent_slot;
+  float* cum;
+  float* sbeta;
+  int32_t* count;
+  float* state;
+  int32_t next_depth;
+} dartree_supertree;
+
+/* Human-readable status name; never NULL. */
+const char* dartree_status_string(dartree_status s);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* dartree_last_error(void);
+/* ABI version of this library. */
+int32_t dartree_version(void);
+
+/* Scratch needed by dartree_topk_candidates and dartree_build_round for
+ * these dims (bytes). */
+dartree_status dartree_workspace_size(const dartree_dims* dims, size_t* bytes);
+
+/* Prepare a freshly allocated workspace (zeroes its per-row tickets). The
+ * kernels leave the tickets at zero when they finish, so this is needed once
+ * per allocation, not per round. */
+dartree_status dartree_workspace_init(const dartree_dims* dims, void* ws, size_t ws_bytes, void* stream);
+
+/* Step a0 (synthetic head input; marsggbo section 3.1: one block-parallel
+ * drafter forward gives the shared representations H_d): for every request
+ * and position, h[n][L][r] = P^T H[n][L][D], with Pt = P^T as in
+ * dartree_head. H and Pt use weight_dtype; h is fp32. Requires D >= 1. */
+dartree_status dartree_head_states(const dartree_dims* dims, const void* H, const void* Pt, float* h,
+                                   void* stream);
+
+/* Step a1 (marsggbo section 3.1, candidate generation; AINews: the 64 best
+ * candidates per position): for each of the n*L rows of logits[n][L][V]
+ * (logits_dtype; row i holds depth i+1), the K largest values ordered by value
+ * descending, ties by token id ascending (values compare numerically, so -0 ==
+ * +0). Outputs cand_ids[n][L][K] int32 and cand_logit[n][L][K] fp32 (the exact
+ * widened logit). Needs a workspace of dartree_workspace_size bytes that was
+ * prepared once by dartree_workspace_init. Logits must be finite. */
+dartree_status dartree_topk_candidates(const dartree_dims* dims, const void* logits, int32_t* cand_ids,
+                                       float* cand_logit, void* ws, size_t ws_bytes, void* stream);
+
+/* Steps a2 + a3 (marsggbo section 3.1, depth-by-depth expansion and the score
+ * equation; AINews: one batched head call per depth): expands depths
+ * depth_begin..depth_end (1 <= depth_begin <= depth_end <= L, and depth_begin
+ * must equal st->next_depth). At depth d every parent of depth d-1 (the root
+ * for d = 1) scores all K candidates of position d:
+ *   log q = log-softmax_K(cand_logit + <s_parent, U[cand]>),
+ *   cum = cum_parent + log q,  s_beta = cum + beta*d,
+ * the W best children under the comparator are kept (slot order), and for
+ * d < L each survivor gets s = tanh(A s_parent + E[u] + h_d).
+ * cand_ids/cand_logit as produced by dartree_topk_candidates (ids outside
+ * [0, V) are read as 0); h[n][L][r] fp32 (row d is used by depth-d states, row
+ * 0 is the root state). Writes levels depth_begin..depth_end of *st and, when
+ * depth_end < L, st->state; advances st->next_depth to depth_end + 1. */
+dartree_status dartree_expand_depth(const dartree_dims* dims, const dartree_head* head, const int32_t* cand_ids,
+                                    const float* cand_logit, const float* h, dartree_supertree* st,
+                                    int32_t depth_begin, int32_t depth_end, void* stream);
+
+/* Steps a4 + a5 (marsggbo section 3.1, deferred pruning and Lemma 1): from the
+ * complete supertree (all L depths expanded), select the min(B, nodes) best
+ * nodes under the comparator (prefix-closed for beta <= 0) and emit them in
+ * breadth-first order: depth ascending, then the parent's emitted index, then
+ * token id. Outputs per request: n_sel[n]; tok, depth, parent, score, slot
+ * [n][B] (parent -1 = the anchor token, slot = the node's slot in its supertree
+ * level); entries >= n_sel are tok -1, depth 0, parent -2, score -inf,
+ * slot -1. */
+dartree_status dartree_select_topB(const dartree_dims* dims, const dartree_supertree* st, int32_t* n_sel,
+                                   int32_t* tok, int32_t* depth, int32_t* parent, float* score, int32_t* slot,
+                                   void* stream);
+
+/* Step a5 (marsggbo section 3.2, tree-attention verification): ancestor
+ * bitmask mask[n][B][ceil(B/64)] uint64. Row i (i < n_sel) has bit j (bit j%64
+ * of word j/64) set iff j == i or node j is an ancestor of node i under the
+ * parent array (the anchor, -1, has no bit); rows >= n_sel are zero. Parent
+ * pointers outside [-1, i) end a chain. */
+dartree_status dartree_tree_mask(const dartree_dims* dims, const int32_t* n_sel, const int32_t* parent,
+                                 uint64_t* mask, void* stream);
+
+/* The whole round (a0..a5) in one call. H_or_h is H[n][L][D] (weight_dtype)
+ * when D > 0, else h[n][L][r] fp32. h receives the head inputs when D > 0
+ * (may equal H_or_h's role otherwise and is then not written). Writes the
+ * candidates, the supertree (st->next_depth must be 1; it ends at L + 1) and
+ * the tree outputs of dartree_select_topB plus the mask. ws as for
+ * dartree_topk_candidates. */
+dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head* head, const void* logits,
+                                   const void* H_or_h, int32_t* cand_ids, float* cand_logit, float* h,
+                                   dartree_supertree* st, int32_t* n_sel, int32_t* tok, int32_t* depth,
+                                   int32_t* parent, float* score, int32_t* slot, uint64_t* mask, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DARTREE_H */

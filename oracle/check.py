@@ -235,20 +235,23 @@ def check_selection(levels: List[List[O.Node]], gst: GpuSupertree, sel: GpuSelec
 
 
 def check_round(cfg, head, rnd, gpu: Dict[str, np.ndarray], tol: float = 1e-4,
-                oracle_h: Optional[np.ndarray] = None) -> Report:
+                oracle_h: Optional[np.ndarray] = None, requests=None) -> Report:
     """Full-round parity for every request. ``gpu`` holds numpy copies of the
     HIP path's outputs: cand_ids, cand_logit [n][L][K]; h [n][L][r] (when
     D > 0); st_tok, st_parent, st_cum, st_sbeta [n][L][W]; st_count [n][L];
-    n_sel [n]; tok, depth, parent, score, slot [n][B]; mask [n][B][words]."""
+    n_sel [n]; tok, depth, parent, score, slot [n][B]; mask [n][B][words].
+    ``requests`` restricts the check to a sample of requests."""
     wd = head.dtype
     A, E, U = O.widen(head.A, wd), O.widen(head.E, wd), O.widen(head.U, wd)
-    logits = O.widen(rnd.logits, cfg.logits_dtype)
+    qs = list(range(cfg.n_req)) if requests is None else list(requests)
+    logits = {q: O.widen(rnd.logits[q], cfg.logits_dtype) for q in qs}
     if cfg.D > 0:
-        h_all = oracle_h if oracle_h is not None else O.head_states(O.widen(rnd.H, wd), O.widen(head.Pt, wd))
+        Pt = O.widen(head.Pt, wd)
+        h_all = {q: (oracle_h[q] if oracle_h is not None else O.head_states(O.widen(rnd.H[q], wd), Pt)) for q in qs}
     else:
-        h_all = np.asarray(rnd.h, np.float64)
+        h_all = {q: np.asarray(rnd.h[q], np.float64) for q in qs}
     rep = Report()
-    for q in range(cfg.n_req):
+    for q in qs:
         where = f"[{cfg.name} req {q}]"
         check_candidates(gpu["cand_ids"][q], gpu["cand_logit"][q], logits[q], cfg.K, where)
         if cfg.D > 0 and "h" in gpu:

@@ -1,0 +1,141 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects invalid arguments on the host before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from diffusion_drafter_tree_amd import _lib as C
+from diffusion_drafter_tree_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dartree.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dartree_[a-z_A-Z0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(C.LIB_PATH):
+        pytest.fail("libdartree.so is not built (run __graft_entry__.build())")
+    return C.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(C.SIGNATURES), "binding and header disagree"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.dartree_version() == 1
+    assert C.status_string(0) == "DARTREE_OK"
+    assert C.status_string(3) == "DARTREE_ERR_WORKSPACE_TOO_SMALL"
+    assert C.status_string(99) == "DARTREE_UNKNOWN_STATUS"
+
+
+def dims(**kw):
+    base = dict(n_req=1, L=16, V=151936, K=64, W=12, B=64, r=256, D=2560, beta=-0.15,
+                logits_dtype=C.BF16, weight_dtype=C.BF16)
+    base.update(kw)
+    return C.Dims(**base)
+
+
+def ws_size(lib, d):
+    n = ctypes.c_size_t(0)
+    st = lib.dartree_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_values(lib):
+    st, n = ws_size(lib, dims())
+    assert st == C.OK
+    # 16 rows of tickets, then 16 rows x 19 chunks x 64 keys of 8 bytes
+    assert n == 256 + 16 * 19 * 64 * 8
+    st, n = ws_size(lib, dims(V=1024, L=6, K=8, W=3, B=16, r=16, D=0, logits_dtype=C.F32, weight_dtype=C.F32))
+    assert st == C.OK and n >= 6 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(beta=0.1), C.ERR_INVALID_ARGUMENT),
+    (dict(beta=float("nan")), C.ERR_INVALID_ARGUMENT),
+    (dict(beta=float("inf")), C.ERR_INVALID_ARGUMENT),
+    (dict(K=0), C.ERR_INVALID_ARGUMENT),
+    (dict(n_req=0), C.ERR_INVALID_ARGUMENT),
+    (dict(K=200000), C.ERR_INVALID_ARGUMENT),
+    (dict(D=-1), C.ERR_INVALID_ARGUMENT),
+    (dict(L=32), C.ERR_UNSUPPORTED),
+    (dict(K=2048), C.ERR_UNSUPPORTED),
+    (dict(W=65), C.ERR_UNSUPPORTED),
+    (dict(B=1025), C.ERR_UNSUPPORTED),
+    (dict(r=1056), C.ERR_UNSUPPORTED),
+    (dict(V=300000), C.ERR_UNSUPPORTED),
+    (dict(W=64, r=256), C.ERR_UNSUPPORTED),
+    (dict(W=16, K=1024), C.ERR_UNSUPPORTED),
+    (dict(logits_dtype=7), C.ERR_UNSUPPORTED),
+])
+def test_invalid_dims_are_rejected(lib, kw, status):
+    st, _ = ws_size(lib, dims(**kw))
+    assert st == status, C.last_error()
+    assert C.last_error() != ""
+
+
+def test_beta_zero_is_allowed(lib):
+    assert ws_size(lib, dims(beta=0.0))[0] == C.OK
+    assert ws_size(lib, dims(beta=-0.0))[0] == C.OK
+
+
+def test_null_and_misaligned_pointers_rejected_before_any_launch(lib):
+    d = dims()
+    st, n = ws_size(lib, d)
+    fake = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+    mis = ctypes.c_void_p(0x10004)
+    s = ctypes.c_void_p(None)
+    assert lib.dartree_topk_candidates(ctypes.byref(d), None, fake, fake, fake, n, s) == C.ERR_INVALID_ARGUMENT
+    assert "logits" in C.last_error()
+    assert lib.dartree_topk_candidates(ctypes.byref(d), mis, fake, fake, fake, n, s) == C.ERR_INVALID_ARGUMENT
+    assert "aligned" in C.last_error()
+    assert lib.dartree_topk_candidates(ctypes.byref(d), fake, fake, fake, fake, n - 1, s) == \
+        C.ERR_WORKSPACE_TOO_SMALL
+    assert lib.dartree_head_states(ctypes.byref(dims(D=0)), fake, fake, fake, s) == C.ERR_INVALID_ARGUMENT
+    assert lib.dartree_tree_mask(ctypes.byref(d), fake, fake, ctypes.c_void_p(0x10004), s) == C.ERR_INVALID_ARGUMENT
+
+
+def test_expand_depth_order_is_enforced(lib):
+    d = dims()
+    fake = 0x10000
+    head = C.Head(A=fake, E=fake, U=fake, Pt=fake)
+    st = C.Supertree(tok=fake, parent_slot=fake, cum=fake, sbeta=fake, count=fake, state=fake, next_depth=1)
+    s = ctypes.c_void_p(None)
+    f = ctypes.c_void_p(fake)
+    # depth_begin must equal next_depth
+    assert lib.dartree_expand_depth(ctypes.byref(d), ctypes.byref(head), f, f, f, ctypes.byref(st), 2, 2, s) == \
+        C.ERR_INVALID_ARGUMENT
+    # range outside [1, L]
+    assert lib.dartree_expand_depth(ctypes.byref(d), ctypes.byref(head), f, f, f, ctypes.byref(st), 1, 17, s) == \
+        C.ERR_INVALID_ARGUMENT
+    assert lib.dartree_expand_depth(ctypes.byref(d), ctypes.byref(head), f, f, f, ctypes.byref(st), 1, 0, s) == \
+        C.ERR_INVALID_ARGUMENT
+    assert st.next_depth == 1
+    # select needs a complete supertree
+    assert lib.dartree_select_topB(ctypes.byref(d), ctypes.byref(st), f, f, f, f, f, f, s) == C.ERR_INVALID_ARGUMENT
+    assert "incomplete" in C.last_error()
+    # a round must start at depth 1
+    st.next_depth = 5
+    assert lib.dartree_build_round(ctypes.byref(d), ctypes.byref(head), f, f, f, f, f, ctypes.byref(st), f, f, f, f,
+                                   f, f, f, f, 1 << 20, s) == C.ERR_INVALID_ARGUMENT
+
+
+def test_binding_config_dims_match_header_limits():
+    from diffusion_drafter_tree_amd import ops
+    for name in I.CONFIG_ORDER:
+        d = ops.make_dims(I.CONFIGS[name])
+        st, _ = ws_size(C.load(), d)
+        assert st == C.OK, (name, C.last_error())

@@ -1,0 +1,201 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: candidate ids, parents, emission and masks bit-exact; fp32 scores within
+1e-4 absolute of the fp64 oracle; kept sets may differ only at near-ties
+(gap <= 1e-4), which the tie-aware checker replays.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from diffusion_drafter_tree_amd import inputs as I
+from diffusion_drafter_tree_amd import ops
+from oracle import check as CK
+from oracle import dartree_oracle as O
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+def say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+_heads = {}
+
+
+def device_head(cfg, seed=0):
+    key = (cfg, seed)
+    if key not in _heads:
+        hd = I.make_head(cfg, seed)
+        _heads[key] = (hd, ops.DeviceHead(hd))
+    return _heads[key]
+
+
+def run_gpu(cfg, hd, dhd, rnd, mode="build", chunks=None):
+    rb = ops.RoundBuffers(cfg)
+    logits = ops.to_device(rnd.logits)
+    hin = ops.to_device(rnd.H if cfg.D > 0 else rnd.h)
+    if mode == "build":
+        ops.build_round(rb.dims, dhd, logits, hin, rb)
+    else:
+        ops.run_steps(rb.dims, dhd, logits, hin, rb, depth_chunks=chunks)
+    torch.cuda.synchronize()
+    return rb.numpy()
+
+
+def check(cfg, seed=0, t=0, mode="build", chunks=None, requests=None):
+    hd, dhd = device_head(cfg, seed)
+    rnd = I.make_round(cfg, seed, t)
+    say(f"case {cfg.name} n={cfg.n_req} V={cfg.V} L={cfg.L} K={cfg.K} W={cfg.W} B={cfg.B} r={cfg.r} D={cfg.D} "
+        f"seed={seed} t={t} mode={mode}")
+    out = run_gpu(cfg, hd, dhd, rnd, mode, chunks)
+    rep = CK.check_round(cfg, hd, rnd, out, tol=TOL, requests=requests)
+    say(f"  ok: nodes={rep.nodes_checked} ties(level/topB)={rep.tie_events_level}/{rep.tie_events_topB} "
+        f"max|dscore|={rep.max_score_err:.2e} max|dh|={rep.max_h_err:.2e}")
+    return out, rep
+
+
+SMALL = {
+    "tiny_f32": I.CONFIGS["tiny"],
+    "bf16_ragged_odd_V": I.small_variant("qwen3_4b", n_req=3, V=5003, L=5, K=40, W=7, B=20, r=64, D=96),
+    "bf16_multichunk": I.small_variant("qwen3_4b", n_req=2, V=40000, L=4, K=64, W=12, B=30, r=128, D=256),
+    "f32_multichunk_valu": I.small_variant("tiny", n_req=2, V=20000, L=7, K=16, W=5, B=25, r=24, D=40),
+    "bf16_r48_valu": I.small_variant("qwen3_4b", n_req=1, V=3000, L=6, K=24, W=6, B=30, r=48, D=64),
+    "wide_W32_K256": I.small_variant("qwen3_4b", n_req=2, V=9000, L=6, K=256, W=32, B=100, r=128, D=128),
+    "big_B200": I.small_variant("qwen3_4b", n_req=1, V=3000, L=8, K=30, W=40, B=200, r=32, D=64),
+    "chain_W1": I.small_variant("qwen3_4b", n_req=2, V=4000, L=9, K=32, W=1, B=6, r=64, D=64),
+    "beta0": I.small_variant("qwen3_4b", n_req=1, V=4000, L=6, K=32, W=5, B=20, r=64, D=64, beta=0.0),
+    "beta_neg5": I.small_variant("qwen3_4b", n_req=1, V=4000, L=6, K=32, W=5, B=12, r=64, D=64, beta=-5.0),
+    "whole_supertree_WL_le_B": I.small_variant("qwen3_4b", n_req=1, V=4000, L=5, K=16, W=4, B=64, r=64, D=64),
+    "K_eq_V": I.small_variant("tiny", V=48, K=48, L=4, W=6, B=10, r=16),
+    "L1": I.small_variant("qwen3_4b", n_req=2, V=5000, L=1, K=20, W=5, B=3, r=32, D=32),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_configs_build_round(name):
+    check(SMALL[name].with_(name=name))
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "bf16_multichunk", "f32_multichunk_valu", "wide_W32_K256"])
+def test_step_entry_points_match_fused_round(name):
+    cfg = SMALL[name].with_(name=name)
+    a, _ = check(cfg, mode="build")
+    b, _ = check(cfg, mode="steps")
+    c, _ = check(cfg, mode="steps", chunks=[(1, 2), (3, cfg.L)])
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+        assert np.array_equal(a[k], c[k]), k
+
+
+def test_metric_config_qwen3_4b():
+    for t in range(2):
+        check(I.CONFIGS["qwen3_4b"], t=t)
+
+
+def test_fixed_width_qwen3_8b():
+    check(I.CONFIGS["fixed_w4_qwen3_8b"])
+
+
+def test_concurrent_c4():
+    check(I.CONFIGS["concurrent_c4"])
+
+
+def test_stress_64req_sampled():
+    check(I.CONFIGS["stress_64req"], requests=[0, 31, 63])
+
+
+def test_repeat_runs_are_bit_identical():
+    cfg = I.CONFIGS["qwen3_4b"]
+    hd, dhd = device_head(cfg)
+    rnd = I.make_round(cfg, 0, 5)
+    say("case repeat-determinism qwen3_4b x4")
+    outs = [run_gpu(cfg, hd, dhd, rnd) for _ in range(4)]
+    for o in outs[1:]:
+        for k in o:
+            assert np.array_equal(o[k], outs[0][k]), k
+
+
+def _topk_rows(logits_bits, K, dtype="bf16"):
+    """Run only the candidate step over [rows][V] logits."""
+    rows, V = logits_bits.shape
+    cfg = I.CONFIGS["qwen3_4b"].with_(n_req=1, L=rows, V=V, K=K, W=1, B=1, r=32, D=0, logits_dtype=dtype,
+                                      weight_dtype="f32")
+    dims = ops.make_dims(cfg)
+    lg = ops.to_device(logits_bits.reshape(1, rows, V))
+    ids = torch.zeros((1, rows, K), dtype=torch.int32, device="cuda")
+    vals = torch.zeros((1, rows, K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ops.workspace_size(dims), dtype=torch.uint8, device="cuda")
+    ops.workspace_init(dims, ws)
+    ops.topk_candidates(dims, lg, ids, vals, ws)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy()[0], vals.cpu().numpy()[0]
+
+
+@pytest.mark.parametrize("K", [64, 512, 1024])
+def test_topk_tie_heavy_rows_bit_exact(K):
+    rng = np.random.default_rng(K)
+    V = 151936
+    rows = []
+    rows.append(np.round(rng.normal(0, 2, V) * 4) / 4)            # heavy exact ties
+    rows.append(np.full(V, 1.5))                                   # all equal
+    r = np.zeros(V)
+    r[rng.choice(V, V // 3, replace=False)] = -0.0                 # +0 / -0 mix
+    r[rng.choice(V, 5, replace=False)] = 3.0
+    rows.append(r)
+    rows.append(rng.normal(0, 2, V))
+    rows.append(np.round(rng.normal(0, 2, V)))                     # integer ties
+    x = np.stack(rows).astype(np.float32)
+    bits = I.f32_to_bf16_bits(x)
+    say(f"case topk tie-heavy bf16 rows={x.shape[0]} V={V} K={K}")
+    ids, vals = _topk_rows(bits, K)
+    ref = I.bf16_bits_to_f32(bits).astype(np.float64)
+    CK.check_candidates(ids, vals, ref, K, where=f"topk K={K}")
+    say(f"case topk tie-heavy f32 rows={x.shape[0]} V={V} K={K}")
+    ids, vals = _topk_rows(x, K, dtype="f32")
+    CK.check_candidates(ids, vals, x.astype(np.float64), K, where=f"topk f32 K={K}")
+
+
+def test_topk_small_and_ragged_rows():
+    rng = np.random.default_rng(7)
+    for V, K in [(1, 1), (7, 7), (9, 3), (4099, 64), (8192, 64), (8193, 100), (16385, 1024), (24577, 17)]:
+        x = (np.round(rng.normal(0, 1, (3, V)) * 2) / 2).astype(np.float32)
+        bits = I.f32_to_bf16_bits(x)
+        say(f"case topk small V={V} K={K}")
+        ids, vals = _topk_rows(bits, K)
+        CK.check_candidates(ids, vals, I.bf16_bits_to_f32(bits).astype(np.float64), K, where=f"V={V}")
+
+
+def test_tree_mask_on_handmade_parents():
+    B = 130
+    rng = np.random.default_rng(3)
+    par = np.full((2, B), -2, np.int32)
+    n_sel = np.array([B, 70], np.int32)
+    for q in range(2):
+        for i in range(n_sel[q]):
+            par[q, i] = rng.integers(-1, i) if i > 0 else -1
+    par[0, 50] = 60      # forward pointer: ends the chain
+    par[0, 51] = -7      # invalid: ends the chain
+    cfg = I.small_variant("tiny", n_req=2, B=B)
+    dims = ops.make_dims(cfg)
+    words = (B + 63) // 64
+    mask = torch.full((2, B, words), -1, dtype=torch.int64, device="cuda")
+    say("case tree_mask handmade parents")
+    ops.tree_mask(dims, torch.from_numpy(n_sel).cuda(), torch.from_numpy(par).cuda(), mask)
+    torch.cuda.synchronize()
+    got = mask.cpu().numpy().view(np.uint64)
+    for q in range(2):
+        exp = np.zeros((B, words), np.uint64)
+        for i in range(n_sel[q]):
+            j = i
+            for _ in range(B + 1):
+                exp[i, j // 64] |= np.uint64(1) << np.uint64(j % 64)
+                p = par[q, j]
+                if p >= j or p < -1 or p == -1:
+                    break
+                j = p
+        assert np.array_equal(got[q], exp), q
