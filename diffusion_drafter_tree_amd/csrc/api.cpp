@@ -61,24 +61,23 @@ dartree_status check_dims(const dartree_dims* d) {
 }
 
 struct WsLayout {
-  dartree::TopkPlan plan;
-  size_t tickets_off, lists_off, total;
+  dartree::ScanPlan plan;
+  size_t lists_off, total;
 };
 
 WsLayout ws_layout(const dartree_dims* d) {
   WsLayout w{};
   const int rows = d->n_req * d->L;
-  w.plan = dartree::topk_plan(rows, d->V, d->K, d->logits_dtype == DARTREE_BF16);
-  w.tickets_off = 0;
-  w.lists_off = (w.plan.ticket_bytes + 255) & ~(size_t)255;
-  w.total = w.lists_off + w.plan.list_bytes;
+  w.plan = dartree::scan_plan(rows, d->V, d->K, d->logits_dtype == DARTREE_BF16);
+  w.lists_off = 0;
+  w.total = w.plan.list_bytes;
   if (w.total == 0) w.total = 256;
   return w;
 }
 
 dartree_status check_ws(const dartree_dims* d, void* ws, size_t ws_bytes, WsLayout* out) {
   *out = ws_layout(d);
-  if (out->plan.nv == 0) return fail(DARTREE_ERR_UNSUPPORTED, "no top-K plan for V=%d K=%d", d->V, d->K);
+  if (!out->plan.ok) return fail(DARTREE_ERR_UNSUPPORTED, "no top-K plan for V=%d K=%d", d->V, d->K);
   REQ_PTR(ws, 256);
   if (ws_bytes < out->total)
     return fail(DARTREE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", ws_bytes, out->total);
@@ -122,21 +121,23 @@ dartree_status check_tree_out(const int32_t* n_sel, const int32_t* tok, const in
     if (_s != DARTREE_OK) return _s;          \
   } while (0)
 
-dartree::ExpandArgs expand_args(const dartree_dims* dims, const dartree_head* head, const int32_t* cand_ids,
-                                const float* cand_logit, const float* h, const dartree_supertree* st, int d0,
-                                int d1) {
-  dartree::ExpandArgs a{};
+dartree::TreeArgs tree_args(const dartree_dims* dims, const dartree_head* head, const int32_t* cand_ids,
+                           const float* cand_logit, const float* h, const dartree_supertree* st, int d0, int d1) {
+  dartree::TreeArgs a{};
   a.n_req = dims->n_req;
   a.L = dims->L;
   a.V = dims->V;
   a.K = dims->K;
   a.W = dims->W;
+  a.B = dims->B;
   a.r = dims->r;
   a.beta = dims->beta;
   a.bf16 = dims->weight_dtype == DARTREE_BF16;
-  a.A = head->A;
-  a.E = head->E;
-  a.U = head->U;
+  if (head) {
+    a.A = head->A;
+    a.E = head->E;
+    a.U = head->U;
+  }
   a.cand_ids = cand_ids;
   a.cand_logit = cand_logit;
   a.h = h;
@@ -151,24 +152,25 @@ dartree::ExpandArgs expand_args(const dartree_dims* dims, const dartree_head* he
   return a;
 }
 
-dartree::SelectArgs select_args(const dartree_dims* dims, const dartree_supertree* st, int32_t* n_sel, int32_t* tok,
-                                int32_t* depth, int32_t* parent, float* score, int32_t* slot) {
-  dartree::SelectArgs a{};
-  a.n_req = dims->n_req;
-  a.L = dims->L;
-  a.W = dims->W;
-  a.B = dims->B;
-  a.st_tok = st->tok;
-  a.st_parent = st->parent_slot;
-  a.st_sbeta = st->sbeta;
-  a.st_count = st->count;
+void set_tree_out(dartree::TreeArgs& a, int32_t* n_sel, int32_t* tok, int32_t* depth, int32_t* parent, float* score,
+                  int32_t* slot, uint64_t* mask) {
+  a.do_select = true;
+  a.do_mask = mask != nullptr;
   a.n_sel = n_sel;
   a.tok = tok;
   a.depth = depth;
   a.parent = parent;
   a.score = score;
   a.slot = slot;
-  return a;
+  a.mask = mask;
+}
+
+dartree_status check_tree_plan(const dartree::TreeArgs& a, dartree::TreePlan* p) {
+  *p = dartree::tree_plan(a);
+  if (!p->ok)
+    return fail(DARTREE_ERR_UNSUPPORTED, "working set of %zu bytes exceeds the 160 KiB of LDS (K=%d W=%d r=%d L=%d B=%d)",
+                p->smem, a.K, a.W, a.r, a.L, a.B);
+  return DARTREE_OK;
 }
 
 }  // namespace
@@ -195,7 +197,7 @@ dartree_status dartree_workspace_size(const dartree_dims* dims, size_t* bytes) {
   TRY(check_dims(dims));
   if (!bytes) return fail(DARTREE_ERR_INVALID_ARGUMENT, "bytes is NULL");
   WsLayout w = ws_layout(dims);
-  if (w.plan.nv == 0) return fail(DARTREE_ERR_UNSUPPORTED, "no top-K plan for V=%d K=%d", dims->V, dims->K);
+  if (!w.plan.ok) return fail(DARTREE_ERR_UNSUPPORTED, "no top-K plan for V=%d K=%d", dims->V, dims->K);
   *bytes = w.total;
   return DARTREE_OK;
 }
@@ -205,9 +207,7 @@ dartree_status dartree_workspace_init(const dartree_dims* dims, void* ws, size_t
   TRY(check_dims(dims));
   WsLayout w;
   TRY(check_ws(dims, ws, ws_bytes, &w));
-  hipError_t e = dartree::launch_fill_u32(static_cast<char*>(ws) + w.tickets_off, w.plan.ticket_bytes / 4, 0u,
-                                          static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "workspace_init");
+  (void)stream;   // the current kernels keep no state in the workspace between calls
   return DARTREE_OK;
 }
 
@@ -218,8 +218,8 @@ dartree_status dartree_head_states(const dartree_dims* dims, const void* H, cons
   REQ_PTR(H, 16);
   REQ_PTR(Pt, 16);
   REQ_PTR(h, 4);
-  hipError_t e = dartree::launch_head_states(dims->weight_dtype == DARTREE_BF16, H, Pt, h, dims->n_req * dims->L,
-                                             dims->D, dims->r, static_cast<hipStream_t>(stream));
+  hipError_t e = dartree::launch_head(dims->weight_dtype == DARTREE_BF16, H, Pt, h, dims->n_req * dims->L, dims->D,
+                                      dims->r, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "head_states launch");
   return DARTREE_OK;
 }
@@ -233,12 +233,21 @@ dartree_status dartree_topk_candidates(const dartree_dims* dims, const void* log
   REQ_PTR(cand_logit, 4);
   WsLayout w;
   TRY(check_ws(dims, ws, ws_bytes, &w));
-  char* wsb = static_cast<char*>(ws);
-  hipError_t e = dartree::launch_topk(w.plan, dims->logits_dtype == DARTREE_BF16, logits, dims->V, dims->K,
-                                      reinterpret_cast<uint64_t*>(wsb + w.lists_off),
-                                      reinterpret_cast<unsigned int*>(wsb + w.tickets_off), cand_ids, cand_logit,
-                                      static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "topk launch");
+  const bool bf = dims->logits_dtype == DARTREE_BF16;
+  const int rows = dims->n_req * dims->L;
+  dartree::ScanArgs sa{};
+  sa.logits = logits;
+  sa.rows = rows;
+  sa.V = dims->V;
+  sa.K = dims->K;
+  sa.lists = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + w.lists_off);
+  sa.cand_ids = cand_ids;
+  sa.cand_logit = cand_logit;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dartree::launch_scan(w.plan, bf, sa, s);
+  if (e != hipSuccess) return hip_fail(e, "scan launch");
+  e = dartree::launch_merge(w.plan, rows, dims->K, bf, sa.lists, cand_ids, cand_logit, s);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
   return DARTREE_OK;
 }
 
@@ -250,15 +259,17 @@ dartree_status dartree_expand_depth(const dartree_dims* dims, const dartree_head
   TRY(check_head(dims, head));
   REQ_PTR(cand_ids, 4);
   REQ_PTR(cand_logit, 4);
-  REQ_PTR(h, 4);
+  REQ_PTR(h, 16);
   TRY(check_supertree(st));
   if (depth_begin != st->next_depth)
     return fail(DARTREE_ERR_INVALID_ARGUMENT, "depth_begin=%d but the supertree expects depth %d", depth_begin,
                 st->next_depth);
   if (depth_begin < 1 || depth_end < depth_begin || depth_end > dims->L)
     return fail(DARTREE_ERR_INVALID_ARGUMENT, "depth range [%d, %d] outside [1, %d]", depth_begin, depth_end, dims->L);
-  hipError_t e = dartree::launch_expand(expand_args(dims, head, cand_ids, cand_logit, h, st, depth_begin, depth_end),
-                                        static_cast<hipStream_t>(stream));
+  dartree::TreeArgs ta = tree_args(dims, head, cand_ids, cand_logit, h, st, depth_begin, depth_end);
+  dartree::TreePlan tp;
+  TRY(check_tree_plan(ta, &tp));
+  hipError_t e = dartree::launch_tree(tp, ta, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "expand launch");
   st->next_depth = depth_end + 1;
   return DARTREE_OK;
@@ -274,8 +285,11 @@ dartree_status dartree_select_topB(const dartree_dims* dims, const dartree_super
     return fail(DARTREE_ERR_INVALID_ARGUMENT, "supertree incomplete: next_depth=%d, expected %d", st->next_depth,
                 dims->L + 1);
   TRY(check_tree_out(n_sel, tok, depth, parent, score, slot));
-  hipError_t e = dartree::launch_select(select_args(dims, st, n_sel, tok, depth, parent, score, slot),
-                                        static_cast<hipStream_t>(stream));
+  dartree::TreeArgs ta = tree_args(dims, nullptr, nullptr, nullptr, nullptr, st, 1, 0);
+  set_tree_out(ta, n_sel, tok, depth, parent, score, slot, nullptr);
+  dartree::TreePlan tp;
+  TRY(check_tree_plan(ta, &tp));
+  hipError_t e = dartree::launch_tree(tp, ta, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return DARTREE_OK;
 }
@@ -305,7 +319,7 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
   REQ_PTR(cand_ids, 4);
   REQ_PTR(cand_logit, 4);
   if (dims->D > 0) {
-    REQ_PTR(h, 4);
+    REQ_PTR(h, 16);
     REQ_PTR(head->Pt, 16);
   }
   TRY(check_supertree(st));
@@ -316,26 +330,45 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
   WsLayout w;
   TRY(check_ws(dims, ws, ws_bytes, &w));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool lbf = dims->logits_dtype == DARTREE_BF16, wbf = dims->weight_dtype == DARTREE_BF16;
+  const int rows = dims->n_req * dims->L;
   const float* hin = static_cast<const float*>(H_or_h);
-  hipError_t e;
-  if (dims->D > 0) {
-    e = dartree::launch_head_states(dims->weight_dtype == DARTREE_BF16, H_or_h, head->Pt, h, dims->n_req * dims->L,
-                                    dims->D, dims->r, s);
-    if (e != hipSuccess) return hip_fail(e, "head_states launch");
-    hin = h;
+  dartree::TreeArgs ta = tree_args(dims, head, cand_ids, cand_logit, dims->D > 0 ? h : hin, st, 1, dims->L);
+  set_tree_out(ta, n_sel, tok, depth, parent, score, slot, mask);
+  dartree::TreePlan tp;
+  TRY(check_tree_plan(ta, &tp));
+  // launch 1: the logits scan, with the head projection tiles riding along
+  dartree::ScanArgs sa{};
+  sa.logits = logits;
+  sa.rows = rows;
+  sa.V = dims->V;
+  sa.K = dims->K;
+  sa.lists = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + w.lists_off);
+  sa.cand_ids = cand_ids;
+  sa.cand_logit = cand_logit;
+  const bool fuse_head = dims->D > 0 && dartree::head_mfma_ok(wbf, H_or_h, head->Pt, dims->D, dims->r);
+  if (fuse_head) {
+    sa.H = static_cast<const uint16_t*>(H_or_h);
+    sa.Pt = static_cast<const uint16_t*>(head->Pt);
+    sa.h = h;
+    sa.M = rows;
+    sa.D = dims->D;
+    sa.r = dims->r;
+    sa.n_head = (dims->r / 16) * ((rows + 15) / 16);
   }
-  char* wsb = static_cast<char*>(ws);
-  e = dartree::launch_topk(w.plan, dims->logits_dtype == DARTREE_BF16, logits, dims->V, dims->K,
-                           reinterpret_cast<uint64_t*>(wsb + w.lists_off),
-                           reinterpret_cast<unsigned int*>(wsb + w.tickets_off), cand_ids, cand_logit, s);
-  if (e != hipSuccess) return hip_fail(e, "topk launch");
-  e = dartree::launch_expand(expand_args(dims, head, cand_ids, cand_logit, hin, st, 1, dims->L), s);
-  if (e != hipSuccess) return hip_fail(e, "expand launch");
+  hipError_t e;
+  if (dims->D > 0 && !fuse_head) {
+    e = dartree::launch_head_valu(wbf, H_or_h, head->Pt, h, rows, dims->D, dims->r, s);
+    if (e != hipSuccess) return hip_fail(e, "head launch");
+  }
+  e = dartree::launch_scan(w.plan, lbf, sa, s);
+  if (e != hipSuccess) return hip_fail(e, "scan launch");
+  e = dartree::launch_merge(w.plan, rows, dims->K, lbf, sa.lists, cand_ids, cand_logit, s);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  // launch 2: expansion, selection, emission and mask, one workgroup per request
+  e = dartree::launch_tree(tp, ta, s);
+  if (e != hipSuccess) return hip_fail(e, "tree launch");
   st->next_depth = dims->L + 1;
-  e = dartree::launch_select(select_args(dims, st, n_sel, tok, depth, parent, score, slot), s);
-  if (e != hipSuccess) return hip_fail(e, "select launch");
-  e = dartree::launch_mask(dims->n_req, dims->B, n_sel, parent, mask, s);
-  if (e != hipSuccess) return hip_fail(e, "mask launch");
   return DARTREE_OK;
 }
 

@@ -1,7 +1,16 @@
 // Device helpers shared by the gfx950 kernels of the draft-tree round.
+//
+// Cost model these helpers are written for (measured on MI355X): a barrier
+// of a 1024-thread workgroup is ~25 cycles, an LDS round trip ~70-90 cycles,
+// a 64-bit cross-lane shuffle through ds_bpermute ~190 cycles per step. Wave
+// reductions therefore use DPP lane moves inside each 16-lane row and four
+// v_readlane reads across rows, never ds_bpermute chains.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+// LDS-qualified pointers (address space 3): accesses compile to ds_* ops.
+#define LDS __attribute__((address_space(3)))
 
 namespace dartree {
 
@@ -25,26 +34,24 @@ __device__ __forceinline__ float key_to_f32(uint32_t k) {
   uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
   return __uint_as_float(u);
 }
-// The same map for bf16 bit patterns (16-bit keys).
+// The same map for bf16 bit patterns: key = 0x8000 +/- magnitude, so -0 and
+// +0 share 0x8000 and every bf16 value maps into [1, 0xFFFF] (0 stays free).
 __device__ __forceinline__ uint32_t bf16_key(uint32_t b) {
-  b &= 0xFFFFu;
-  if (b == 0x8000u) b = 0u;
-  return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+  const uint32_t mag = b & 0x7FFFu;
+  return (b & 0x8000u) ? (0x8000u - mag) : (0x8000u + mag);
 }
 __device__ __forceinline__ float bf16_key_to_f32(uint32_t k) {
-  uint32_t b = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+  const uint32_t b = k >= 0x8000u ? (k - 0x8000u) : (0x8000u | (0x8000u - k));
   return bf16_to_f32(b);
 }
 
-// Split an fp32 value into three bf16 parts by truncation: x == hi + mid + lo
-// exactly for normal x (each part keeps the next 8 significant bits).
+// fp32 -> three bf16 parts by truncation: x == hi + mid + lo exactly for
+// normal x (each part carries the next 8 significant bits).
 __device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  uint32_t u = __float_as_uint(x);
-  float fh = __uint_as_float(u & 0xFFFF0000u);
-  float r1 = x - fh;
-  uint32_t u1 = __float_as_uint(r1);
-  float fm = __uint_as_float(u1 & 0xFFFF0000u);
-  float r2 = r1 - fm;
+  const uint32_t u = __float_as_uint(x);
+  const float r1 = x - __uint_as_float(u & 0xFFFF0000u);
+  const uint32_t u1 = __float_as_uint(r1);
+  const float r2 = r1 - __uint_as_float(u1 & 0xFFFF0000u);
   hi = u >> 16;
   mid = u1 >> 16;
   lo = __float_as_uint(r2) >> 16;
@@ -52,40 +59,89 @@ __device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uin
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// ---- DPP lane moves (gfx9 encodings) -------------------------------------
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// Wave reductions; the result is wave-uniform.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t w = __shfl_xor(v, o, kWave);
-    v = v > w ? v : w;
+  v = max(v, dpp<kDppXor1>(v));
+  v = max(v, dpp<kDppXor2>(v));
+  v = max(v, dpp<kDppHalfMirror>(v));
+  v = max(v, dpp<kDppMirror>(v));
+  return max(max(readlane(v, 0), readlane(v, 16)), max(readlane(v, 32), readlane(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp<kDppXor1>(v));
+  v = min(v, dpp<kDppXor2>(v));
+  v = min(v, dpp<kDppHalfMirror>(v));
+  v = min(v, dpp<kDppMirror>(v));
+  return min(min(readlane(v, 0), readlane(v, 16)), min(readlane(v, 32), readlane(v, 48)));
+}
+__device__ __forceinline__ float wave_max_f32(float x) {
+  uint32_t v = __float_as_uint(x);
+  v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp<kDppXor1>(v))));
+  v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp<kDppXor2>(v))));
+  v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp<kDppHalfMirror>(v))));
+  v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp<kDppMirror>(v))));
+  return fmaxf(fmaxf(__uint_as_float(readlane(v, 0)), __uint_as_float(readlane(v, 16))),
+               fmaxf(__uint_as_float(readlane(v, 32)), __uint_as_float(readlane(v, 48))));
+}
+// Fixed-pattern sum: every call adds in the same order, so results are
+// reproducible bit for bit.
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  uint32_t v = __float_as_uint(x);
+  v = __float_as_uint(__uint_as_float(v) + __uint_as_float(dpp<kDppXor1>(v)));
+  v = __float_as_uint(__uint_as_float(v) + __uint_as_float(dpp<kDppXor2>(v)));
+  v = __float_as_uint(__uint_as_float(v) + __uint_as_float(dpp<kDppHalfMirror>(v)));
+  v = __float_as_uint(__uint_as_float(v) + __uint_as_float(dpp<kDppMirror>(v)));
+  return (__uint_as_float(readlane(v, 0)) + __uint_as_float(readlane(v, 16))) +
+         (__uint_as_float(readlane(v, 32)) + __uint_as_float(readlane(v, 48)));
+}
+__device__ __forceinline__ int wave_sum_i32(int x) {
+  uint32_t v = (uint32_t)x;
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  return (int)(readlane(v, 0) + readlane(v, 16) + readlane(v, 32) + readlane(v, 48));
+}
+
+// m-th largest of the lanes' values among lanes with valid set (wave-uniform;
+// 0 when fewer than m lanes are valid). Bit-by-bit search on ballots.
+__device__ __forceinline__ uint32_t wave_mth_largest(uint32_t v, bool valid, int m, int nbits) {
+  uint32_t t = 0;
+  for (int b = nbits - 1; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    const int n = __popcll(__ballot(valid && v >= c));
+    if (n >= m) t = c;
   }
-  return v;
+  return t;
 }
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+
+// Workgroup-scope atomics on LDS-qualified addresses.
+__device__ __forceinline__ int lds_add(LDS int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+__device__ __forceinline__ unsigned lds_max(LDS unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+__device__ __forceinline__ int lds_or(LDS int* p, int v) {
+  return __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-// Exclusive prefix sum across the wave.
-__device__ __forceinline__ int wave_excl_scan(int v, int& total) {
-  int lane = lane_id();
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  total = __shfl(x, kWave - 1, kWave);
-  return x - v;
+
+__device__ __forceinline__ uint32_t mbcnt64(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const u16x8_t& a, const u16x8_t& b, f32x4_t c) {
@@ -94,184 +150,180 @@ __device__ __forceinline__ f32x4_t mfma_bf16(const u16x8_t& a, const u16x8_t& b,
 }
 
 // ---------------------------------------------------------------------------
-// Block-wide exact top-K of unique 64-bit keys.
+// Block-wide exact top-K of unique 64-bit keys (0 = empty) with an int
+// payload carried along. All threads of the block must call these.
 //
-// Every thread of the block holds EPT keys in registers; 0 marks an empty
-// slot (real keys are never 0). On return, out[0..n) holds the n = min(K,
-// #keys) largest keys in descending order and out[n..K) is 0. Returns n.
+//   block_select = bound + select_compact (+ select_exact) + select_rank
 //
-// Method: (1) a lower bound tau on the high 32 bits of the K-th largest key:
-// each wave whose 64 lanes all hold keys takes the m-th largest of its lane
-// maxima, m = ceil(K / number of such waves); the minimum over those waves is
-// exceeded by at least K keys. (2) Keys at or above the bound are compacted
-// into LDS. (3) Survivors are ranked by counting (small sets) or bitonic
-// sorted (larger sets). (4) If more survive than LDS holds, the K-th largest
-// key is found exactly by a bitwise search over all 64 bits.
+// (1) Bound: each wave whose 64 lanes all hold a key takes the m-th largest of
+//     its lane maxima (high 32 bits), m = ceil(K / such waves); at least K keys
+//     reach the minimum tau of those values.
+// (2) select_compact: keys with high word >= tau are compacted into LDS.
+// (3) select_rank: survivors are ranked by counting, rank(i) = #{j : key_j >
+//     key_i}, split over the whole block, and scattered to their ranks.
+// (4) select_exact: if more than `cap` survive (massive ties, or no bound),
+//     the K-th largest key is found by a bitwise search over the 64 bits and
+//     exactly the keys at or above it are compacted.
 //
-// Shared memory: buf[cap] u64, out[K] u64, rank[min(cap, kRankMax)] int,
-// misc[8] int. All threads of the block must call it (it synchronises).
+// misc[0..7] must be zero on entry to a selection; select_rank leaves it zero.
 // ---------------------------------------------------------------------------
-constexpr int kRankMax = 256;
-
-struct TopkSmem {
-  uint64_t* buf;
-  uint64_t* out;
-  int* rank;
-  int* misc;
+struct SelSmem {
+  LDS uint64_t* key;      // [cap]
+  LDS int* pay;           // [cap]
+  LDS int* rank;          // [cap]
+  LDS uint64_t* out_key;  // [>= K]
+  LDS int* out_pay;       // [>= K]
+  LDS int* misc;          // [8]
   int cap;
 };
 
+// Compacts keys whose high word is >= thr_hi; returns the survivor count
+// (which may exceed cap; then only the first cap are stored).
 template <int EPT>
-__device__ int block_topk(const uint64_t (&sk)[EPT], int K, const TopkSmem& sm) {
-  const int tid = threadIdx.x;
-  const int nthr = blockDim.x;
+__device__ __forceinline__ int select_compact(const uint64_t (&k)[EPT], const int (&p)[EPT], uint32_t thr_hi, const SelSmem& sm) {
   const int lane = lane_id();
-  const int nwave = nthr / kWave;
-  int* misc = sm.misc;
-  // misc: 0 full waves, 1 total keys, 2 tau (min), 3 survivors, 4 tau set flag
-  if (tid == 0) {
-    misc[0] = 0; misc[1] = 0; misc[2] = -1; misc[3] = 0; misc[4] = 0; misc[5] = 0;
-  }
-  __syncthreads();
-  uint32_t lmax = 0;
-  int cnt = 0;
+  uint64_t bal[EPT];
+  int wtot = 0;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    uint32_t hi = (uint32_t)(sk[e] >> 32);
-    lmax = hi > lmax ? hi : lmax;
-    cnt += sk[e] != 0ull;
+    bal[e] = __ballot(k[e] != 0ull && (uint32_t)(k[e] >> 32) >= thr_hi);
+    wtot += __popcll(bal[e]);
   }
-  uint64_t valid = __ballot(lmax != 0u);
-  bool full = valid == ~0ull;
-  int wcnt = wave_sum_i32(cnt);
-  if (lane == 0) {
-    if (full) atomicAdd(&misc[0], 1);
-    atomicAdd(&misc[1], wcnt);
+  int base = 0;
+  if (lane == 0 && wtot) base = lds_add(&sm.misc[3], wtot);
+  base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (bal[e]) {
+      if ((bal[e] >> lane) & 1ull) {
+        const int pos = base + (int)mbcnt64(bal[e]);
+        if (pos < sm.cap) {
+          sm.key[pos] = k[e];
+          sm.pay[pos] = p[e];
+        }
+      }
+      base += __popcll(bal[e]);
+    }
   }
+  __syncthreads();
+  return sm.misc[3];
+}
+
+// Exact fallback: compacts exactly the min(K, #keys) largest keys.
+template <int EPT>
+__device__ __forceinline__ int select_exact(const uint64_t (&k)[EPT], const int (&p)[EPT], int K, const SelSmem& sm) {
+  const int tid = threadIdx.x, lane = lane_id();
+  LDS int* misc = sm.misc;
+  int ntot = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) ntot += __popcll(__ballot(k[e] != 0ull));
+  if (tid == 0) { misc[1] = 0; misc[5] = 0; }
+  __syncthreads();
+  if (lane == 0 && ntot) lds_add(&misc[1], ntot);
+  __syncthreads();
+  const int need = min(K, misc[1]);
+  uint64_t T = 0;
+  for (int b = 63; b >= 0; --b) {
+    const uint64_t c = T | (1ull << b);
+    int n = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) n += __popcll(__ballot(k[e] != 0ull && k[e] >= c));
+    if (lane == 0 && n) lds_add(&misc[5], n);
+    __syncthreads();
+    const int tot = misc[5];
+    __syncthreads();
+    if (tid == 0) misc[5] = 0;
+    __syncthreads();
+    if (tot >= need) T = c;
+  }
+  if (tid == 0) misc[3] = 0;
+  __syncthreads();
+  uint64_t bal[EPT];
+  int wtot = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    bal[e] = __ballot(k[e] != 0ull && k[e] >= T);
+    wtot += __popcll(bal[e]);
+  }
+  int base = 0;
+  if (lane == 0 && wtot) base = lds_add(&misc[3], wtot);
+  base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (bal[e]) {
+      if ((bal[e] >> lane) & 1ull) {
+        const int pos = base + (int)mbcnt64(bal[e]);
+        sm.key[pos] = k[e];
+        sm.pay[pos] = p[e];
+      }
+      base += __popcll(bal[e]);
+    }
+  }
+  __syncthreads();
+  return misc[3];
+}
+
+// Ranks ns (<= cap) compacted keys and scatters the K largest, descending, to
+// out_key/out_pay; zero-fills out_key[n..K). sm.rank[0..ns) must be zero.
+// Leaves misc zeroed and rank zeroed for the next selection.
+__device__ __forceinline__ int select_rank(int ns, int K, const SelSmem& sm) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  if (ns > 0) {
+    int nseg = nthr / ns;
+    if (nseg < 1) nseg = 1;
+    const int seg = (ns + nseg - 1) / nseg;
+    for (int t = tid; t < ns * nseg; t += nthr) {
+      const int i = t % ns, s = t / ns;
+      const uint64_t x = sm.key[i];
+      const int j0 = s * seg, j1 = min(ns, j0 + seg);
+      int r = 0;
+      for (int j = j0; j < j1; ++j) r += sm.key[j] > x;
+      if (r) lds_add(&sm.rank[i], r);
+    }
+  }
+  __syncthreads();
+  const int n_out = min(ns, K);
+  for (int i = tid; i < ns; i += nthr) {
+    const int r = sm.rank[i];
+    if (r < K) {
+      sm.out_key[r] = sm.key[i];
+      sm.out_pay[r] = sm.pay[i];
+    }
+    sm.rank[i] = 0;
+  }
+  for (int i = n_out + tid; i < K; i += nthr) sm.out_key[i] = 0ull;
+  if (tid < 8) sm.misc[tid] = 0;
+  __syncthreads();
+  return n_out;
+}
+
+// Full selection from register-held keys. sm.rank[0..cap) must be zero.
+template <int EPT>
+__device__ __forceinline__ int block_select(const uint64_t (&k)[EPT], const int (&p)[EPT], int K, int hi_bits, const SelSmem& sm) {
+  const int lane = lane_id();
+  LDS int* misc = sm.misc;
+  uint32_t lmax = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) lmax = max(lmax, (uint32_t)(k[e] >> 32));
+  const bool full = __ballot(lmax != 0u) == ~0ull;
+  if (lane == 0 && full) lds_add(&misc[0], 1);
   __syncthreads();
   const int nwf = misc[0];
-  const int ntot = misc[1];
-  (void)nwave;
   if (nwf > 0) {
-    int m = (K + nwf - 1) / nwf;
+    const int m = (K + nwf - 1) / nwf;
     if (m <= kWave && full) {
-      // m-th largest lane maximum of this wave, bit by bit from the top
-      uint32_t t = 0;
-      for (int b = 31; b >= 0; --b) {
-        uint32_t c = t | (1u << b);
-        int n = __popcll(__ballot(lmax >= c));
-        if (n >= m) t = c;
-      }
+      const uint32_t t = wave_mth_largest(lmax, true, m, hi_bits);
       if (lane == 0) {
-        atomicMin(reinterpret_cast<unsigned int*>(&misc[2]), t);
-        atomicOr(&misc[4], 1);
+        lds_max((LDS unsigned*)&misc[2], ~t);   // min of t, complemented
+        misc[4] = 1;
       }
     }
   }
   __syncthreads();
-  const uint64_t thr = misc[4] ? ((uint64_t)(uint32_t)misc[2] << 32) : 1ull;
-  // compaction of survivors
-  int c2 = 0;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) c2 += (sk[e] != 0ull && sk[e] >= thr);
-  int wtot;
-  int pre = wave_excl_scan(c2, wtot);
-  int base = 0;
-  if (lane == 0 && wtot) base = atomicAdd(&misc[3], wtot);
-  base = __shfl(base, 0, kWave);
-  int pos = base + pre;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    if (sk[e] != 0ull && sk[e] >= thr) {
-      if (pos < sm.cap) sm.buf[pos] = sk[e];
-      ++pos;
-    }
-  }
-  __syncthreads();
-  int ns = misc[3];
-  if (ns > sm.cap) {
-    // Exact K-th largest key by a bitwise search (rare: massive ties).
-    uint64_t T = 0;
-    int need = K < ntot ? K : ntot;
-    for (int b = 63; b >= 0; --b) {
-      uint64_t c = T | (1ull << b);
-      int n = 0;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) n += (sk[e] != 0ull && sk[e] >= c);
-      n = wave_sum_i32(n);
-      if (tid == 0) misc[5] = 0;
-      __syncthreads();
-      if (lane == 0 && n) atomicAdd(&misc[5], n);
-      __syncthreads();
-      if (misc[5] >= need) T = c;
-      __syncthreads();
-    }
-    if (tid == 0) misc[3] = 0;
-    __syncthreads();
-    c2 = 0;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) c2 += (sk[e] != 0ull && sk[e] >= T);
-    pre = wave_excl_scan(c2, wtot);
-    base = 0;
-    if (lane == 0 && wtot) base = atomicAdd(&misc[3], wtot);
-    base = __shfl(base, 0, kWave);
-    pos = base + pre;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      if (sk[e] != 0ull && sk[e] >= T) {
-        if (pos < sm.cap) sm.buf[pos] = sk[e];
-        ++pos;
-      }
-    }
-    __syncthreads();
-    ns = misc[3];
-  }
-  const int n_out = ns < K ? ns : K;
-  if (ns <= kRankMax) {
-    // rank by counting: rank(i) = #{j : buf[j] > buf[i]}
-    for (int i = tid; i < ns; i += nthr) sm.rank[i] = 0;
-    __syncthreads();
-    if (ns > 0) {
-      int nseg = nthr / ns;
-      if (nseg < 1) nseg = 1;
-      int seg = (ns + nseg - 1) / nseg;
-      for (int t = tid; t < ns * nseg; t += nthr) {
-        int i = t % ns, s = t / ns;
-        uint64_t x = sm.buf[i];
-        int j0 = s * seg, j1 = min(ns, j0 + seg);
-        int r = 0;
-        for (int j = j0; j < j1; ++j) r += sm.buf[j] > x;
-        if (r) atomicAdd(&sm.rank[i], r);
-      }
-    }
-    __syncthreads();
-    for (int i = tid; i < ns; i += nthr) {
-      int r = sm.rank[i];
-      if (r < K) sm.out[r] = sm.buf[i];
-    }
-    for (int i = n_out + tid; i < K; i += nthr) sm.out[i] = 0ull;
-    __syncthreads();
-  } else {
-    int P = 1;
-    while (P < ns) P <<= 1;
-    for (int i = ns + tid; i < P; i += nthr) sm.buf[i] = 0ull;
-    __syncthreads();
-    for (int k = 2; k <= P; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < (P >> 1); i += nthr) {
-          int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-          int hi = lo + j;
-          bool desc = (lo & k) == 0;
-          uint64_t x = sm.buf[lo], y = sm.buf[hi];
-          if ((x < y) == desc) { sm.buf[lo] = y; sm.buf[hi] = x; }
-        }
-        __syncthreads();
-      }
-    }
-    for (int i = tid; i < K; i += nthr) sm.out[i] = i < n_out ? sm.buf[i] : 0ull;
-    __syncthreads();
-  }
-  return n_out;
+  const uint32_t thr = misc[4] ? ~(uint32_t)misc[2] : 0u;
+  int ns = select_compact<EPT>(k, p, thr, sm);
+  if (ns > sm.cap) ns = select_exact<EPT>(k, p, K, sm);
+  return select_rank(ns, K, sm);
 }
 
 }  // namespace dartree

@@ -6,26 +6,37 @@
 
 namespace dartree {
 
-// ---- step a1: top-K candidates --------------------------------------------
-struct TopkPlan {
-  int nv;            // 16-byte vectors per thread in the chunk pass
-  int chunks;        // chunks per row
-  int chunk_elems;   // elements per chunk
-  int merge_ept;     // keys per thread in the per-row merge
-  int grid;          // workgroups
-  size_t list_bytes;    // per-chunk top-K lists (workspace)
-  size_t ticket_bytes;  // per-row tickets (workspace, zero between calls)
+// ---- steps a1 (+ a0 in the same launch) -----------------------------------
+struct ScanArgs {
+  const void* logits;   // [rows][V]
+  int rows, V, K;
+  int S, slice, n_scan;  // filled from the plan
+  uint64_t* lists;      // [rows][S][K] when S > 1
+  int32_t* cand_ids;    // [rows][K] when S == 1
+  float* cand_logit;
+  // head projection tiles (bf16 MFMA path), n_head = 0 for none
+  const uint16_t* H;    // [M][D]
+  const uint16_t* Pt;   // [r][D]
+  float* h;             // [M][r]
+  int M, D, r, n_head;
 };
-TopkPlan topk_plan(int rows, int V, int K, bool bf16);
-hipError_t launch_topk(const TopkPlan& p, bool bf16, const void* logits, int V, int K, uint64_t* lists,
-                       unsigned int* tickets, int32_t* cand_ids, float* cand_logit, hipStream_t s);
+struct ScanPlan {
+  int S, slice, nv, n_scan, merge_ept;
+  size_t list_bytes;
+  bool ok;
+};
+ScanPlan scan_plan(int rows, int V, int K, bool bf16);
+bool head_mfma_ok(bool bf16, const void* H, const void* Pt, int D, int r);
+hipError_t launch_scan(const ScanPlan& p, bool bf16, const ScanArgs& a, hipStream_t s);
+hipError_t launch_merge(const ScanPlan& p, int rows, int K, bool bf16, const uint64_t* lists, int32_t* cand_ids,
+                        float* cand_logit, hipStream_t s);
+hipError_t launch_head_valu(bool bf16, const void* H, const void* Pt, float* h, int M, int D, int r, hipStream_t s);
+// h = P^T H on its own (bf16 MFMA tiles when possible, else fp32 FMAs)
+hipError_t launch_head(bool bf16, const void* H, const void* Pt, float* h, int M, int D, int r, hipStream_t s);
 
-// ---- step a0: head inputs h = P^T H ----------------------------------------
-hipError_t launch_head_states(bool bf16, const void* H, const void* Pt, float* h, int M, int D, int r, hipStream_t s);
-
-// ---- steps a2 + a3: depth-by-depth expansion --------------------------------
-struct ExpandArgs {
-  int n_req, L, V, K, W, r;
+// ---- steps a2..a5 in one workgroup per request -------------------------------
+struct TreeArgs {
+  int n_req, L, V, K, W, B, r;
   float beta;
   bool bf16;
   const void* A;
@@ -40,28 +51,26 @@ struct ExpandArgs {
   float* st_sbeta;            // [n][L][W]
   int32_t* st_count;          // [n][L]
   float* st_state;            // [n][W][r]
-  int d0, d1;
+  int d0, d1;                 // depths to expand (d1 < d0: none)
+  bool do_select, do_mask;
+  int32_t* n_sel;             // [n]
+  int32_t* tok;               // [n][B]
+  int32_t* depth;             // [n][B]
+  int32_t* parent;            // [n][B]
+  float* score;               // [n][B]
+  int32_t* slot;              // [n][B]
+  uint64_t* mask;             // [n][B][ceil(B/64)]
 };
-size_t expand_smem_bytes(int K, int W, int r);
-hipError_t launch_expand(const ExpandArgs& a, hipStream_t s);
+struct TreePlan {
+  int mode;          // 0 VALU, 1 MFMA general, 2 MFMA resident/prefetched
+  int kq;            // k-groups of the score contraction (mode 2)
+  size_t smem;       // dynamic LDS bytes
+  bool ok;
+};
+TreePlan tree_plan(const TreeArgs& a);
+hipError_t launch_tree(const TreePlan& p, const TreeArgs& a, hipStream_t s);
 
-// ---- step a4 + a5: global top-B, breadth-first emission, mask ---------------
-struct SelectArgs {
-  int n_req, L, W, B;
-  const int32_t* st_tok;
-  const int32_t* st_parent;
-  const float* st_sbeta;
-  const int32_t* st_count;
-  int32_t* n_sel;   // [n]
-  int32_t* tok;     // [n][B]
-  int32_t* depth;   // [n][B]
-  int32_t* parent;  // [n][B]
-  float* score;     // [n][B]
-  int32_t* slot;    // [n][B]
-};
-hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_mask(int n_req, int B, const int32_t* n_sel, const int32_t* parent, uint64_t* mask, hipStream_t s);
-
 hipError_t launch_fill_u32(void* p, size_t n_words, uint32_t value, hipStream_t s);
 
 }  // namespace dartree

@@ -57,8 +57,11 @@ def ws_size(lib, d):
 def test_workspace_size_values(lib):
     st, n = ws_size(lib, dims())
     assert st == C.OK
-    # 16 rows of tickets, then 16 rows x 19 chunks x 64 keys of 8 bytes
-    assert n == 256 + 16 * 19 * 64 * 8
+    # a 151936-entry bf16 row fits one workgroup's registers: no slice lists
+    assert n == 256
+    # fp32 rows of that length take two slices per row: 16 rows x 2 x 64 keys
+    st, n = ws_size(lib, dims(logits_dtype=C.F32))
+    assert st == C.OK and n == 16 * 2 * 64 * 8
     st, n = ws_size(lib, dims(V=1024, L=6, K=8, W=3, B=16, r=16, D=0, logits_dtype=C.F32, weight_dtype=C.F32))
     assert st == C.OK and n >= 6 * 4
 
