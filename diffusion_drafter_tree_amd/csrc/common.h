@@ -20,6 +20,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -71,6 +72,61 @@ __device__ __forceinline__ uint32_t dpp(uint32_t v) {
 }
 __device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// Exact lane exchanges x[lane ^ J] for the sorting networks. Strides 1..8
+// stay inside a 16-lane row (one or two DPP moves: quad xor 3 followed by a
+// half-row mirror is xor 4, a row mirror followed by a half-row mirror is
+// xor 8); stride 16 is a ds_swizzle swap of 16-lane groups; stride 32 goes
+// through ds_bpermute.
+constexpr int kDppXor3 = 0x1B;        // quad_perm [3,2,1,0]
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (J == 1) return dpp<kDppXor1>(v);
+  else if constexpr (J == 2) return dpp<kDppXor2>(v);
+  else if constexpr (J == 4) return dpp<kDppHalfMirror>(dpp<kDppXor3>(v));
+  else if constexpr (J == 8) return dpp<kDppHalfMirror>(dpp<kDppMirror>(v));
+  else if constexpr (J == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+  else return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ J) << 2), (int)v);
+}
+
+// One compare-exchange stage of a bitonic network over 64-bit keys (hi, lo)
+// held one per lane; after the stage (K, J) every block of K lanes is
+// ordered descending where lane & K == 0 and ascending elsewhere.
+template <int K, int J>
+__device__ __forceinline__ void bitonic_stage(uint32_t& hi, uint32_t& lo) {
+  const int lane = __lane_id();
+  const uint32_t ph = lane_xor<J>(hi), pl = lane_xor<J>(lo);
+  const uint64_t me = ((uint64_t)hi << 32) | lo, pa = ((uint64_t)ph << 32) | pl;
+  const bool take_max = ((lane & J) == 0) == ((lane & K) == 0);
+  if (take_max ? (pa > me) : (pa < me)) {
+    hi = ph;
+    lo = pl;
+  }
+}
+// Sorts the wave's 64 keys descending (lane 0 holds the largest).
+__device__ __forceinline__ void wave_sort_desc(uint32_t& hi, uint32_t& lo) {
+  bitonic_stage<2, 1>(hi, lo);
+  bitonic_stage<4, 2>(hi, lo);
+  bitonic_stage<4, 1>(hi, lo);
+  bitonic_stage<8, 4>(hi, lo);
+  bitonic_stage<8, 2>(hi, lo);
+  bitonic_stage<8, 1>(hi, lo);
+  bitonic_stage<16, 8>(hi, lo);
+  bitonic_stage<16, 4>(hi, lo);
+  bitonic_stage<16, 2>(hi, lo);
+  bitonic_stage<16, 1>(hi, lo);
+  bitonic_stage<32, 16>(hi, lo);
+  bitonic_stage<32, 8>(hi, lo);
+  bitonic_stage<32, 4>(hi, lo);
+  bitonic_stage<32, 2>(hi, lo);
+  bitonic_stage<32, 1>(hi, lo);
+  bitonic_stage<64, 32>(hi, lo);
+  bitonic_stage<64, 16>(hi, lo);
+  bitonic_stage<64, 8>(hi, lo);
+  bitonic_stage<64, 4>(hi, lo);
+  bitonic_stage<64, 2>(hi, lo);
+  bitonic_stage<64, 1>(hi, lo);
 }
 
 // Wave reductions; the result is wave-uniform.
@@ -128,6 +184,16 @@ __device__ __forceinline__ uint32_t wave_mth_largest(uint32_t v, bool valid, int
   }
   return t;
 }
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are
+// complete when it arrives, its outstanding global loads (also those that
+// write LDS directly) are not waited for. A wave that needs its direct-to-LDS
+// loads published waits with vmcnt_zero() before the barrier. The wait and
+// the barrier are one asm statement with a memory clobber, so no LDS access
+// moves across it. (__syncthreads() would also wait for every outstanding
+// global load that writes LDS.)
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void vmcnt_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Workgroup-scope atomics on LDS-qualified addresses.
 __device__ __forceinline__ int lds_add(LDS int* p, int v) {

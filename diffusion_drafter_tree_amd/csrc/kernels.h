@@ -62,13 +62,16 @@ struct TreeArgs {
   uint64_t* mask;             // [n][B][ceil(B/64)]
 };
 struct TreePlan {
-  int mode;          // 0 VALU, 1 MFMA general, 2 MFMA resident/prefetched
+  int mode;          // 0 VALU, 1 MFMA general, 2 MFMA resident/prefetched, 3 block-decoding kernel
   int kq;            // k-groups of the score contraction (mode 2)
   size_t smem;       // dynamic LDS bytes
   bool ok;
 };
+// mode 3 (tree_fast.hip) when the shapes allow it, else the general kernel
 TreePlan tree_plan(const TreeArgs& a);
 hipError_t launch_tree(const TreePlan& p, const TreeArgs& a, hipStream_t s);
+TreePlan tree_fast_plan(const TreeArgs& a);
+hipError_t launch_tree_fast(const TreePlan& p, const TreeArgs& a, hipStream_t s);
 
 hipError_t launch_mask(int n_req, int B, const int32_t* n_sel, const int32_t* parent, uint64_t* mask, hipStream_t s);
 hipError_t launch_fill_u32(void* p, size_t n_words, uint32_t value, hipStream_t s);

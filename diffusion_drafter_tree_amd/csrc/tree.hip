@@ -780,6 +780,8 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
 }  // namespace
 
 TreePlan tree_plan(const TreeArgs& a) {
+  const TreePlan f = tree_fast_plan(a);
+  if (f.ok) return f;
   TreePlan p{};
   const bool al = ((((uintptr_t)a.A) | ((uintptr_t)a.E) | ((uintptr_t)a.U)) & 15u) == 0;
   int mode = 0;
@@ -800,6 +802,7 @@ TreePlan tree_plan(const TreeArgs& a) {
 }
 
 hipError_t launch_tree(const TreePlan& p, const TreeArgs& a, hipStream_t s) {
+  if (p.mode == 3) return launch_tree_fast(p, a, s);
   dim3 grid(a.n_req), block(kT);
   hipError_t e = hipSuccess;
 #define DT_TREE(T, M, KS, EP)                                                                              \

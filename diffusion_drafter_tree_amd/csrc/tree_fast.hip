@@ -1,0 +1,703 @@
+// Steps a2..a5 for the block-decoding shapes: bf16 weights, state width
+// r = 256, K in {16, 32, 64} candidates per position, W <= 16 per depth.
+// One 1024-thread workgroup per request with the general kernel's arithmetic
+// for the scores (split-bf16 MFMA contractions with exact products, fp32
+// log-softmax), arranged for latency: five barriers per depth and no wait on
+// global memory inside the depth loop.
+//
+// DARTree (marsggbo blog, section 3.1): at depth d the surviving parents of
+// depth d-1 are scored in one batched head call against their K candidates;
+// s_beta = sum of log q + beta * d; each depth keeps its W best (the
+// supertree); the B best supertree nodes are then taken in one pass, which is
+// prefix-closed for beta <= 0 (Lemma 1). Section 3.2: the draft tree is
+// verified under an ancestor mask. Node order everywhere: s_beta descending,
+// then depth, token and parent slot ascending.
+//
+// Per depth:
+//   P1  stage the E rows and h row prefetched one depth earlier into LDS; the
+//       contractions Z = S U_C^T (KQ partial tiles) and AS = A S^T (A resident
+//       in registers, wave w owning rows 16w..16w+15); then issue the next
+//       depth's prefetch into registers (U fragments, E rows, h row).
+//   P2  one wave per parent: log-softmax over its K candidates, cum, s_beta,
+//       64-bit keys; the W-th largest high word of the wave's keys by a
+//       ballot bit search, max-reduced over the parents into T. At least W
+//       keys reach T (all of them in the wave that attains it).
+//   P3  keys with high word >= T are compacted, then ranked by counting; the
+//       W smallest ranks are the depth's survivors, in order.
+//   P4  one wave per survivor: its state tanh(A s_parent + E[u] + h_d) split
+//       into three bf16 parts; one wave ranks the level's token paths.
+// The selection, emission and mask after the depth loop follow the general
+// kernel's definitions, with ranks by counting over the at most L*W nodes.
+#include "common.h"
+#include "kernels.h"
+
+namespace dartree {
+
+namespace {
+
+constexpr int kT = 1024;
+constexpr int kWaves = kT / kWave;
+constexpr int RT = 256;            // state width
+constexpr int SSTR = RT + 8;       // split-state row stride (bf16 halves)
+constexpr int ASTR = RT + 4;       // A*S row stride (floats)
+constexpr int kWMax = 16;
+constexpr int kSkCap = 1024;       // survivor keys (>= 16 parents x 64 candidates)
+constexpr size_t kMaxSmem = 160 * 1024;
+
+// Fixed LDS region (compile-time offsets, in bytes).
+template <int KC>
+struct FX {
+  static constexpr int NT = KC / 16;                         // candidate tiles of Z
+  static constexpr int KQ = 16 / NT > 8 ? 8 : 16 / NT;       // k-groups of Z
+  static constexpr int KSQ = 8 / KQ;                         // 32-wide k-steps per group
+  static constexpr int ZSTR = KC + 4;
+  static constexpr int NEVEC = KC * RT / 8;                  // 16-byte vectors of E rows
+  static constexpr int NEV = NEVEC >= kT ? NEVEC / kT : 1;   // per thread
+  static constexpr size_t o_sh = 0;
+  static constexpr size_t o_sm = o_sh + 2 * 16 * SSTR;
+  static constexpr size_t o_sl = o_sm + 2 * 16 * SSTR;
+  static constexpr size_t o_zp = o_sl + 2 * 16 * SSTR;
+  static constexpr size_t zp_bytes = 4 * KQ * 16 * ZSTR;
+  static constexpr size_t sk_bytes = 8 * (kSkCap + 4);
+  static constexpr size_t o_sk = o_zp;                // survivors reuse the Z partials (P3 vs P1/P2)
+  static constexpr size_t o_as = o_zp + (zp_bytes > sk_bytes ? zp_bytes : sk_bytes);
+  static constexpr size_t o_ec = o_as + 4 * 16 * ASTR;  // [2][KC][RT], written by direct loads
+  static constexpr size_t o_hb = o_ec + 2 * 2 * KC * RT;  // [2][RT]
+  static constexpr size_t o_ck = o_hb + 2 * 4 * RT;
+  static constexpr size_t o_win = o_ck + 4 * 16 * KC;
+  static constexpr size_t o_misc = o_win + 8 * 16;
+  static constexpr size_t fixed = o_misc + 4 * 16;
+};
+
+// Variable LDS region (depends on L, W, B).
+struct VOff {
+  size_t cid, clog, tok, ps, lex, cum, sb, cnt, nkey, sf, eix, nd, base, epar, mb, ab, total;
+};
+
+__host__ __device__ inline size_t fal16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+__host__ __device__ inline VOff voff(int L, int KC, int W, int B, size_t fixed) {
+  VOff o{};
+  size_t off = fixed;
+  auto take = [&](size_t b) {
+    const size_t x = off;
+    off = fal16(off + b);
+    return x;
+  };
+  const size_t LW = (size_t)L * W;
+  o.cid = take(4ul * L * KC);
+  o.clog = take(4ul * L * KC);
+  o.tok = take(4 * LW);
+  o.ps = take(4 * LW);
+  o.lex = take(4 * LW);
+  o.cum = take(4 * LW);
+  o.sb = take(4 * LW);
+  o.cnt = take(4 * 32);
+  o.nkey = take(8 * LW);
+  o.sf = take(4 * LW);
+  o.eix = take(4 * LW);
+  o.nd = take(4 * 32);
+  o.base = take(4 * 33);
+  o.epar = take(4ul * B);
+  o.mb = take(8 * 128);
+  o.ab = take(4 * 128);
+  o.total = off;
+  return o;
+}
+
+size_t fixed_bytes(int KC) {
+  switch (KC) {
+    case 16: return FX<16>::fixed;
+    case 32: return FX<32>::fixed;
+    default: return FX<64>::fixed;
+  }
+}
+
+struct FLay {
+  LDS uint16_t* Sh;    // [16][SSTR] split parent states
+  LDS uint16_t* Sm;
+  LDS uint16_t* Sl;
+  LDS float* Zp;       // [KQ][16][ZSTR]
+  LDS float* AS;       // [16][ASTR]
+  LDS uint16_t* EC;    // [2][KC][RT] E rows of a depth's candidates (by depth parity)
+  LDS float* hb;       // [2][RT] h row of a depth
+  LDS float* cumK;     // [16][KC]
+  LDS uint64_t* sk;    // [kSkCap + 4] survivor keys
+  LDS uint64_t* win;   // [16] the depth's survivors by rank
+  LDS int* misc;       // [16]
+  LDS int* cid;        // [L][KC]
+  LDS float* clog;     // [L][KC]
+  LDS int* lv_tok;     // [L][W]
+  LDS int* lv_ps;
+  LDS int* lv_lex;
+  LDS float* lv_cum;
+  LDS float* lv_sb;
+  LDS int* lv_cnt;     // [32]
+  LDS uint64_t* nkey;  // [L*W]
+  LDS int* sf;         // [L*W] selected flag
+  LDS int* eix;        // [L*W] emitted index
+  LDS int* nd;         // [32]
+  LDS int* base;       // [33]
+  LDS int* epar;       // [B]
+  LDS uint64_t* mb;    // [2][64]
+  LDS int* ab;         // [2][64]
+};
+
+template <int KC>
+__device__ __forceinline__ FLay make_flay(const VOff& o) {
+  using C = FX<KC>;
+  extern __shared__ __align__(16) char smem[];
+  LDS char* b = (LDS char*)smem;
+  FLay s;
+  s.Sh = (LDS uint16_t*)(b + C::o_sh);
+  s.Sm = (LDS uint16_t*)(b + C::o_sm);
+  s.Sl = (LDS uint16_t*)(b + C::o_sl);
+  s.Zp = (LDS float*)(b + C::o_zp);
+  s.AS = (LDS float*)(b + C::o_as);
+  s.EC = (LDS uint16_t*)(b + C::o_ec);
+  s.hb = (LDS float*)(b + C::o_hb);
+  s.cumK = (LDS float*)(b + C::o_ck);
+  s.sk = (LDS uint64_t*)(b + C::o_sk);
+  s.win = (LDS uint64_t*)(b + C::o_win);
+  s.misc = (LDS int*)(b + C::o_misc);
+  s.cid = (LDS int*)(b + o.cid);
+  s.clog = (LDS float*)(b + o.clog);
+  s.lv_tok = (LDS int*)(b + o.tok);
+  s.lv_ps = (LDS int*)(b + o.ps);
+  s.lv_lex = (LDS int*)(b + o.lex);
+  s.lv_cum = (LDS float*)(b + o.cum);
+  s.lv_sb = (LDS float*)(b + o.sb);
+  s.lv_cnt = (LDS int*)(b + o.cnt);
+  s.nkey = (LDS uint64_t*)(b + o.nkey);
+  s.sf = (LDS int*)(b + o.sf);
+  s.eix = (LDS int*)(b + o.eix);
+  s.nd = (LDS int*)(b + o.nd);
+  s.base = (LDS int*)(b + o.base);
+  s.epar = (LDS int*)(b + o.epar);
+  s.mb = (LDS uint64_t*)(b + o.mb);
+  s.ab = (LDS int*)(b + o.ab);
+  return s;
+}
+
+// split of 4 consecutive state values into the three bf16 planes (8 bytes each)
+__device__ __forceinline__ void split_store4(const FLay& s, int row, int j0, const float (&v)[4]) {
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) split3(v[i], h[i], m[i], l[i]);
+  const int o = row * SSTR + j0;
+  *reinterpret_cast<LDS u32x2_t*>(s.Sh + o) = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  *reinterpret_cast<LDS u32x2_t*>(s.Sm + o) = u32x2_t{m[0] | (m[1] << 16), m[2] | (m[3] << 16)};
+  *reinterpret_cast<LDS u32x2_t*>(s.Sl + o) = u32x2_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+}
+
+// tanh(x) = 1 - 2 / (2^(2 x log2 e) + 1) on the hardware exp2 and reciprocal
+// (each within about 1 ulp): absolute error a few 1e-7, saturating to +-1.
+__device__ __forceinline__ float tanh_fast(float x) {
+  const float e = __builtin_amdgcn_exp2f(x * 2.8853900817779268f);
+  return __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f);
+}
+
+// Path ranks of level d (1-based) from the ranks of level d-1: the order of
+// (parent's path rank, token) among the level's cnt nodes. One wave.
+__device__ __forceinline__ void level_lex_wave(const FLay& s, int d, int W, int cnt, const uint32_t tok,
+                                               const int ps) {
+  const int lane = lane_id();
+  uint32_t k2 = 0xFFFFFFFFu;
+  if (lane < cnt) {
+    const int lp = d == 1 ? 0 : s.lv_lex[(d - 2) * W + min(max(ps, 0), W - 1)];
+    k2 = ((uint32_t)lp << 18) | (tok & 0x3FFFFu);
+  }
+  int rk = 0;
+  for (int c = 0; c < cnt; ++c) rk += readlane(k2, c) < k2;
+  if (lane < cnt) s.lv_lex[(d - 1) * W + lane] = rk;
+}
+
+// Sum of a per-lane count over aligned groups of G consecutive lanes (G a
+// power of two <= 16, wave-uniform); every lane of a group gets the sum.
+__device__ __forceinline__ uint32_t group_sum(uint32_t c, int G) {
+  if (G >= 2) c += dpp<kDppXor1>(c);
+  if (G >= 4) c += dpp<kDppXor2>(c);
+  if (G >= 8) c += lane_xor<4>(c);
+  if (G >= 16) c += lane_xor<8>(c);
+  return c;
+}
+
+template <int KC>
+__global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
+  using C = FX<KC>;
+  const FLay s = make_flay<KC>(voff(a.L, KC, a.W, a.B, C::fixed));
+  const int q = blockIdx.x, tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int L = a.L, W = a.W, B = a.B;
+  const size_t lw = (size_t)q * L * W;
+  const uint16_t* A = static_cast<const uint16_t*>(a.A);
+  const uint16_t* E = static_cast<const uint16_t*>(a.E);
+  const uint16_t* U = static_cast<const uint16_t*>(a.U);
+  const float* hq = a.h + (size_t)q * L * RT;
+  const int32_t* cid_g = a.cand_ids + (size_t)q * L * KC;
+  const float* clog_g = a.cand_logit + (size_t)q * L * KC;
+  const bool expand = a.d0 <= a.d1;
+
+  // ---- prologue ------------------------------------------------------------
+  if (tid < 16) s.misc[tid] = 0;
+  if (tid < 32) s.lv_cnt[tid] = tid < L ? min(max(a.st_count[(size_t)q * L + tid], 0), W) : 0;
+  for (int i = tid; i < L * W; i += kT) {
+    const int d = i / W + 1;
+    const bool here = expand && d >= a.d0 && d <= a.d1;
+    if (!here && (a.do_select || (expand && d == a.d0 - 1))) {
+      s.lv_tok[i] = a.st_tok[lw + i];
+      s.lv_ps[i] = d == 1 ? 0 : a.st_parent[lw + i];
+      s.lv_sb[i] = a.st_sbeta[lw + i];
+      s.lv_cum[i] = a.st_cum[lw + i];
+    }
+  }
+  int Wp = 1;
+  if (expand) {
+    for (int i = tid; i < L * KC; i += kT) {
+      const int c = cid_g[i];
+      s.cid[i] = (c < 0 || c >= a.V) ? 0 : c;
+      s.clog[i] = clog_g[i];
+    }
+    if (a.d0 > 1) Wp = min(max(a.st_count[(size_t)q * L + a.d0 - 2], 1), W);
+    const float* st = a.st_state + (size_t)q * W * RT;
+    for (int i = tid; i < 16 * RT / 4; i += kT) {
+      const int p = i / (RT / 4), j0 = (i % (RT / 4)) * 4;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (a.d0 == 1 && p == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = hq[j0 + e];
+      } else if (a.d0 > 1 && p < Wp) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = st[p * RT + j0 + e];
+      }
+      split_store4(s, p, j0, v);
+    }
+  }
+  __syncthreads();
+
+  // ---- register-resident operands and the prefetch ---------------------------
+  const int sub = (lane >> 4) * 8;
+  const bool zw = w < C::NT * C::KQ;   // this wave computes a Z tile
+  const int z_nt = w % C::NT, z_kq = w / C::NT;
+  const int kofs = zw ? z_kq * C::KSQ : 0;   // first k-step of this wave's pass
+  u16x8_t areg[8];
+  u16x8_t ureg[C::KSQ];   // U fragments of the depth being expanded, then of the next
+  auto load_u = [&](u16x8_t (&dst)[C::KSQ], int d) {
+    if (zw) {
+      const int row = s.cid[(d - 1) * KC + z_nt * 16 + (lane & 15)];
+      const uint16_t* src = U + (size_t)row * RT + sub;
+#pragma unroll
+      for (int i = 0; i < C::KSQ; ++i) dst[i] = *reinterpret_cast<const u16x8_t*>(src + (z_kq * C::KSQ + i) * 32);
+    }
+  };
+  // E rows of depth d's candidates and the h row of depth d go straight from
+  // global memory into the depth's LDS buffers (lane l of a wave writes 16
+  // bytes at the wave's base + 16 l), no registers involved.
+  auto load_eh = [&](int d) {
+    LDS uint16_t* eb = s.EC + (size_t)(d & 1) * KC * RT;
+#pragma unroll
+    for (int i = 0; i < C::NEV; ++i) {
+      const int v0 = w * kWave + i * kT;   // first vector of this wave
+      if (v0 < C::NEVEC) {
+        const int v = v0 + lane;
+        const int k = v / (RT / 8), c = (v % (RT / 8)) * 8;
+        __builtin_amdgcn_global_load_lds(E + (size_t)s.cid[(d - 1) * KC + k] * RT + c, eb + (size_t)v0 * 8, 16, 0, 0);
+      }
+    }
+    if (w == 0) __builtin_amdgcn_global_load_lds(hq + (size_t)d * RT + lane * 4, s.hb + (d & 1) * RT, 16, 0, 0);
+  };
+  if (expand) {
+    const uint16_t* arow = A + (size_t)(w * 16 + (lane & 15)) * RT + sub;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) areg[i] = *reinterpret_cast<const u16x8_t*>(arow + ((i + kofs) & 7) * 32);
+    load_u(ureg, a.d0);
+    if (a.d0 < L) load_eh(a.d0);
+    vmcnt_zero();
+  }
+  lds_sync();
+
+  // ---- the depth loop ----------------------------------------------------------
+  for (int d = a.d0; d <= a.d1; ++d) {
+    const bool need_state = d < L;
+    const int par = d & 1;
+    // P1: contractions, then the next depth's prefetch
+    {
+      // One pass over the parents' split states: each 32-wide k-step feeds the
+      // wave's A*S tile and, for the k-steps of its k-group, its Z tile (the
+      // operand fragment is the same for both). The pass starts at the
+      // wave's k-group (A fragments are held in that rotated order), so the
+      // Z steps are the first KSQ steps. Lanes of absent parents read nothing
+      // and contribute zeros.
+      const int p = lane & 15;
+      const bool pv = p < Wp;
+      const LDS uint16_t* rl = s.Sl + p * SSTR + sub;
+      const LDS uint16_t* rm = s.Sm + p * SSTR + sub;
+      const LDS uint16_t* rh = s.Sh + p * SSTR + sub;
+      const u16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
+      u16x8_t f[2][3];
+      auto ld = [&](int i, u16x8_t (&dst)[3]) {
+        const int o = ((i + kofs) & 7) * 32;
+        dst[0] = pv ? *reinterpret_cast<const LDS u16x8_t*>(rl + o) : zero;
+        dst[1] = pv ? *reinterpret_cast<const LDS u16x8_t*>(rm + o) : zero;
+        dst[2] = pv ? *reinterpret_cast<const LDS u16x8_t*>(rh + o) : zero;
+      };
+      ld(0, f[0]);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, zacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i + 1 < 8) ld(i + 1, f[(i + 1) & 1]);
+        if (i < C::KSQ && zw) {
+          zacc = mfma_bf16(f[i & 1][0], ureg[i], zacc);
+          zacc = mfma_bf16(f[i & 1][1], ureg[i], zacc);
+          zacc = mfma_bf16(f[i & 1][2], ureg[i], zacc);
+        }
+        if (need_state) {
+          acc = mfma_bf16(areg[i], f[i & 1][0], acc);
+          acc = mfma_bf16(areg[i], f[i & 1][1], acc);
+          acc = mfma_bf16(areg[i], f[i & 1][2], acc);
+        }
+      }
+      if (zw) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s.Zp[(z_kq * 16 + (lane >> 4) * 4 + i) * C::ZSTR + z_nt * 16 + (lane & 15)] = zacc[i];
+      }
+      if (need_state) *reinterpret_cast<LDS f32x4_t*>(s.AS + p * ASTR + w * 16 + (lane >> 4) * 4) = acc;
+    }
+    if (d < a.d1) {
+      load_u(ureg, d + 1);   // the Z MFMAs above were the last readers
+      if (d + 1 < L) load_eh(d + 1);
+    }
+    lds_sync();
+
+    // P2: log-softmax and keys (kept in registers); the bound T
+    const float bd = a.beta * (float)d;
+    uint32_t kh = 0u, kl = 0u;
+    if (w < Wp) {
+      const int p = w;
+      const bool v = lane < KC;
+      float z = -__builtin_huge_valf();
+      int tok = 0;
+      if (v) {
+        float zs = 0.f;
+#pragma unroll
+        for (int qq = 0; qq < C::KQ; ++qq) zs += s.Zp[(qq * 16 + p) * C::ZSTR + lane];
+        z = zs + s.clog[(d - 1) * KC + lane];
+        tok = s.cid[(d - 1) * KC + lane];
+      }
+      const float cp = d == 1 ? 0.f : s.lv_cum[(d - 2) * W + p];
+      // exp and log on the hardware exp2/log2 (relative error about 1e-7
+      // where it matters: terms near the maximum dominate the sum)
+      const float m = wave_max_f32(z);
+      const float ssum = wave_sum_f32(v ? __builtin_amdgcn_exp2f((z - m) * 1.4426950408889634f) : 0.f);
+      const float lse = m + __builtin_amdgcn_logf(ssum) * 0.6931471805599453f;
+      if (v) {
+        const float cum = cp + fminf(z - lse, 0.f);
+        s.cumK[p * KC + lane] = cum;
+        kh = f32_key(cum + bd);
+        kl = ~(((uint32_t)tok << 10) | ((uint32_t)p << 6) | (uint32_t)lane);
+      }
+      // the largest 16-bit prefix t of the high words with at least W of the
+      // wave's keys at or above t << 16 (K >= W keys are valid; invalid lanes
+      // hold 0 and never count since t >= 1 << 16 once any bit is set)
+      const uint64_t vmask = __ballot(v);
+      uint32_t t = 0u;
+      for (int b = 15; b >= 0; --b) {
+        const uint32_t c = (t | (1u << b)) << 16;
+        if (__popcll(__builtin_amdgcn_ballot_w64(kh >= c) & vmask) >= W) t |= 1u << b;
+      }
+      if (lane == 0) lds_max((LDS unsigned*)&s.misc[par], t << 16);
+    }
+    lds_sync();
+
+    // P3: survivors (high word >= T) compacted, then ranked by counting
+    if (w < Wp) {
+      const uint32_t T = (uint32_t)s.misc[par];
+      const bool sv = lane < KC && kh >= T;
+      const uint64_t bal = __ballot(sv);
+      int base = 0;
+      if (lane == 0) base = lds_add(&s.misc[2 + par], __popcll(bal));
+      base = __builtin_amdgcn_readfirstlane(base);
+      if (sv) s.sk[base + (int)mbcnt64(bal)] = ((uint64_t)kh << 32) | kl;
+    }
+    lds_sync();
+    const int nk = min(W, Wp * KC);
+    {
+      const int ns = min(s.misc[2 + par], kSkCap);
+      int G = 16;
+      while (G > 1 && ns * G > kT) G >>= 1;
+      const int per = (ns + G - 1) / G;
+      const int x = tid / G, seg = tid - x * G;
+      uint64_t kx = 0ull;
+      uint32_t cnt = 0u;
+      if (x < ns) {
+        kx = s.sk[x];
+        const int y0 = seg * per, y1 = min(ns, y0 + per);
+        for (int y = y0; y < y1; y += 4) {
+          uint64_t k4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) k4[e] = s.sk[y + e];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cnt += (y + e < y1 && k4[e] > kx) ? 1u : 0u;
+        }
+      }
+      const int rk = (int)group_sum(cnt, G);
+      if (x < ns && seg == 0 && rk < W) {
+        const uint32_t lo = ~(uint32_t)kx;
+        const int k = lo & 63, p = (lo >> 6) & 15;
+        const int row = (d - 1) * W + rk;
+        const float cum = s.cumK[p * KC + k];
+        s.win[rk] = kx;
+        s.lv_tok[row] = (int)(lo >> 10);
+        s.lv_ps[row] = p;
+        s.lv_cum[row] = cum;
+        s.lv_sb[row] = cum + bd;
+      }
+      if (tid == 0) s.lv_cnt[d - 1] = nk;
+      // the other parity's bound and count are free again (read one depth ago)
+      if (tid < 2) s.misc[(par ^ 1) + 2 * tid] = 0;
+    }
+    lds_sync();
+
+    // P4: states of the survivors, one wave each; path ranks of the level
+    if (need_state && w < nk) {
+      const uint32_t lo = ~(uint32_t)s.win[w];
+      const int k = lo & 63, p = (lo >> 6) & 15;
+      const int j0 = lane * 4;
+      const f32x4_t as4 = *reinterpret_cast<const LDS f32x4_t*>(s.AS + p * ASTR + j0);
+      const u32x2_t e2 = *reinterpret_cast<const LDS u32x2_t*>(s.EC + ((size_t)par * KC + k) * RT + j0);
+      const f32x4_t h4 = *reinterpret_cast<const LDS f32x4_t*>(s.hb + par * RT + j0);
+      const float ev[4] = {bf16_to_f32(e2.x & 0xFFFFu), bf16_to_f32(e2.x >> 16), bf16_to_f32(e2.y & 0xFFFFu),
+                           bf16_to_f32(e2.y >> 16)};
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = tanh_fast((as4[i] + ev[i]) + h4[i]);
+      split_store4(s, w, j0, v);
+      if (d == a.d1)
+        *reinterpret_cast<f32x4_t*>(a.st_state + ((size_t)q * W + w) * RT + j0) = f32x4_t{v[0], v[1], v[2], v[3]};
+    }
+    if (a.do_select && a.d0 == 1 && w == kWaves - 1) {
+      uint32_t tk = 0u;
+      int ps = 0;
+      if (lane < nk) {
+        const uint32_t lo = ~(uint32_t)s.win[lane];
+        tk = lo >> 10;
+        ps = (lo >> 6) & 15;
+      }
+      level_lex_wave(s, d, W, nk, tk, ps);
+    }
+    Wp = nk;
+    vmcnt_zero();   // this wave's prefetch for the next depth has landed
+    lds_sync();
+  }
+  __syncthreads();
+
+  // ---- the expanded levels to global memory ---------------------------------------
+  if (expand) {
+    const int n0 = (a.d0 - 1) * W, n1 = a.d1 * W;
+    for (int i = n0 + tid; i < n1; i += kT) {
+      const int d = i / W + 1, sl = i - (d - 1) * W;
+      if (sl < s.lv_cnt[d - 1]) {
+        a.st_tok[lw + i] = s.lv_tok[i];
+        a.st_parent[lw + i] = d == 1 ? 0 : s.lv_ps[i];
+        a.st_cum[lw + i] = s.lv_cum[i];
+        a.st_sbeta[lw + i] = s.lv_sb[i];
+      } else {
+        a.st_tok[lw + i] = -1;
+        a.st_parent[lw + i] = -1;
+        a.st_cum[lw + i] = -__builtin_huge_valf();
+        a.st_sbeta[lw + i] = -__builtin_huge_valf();
+      }
+    }
+    for (int d = a.d0 + tid; d <= a.d1; d += kT) a.st_count[(size_t)q * L + d - 1] = s.lv_cnt[d - 1];
+  }
+  if (!a.do_select) return;
+
+  // ---- deferred global top-B -----------------------------------------------------
+  if (!(expand && a.d0 == 1)) {
+    if (w == 0) {
+      for (int d = 1; d <= L; ++d) {
+        const int cnt = s.lv_cnt[d - 1];
+        uint32_t tk = 0u;
+        int ps = 0;
+        if (lane < cnt) {
+          tk = (uint32_t)s.lv_tok[(d - 1) * W + lane];
+          ps = s.lv_ps[(d - 1) * W + lane];
+        }
+        level_lex_wave(s, d, W, cnt, tk, ps);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    __syncthreads();
+  }
+  const int N = L * W;
+  for (int i = tid; i < N; i += kT) {
+    const int d = i / W + 1, sl = i - (d - 1) * W;
+    uint64_t key = 0ull;
+    if (sl < s.lv_cnt[d - 1]) {
+      const uint32_t tok = (uint32_t)s.lv_tok[i] & 0x3FFFFu;
+      const uint32_t ps = d == 1 ? 0u : ((uint32_t)s.lv_ps[i] & 0x1FFu);
+      key = ((uint64_t)f32_key(s.lv_sb[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (((uint32_t)d << 27) | (tok << 9) | ps));
+    }
+    s.nkey[i] = key;
+    s.sf[i] = 0;
+  }
+  if (tid < 32) s.nd[tid] = 0;
+  __syncthreads();
+  {
+    // rank of each node = number of larger keys; G threads per node
+    int G = 8;
+    while (G > 1 && N * G > kT) G >>= 1;
+    const int per = (N + G - 1) / G;
+    const int x = tid / G, seg = tid - x * G;
+    uint64_t kx = 0ull;
+    int cnt = 0;
+    if (x < N) {
+      kx = s.nkey[x];
+      const int y1 = min(N, (seg + 1) * per);
+      for (int y = seg * per; y < y1; ++y) cnt += s.nkey[y] > kx;
+    }
+    uint32_t c2 = (uint32_t)cnt;
+    if (G >= 2) c2 += dpp<kDppXor1>(c2);
+    if (G >= 4) c2 += dpp<kDppXor2>(c2);
+    if (G >= 8) c2 += lane_xor<4>(c2);
+    if (x < N && seg == 0 && kx != 0ull && (int)c2 < B) {
+      s.sf[x] = 1;
+      lds_add(&s.nd[x / W], 1);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int d = 0; d < L; ++d) {
+      s.base[d] = acc;
+      acc += s.nd[d];
+    }
+    s.base[L] = acc;
+  }
+  __syncthreads();
+  const int n = s.base[L];
+  // emitted index: level base + selected nodes of the level with a smaller path rank
+  for (int i = tid; i < N; i += kT) {
+    int e = -1;
+    if (s.sf[i]) {
+      const int d = i / W + 1;
+      const int row = (d - 1) * W, cnt = s.lv_cnt[d - 1];
+      const int my = s.lv_lex[i];
+      int rk = 0;
+      for (int sl = 0; sl < cnt; ++sl) rk += s.sf[row + sl] && s.lv_lex[row + sl] < my;
+      e = s.base[d - 1] + rk;
+    }
+    s.eix[i] = e;
+  }
+  __syncthreads();
+  int32_t* o_tok = a.tok + (size_t)q * B;
+  int32_t* o_dep = a.depth + (size_t)q * B;
+  int32_t* o_par = a.parent + (size_t)q * B;
+  float* o_sc = a.score + (size_t)q * B;
+  int32_t* o_slot = a.slot + (size_t)q * B;
+  for (int i = tid; i < N; i += kT) {
+    const int e = s.eix[i];
+    if (e >= 0) {
+      const int d = i / W + 1, sl = i - (d - 1) * W;
+      const int pe = d == 1 ? -1 : s.eix[(d - 2) * W + min(max(s.lv_ps[i], 0), W - 1)];
+      o_tok[e] = s.lv_tok[i];
+      o_dep[e] = d;
+      o_par[e] = pe;
+      o_sc[e] = s.lv_sb[i];
+      o_slot[e] = sl;
+      s.epar[e] = pe;
+    }
+  }
+  for (int i = n + tid; i < B; i += kT) {
+    o_tok[i] = -1;
+    o_dep[i] = 0;
+    o_par[i] = -2;
+    o_sc[i] = -__builtin_huge_valf();
+    o_slot[i] = -1;
+  }
+  if (tid == 0) a.n_sel[q] = n;
+  if (!a.do_mask) return;
+  __syncthreads();
+
+  // ---- ancestor mask ------------------------------------------------------------------
+  const int words = (B + 63) / 64;
+  uint64_t* mq = a.mask + (size_t)q * B * words;
+  if (words == 1) {
+    // pointer doubling: after round k, mb covers a node and its 2^k - 1
+    // nearest ancestors and ab points at its 2^k-th ancestor
+    if (tid < 64) {
+      s.mb[tid] = tid < n ? (1ull << tid) : 0ull;
+      s.ab[tid] = tid < n ? s.epar[tid] : -1;
+    }
+    __syncthreads();
+    int cur = 0;
+    for (int span = 1; span < L; span *= 2) {
+      if (tid < 64) {
+        const int an = s.ab[cur * 64 + tid];
+        uint64_t mm = s.mb[cur * 64 + tid];
+        int nx = -1;
+        if (an >= 0 && an < tid) {
+          mm |= s.mb[cur * 64 + an];
+          nx = s.ab[cur * 64 + an];
+        }
+        s.mb[(cur ^ 1) * 64 + tid] = mm;
+        s.ab[(cur ^ 1) * 64 + tid] = nx;
+      }
+      __syncthreads();
+      cur ^= 1;
+    }
+    if (tid < B) mq[tid] = s.mb[cur * 64 + tid];
+  } else {
+    for (int t = tid; t < B * words; t += kT) {
+      const int i = t / words, wd = t - i * words;
+      uint64_t bits = 0ull;
+      if (i < n) {
+        int j = i;
+        for (int step = 0; step <= L && j >= 0; ++step) {
+          if ((j >> 6) == wd) bits |= 1ull << (j & 63);
+          const int pj = s.epar[j];
+          if (pj >= j || pj < -1) break;
+          j = pj;
+        }
+      }
+      mq[t] = bits;
+    }
+  }
+}
+
+}  // namespace
+
+TreePlan tree_fast_plan(const TreeArgs& a) {
+  TreePlan p{};
+  p.ok = false;
+  const bool al = ((((uintptr_t)a.A) | ((uintptr_t)a.E) | ((uintptr_t)a.U) | ((uintptr_t)a.h) |
+                    ((uintptr_t)a.st_state)) & 15u) == 0;
+  if (!a.bf16 || a.r != RT || !(a.K == 16 || a.K == 32 || a.K == 64) || a.W > kWMax || a.W < 1 || a.V < a.K ||
+      a.L > 31 || a.B > 1024 || !al)
+    return p;
+  p.mode = 3;
+  p.kq = 16 / (a.K / 16) > 8 ? 8 : 16 / (a.K / 16);
+  p.smem = voff(a.L, a.K, a.W, a.B, fixed_bytes(a.K)).total;
+  p.ok = p.smem <= kMaxSmem;
+  return p;
+}
+
+hipError_t launch_tree_fast(const TreePlan& p, const TreeArgs& a, hipStream_t s) {
+  dim3 grid(a.n_req), block(kT);
+  hipError_t e = hipSuccess;
+#define DT_FAST(KCV)                                                                                         \
+  do {                                                                                                       \
+    e = hipFuncSetAttribute((const void*)tree_fast_kernel<KCV>, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                            (int)p.smem);                                                                    \
+    if (e != hipSuccess) return e;                                                                           \
+    hipLaunchKernelGGL((tree_fast_kernel<KCV>), grid, block, p.smem, s, a);                                 \
+  } while (0)
+  if (a.K == 16) DT_FAST(16);
+  else if (a.K == 32) DT_FAST(32);
+  else DT_FAST(64);
+#undef DT_FAST
+  return hipGetLastError();
+}
+
+}  // namespace dartree
