@@ -176,10 +176,11 @@ __device__ __forceinline__ int wave_sum_i32(int x) {
 // m-th largest of the lanes' values among lanes with valid set (wave-uniform;
 // 0 when fewer than m lanes are valid). Bit-by-bit search on ballots.
 __device__ __forceinline__ uint32_t wave_mth_largest(uint32_t v, bool valid, int m, int nbits) {
+  const uint64_t vm = __builtin_amdgcn_ballot_w64(valid);
   uint32_t t = 0;
   for (int b = nbits - 1; b >= 0; --b) {
     const uint32_t c = t | (1u << b);
-    const int n = __popcll(__ballot(valid && v >= c));
+    const int n = __popcll(__builtin_amdgcn_ballot_w64(v >= c) & vm);
     if (n >= m) t = c;
   }
   return t;

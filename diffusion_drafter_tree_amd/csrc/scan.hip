@@ -5,18 +5,18 @@
 // tokens of the drafter's base logits (value descending, token id ascending);
 // a block-parallel drafter forward provides H_d, here projected to h_d.
 //
-// Scan workgroups (1024 threads): one per (row, slice) of logits[rows][V]. A
-// slice is held in registers (up to NV 16-byte vectors per thread). The
-// values are scanned as signed 16-bit (bf16) or 32-bit (fp32) integers: for
-// positive numbers that order equals the numeric order and negative numbers
-// sort below every positive one, so packed integer max and compare work on
-// the raw bits. Each wave takes the m-th largest positive lane maximum, m =
-// ceil(K / 16), and the smallest of those is a lower bound exceeded by at
-// least K elements; only elements at or above it become 64-bit sort keys and
-// go through the exact selection. Rows where the bound does not hold
-// (fewer than m positive lanes in a wave, or more survivors than fit) take an
-// exact path: a bitwise search for the K-th largest value and an id-ordered
-// choice among values equal to it.
+// Scan workgroups (1024 threads): one per (row, slice) of logits[rows][V]; a
+// thread holds at most five 16-byte vectors of its slice in registers. Values
+// are compared as ordered integer keys (bf16: 16 bits, fp32: 32 bits, -0 and
+// +0 equal). A vector's largest key comes from a packed signed max and min of
+// its raw bits (the signed view orders non-negative values and reverses
+// negative ones). Each wave takes the m-th largest of its lanes' largest keys,
+// m = ceil(K / active waves); the smallest of those, T, is reached by at least
+// K elements. Elements with key >= T are compacted (one LDS atomic per
+// thread that holds any) and ranked by counting, G threads per survivor. A
+// slice whose bound fails (a wave with fewer than m lanes) or whose survivors
+// overflow takes an exact path: bitwise searches for the K-th largest key and,
+// among keys equal to it, for the largest complemented ids.
 //
 // Head workgroups: one per 16x16 tile of h[M][r] = H[M][D] * P[D][r] (Pt
 // stored [r][D]); the 16 waves split D, each issuing all its loads before its
@@ -31,14 +31,15 @@ namespace {
 
 constexpr int kT = 1024;
 constexpr int kWaves = kT / kWave;
-constexpr int kScanCap = 1024;
+constexpr int kScanCap = 2048;   // survivors a slice may hold
+constexpr int kMaxNV = 5;        // 16-byte vectors per thread
 
+constexpr int kHitCap = 512;     // vectors holding a key >= T
 struct ScanSmem {
-  uint64_t key[kScanCap];
-  int pay[kScanCap];
-  int rank[kScanCap];
-  uint64_t out_key[1024];
-  int out_pay[1024];
+  uint64_t key[kScanCap + 8];
+  uint64_t out[1024];
+  u32x4_t hitq[kHitCap];
+  int hitid[kHitCap];
   int misc[8];
   int wsum[kWaves];
 };
@@ -56,60 +57,38 @@ template <>
 struct Traits<true> {
   static constexpr int EPV = 8;   // elements per 16-byte vector
   static constexpr int KBITS = 16;
-  __device__ static uint32_t raw(const u32x4_t& q, int e) { return (q[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu; }
-  __device__ static int sval(uint32_t raw) { return (int)(int16_t)(uint16_t)raw; }   // signed view
+  __device__ static uint32_t raw(u32x4_t q, int e) {
+    const uint32_t w = e < 2 ? q.x : e < 4 ? q.y : e < 6 ? q.z : q.w;
+    return (w >> ((e & 1) * 16)) & 0xFFFFu;
+  }
   __device__ static uint32_t key(uint32_t raw) { return bf16_key(raw); }
   __device__ static float value(uint32_t key) { return bf16_key_to_f32(key); }
-  // signed max of the 8 lanes of a vector (packed 16-bit max). The words are
-  // taken from a local copy by name: bit-casting subscripted elements of a
-  // vector reference was seen to drop all but the first word.
   typedef short s16x2_t __attribute__((ext_vector_type(2)));
   __device__ static s16x2_t as_s16x2(unsigned int x) { return __builtin_bit_cast(s16x2_t, x); }
-  __device__ static int vmax(u32x4_t q) {
-    const s16x2_t m2 = __builtin_elementwise_max(__builtin_elementwise_max(as_s16x2(q.x), as_s16x2(q.y)),
-                                                 __builtin_elementwise_max(as_s16x2(q.z), as_s16x2(q.w)));
-    return max((int)m2.x, (int)m2.y);
+  // largest key of the 8 values (words taken by name from a local copy)
+  __device__ static uint32_t vec_key_max(u32x4_t q) {
+    const s16x2_t a = as_s16x2(q.x), b = as_s16x2(q.y), c = as_s16x2(q.z), d = as_s16x2(q.w);
+    const s16x2_t mx = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+    const s16x2_t mn = __builtin_elementwise_min(__builtin_elementwise_min(a, b), __builtin_elementwise_min(c, d));
+    const int smax = max((int)mx.x, (int)mx.y), smin = min((int)mn.x, (int)mn.y);
+    return smax >= 0 ? 0x8000u + (uint32_t)smax : (uint32_t)(-smin);
   }
-  __device__ static u32x4_t neg_fill() { return u32x4_t{0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u}; }
+  __device__ static uint32_t fill_word() { return 0xFFFFFFFFu; }   // key 1 per element, the lowest
 };
 template <>
 struct Traits<false> {
   static constexpr int EPV = 4;
   static constexpr int KBITS = 32;
-  __device__ static uint32_t raw(const u32x4_t& q, int e) { return q[e]; }
-  __device__ static int sval(uint32_t raw) { return (int)raw; }
+  __device__ static uint32_t raw(u32x4_t q, int e) { return e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w; }
   __device__ static uint32_t key(uint32_t raw) { return f32_key(__uint_as_float(raw)); }
   __device__ static float value(uint32_t key) { return key_to_f32(key); }
-  __device__ static int vmax(u32x4_t q) { return max(max((int)q.x, (int)q.y), max((int)q.z, (int)q.w)); }
-  __device__ static u32x4_t neg_fill() { return u32x4_t{0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u}; }
+  __device__ static uint32_t vec_key_max(u32x4_t q) {
+    const int smax = max(max((int)q.x, (int)q.y), max((int)q.z, (int)q.w));
+    const int smin = min(min((int)q.x, (int)q.y), min((int)q.z, (int)q.w));
+    return smax >= 0 ? (0x80000000u | (uint32_t)smax) : (smin == (int)0x80000000 ? 0x80000000u : ~(uint32_t)smin);
+  }
+  __device__ static uint32_t fill_word() { return 0xFFFFFFFFu; }   // key 0, the lowest
 };
-
-// rank-count selection over ns keys already in sm.key/sm.pay (ns <= cap)
-__device__ int lds_rank_select(ScanSmem& sm, int ns, int K) {
-  const int tid = threadIdx.x;
-  if (ns > 0) {
-    int nseg = kT / ns;
-    if (nseg < 1) nseg = 1;
-    const int seg = (ns + nseg - 1) / nseg;
-    for (int t = tid; t < ns * nseg; t += kT) {
-      const int i = t % ns, s = t / ns;
-      const uint64_t x = sm.key[i];
-      const int j0 = s * seg, j1 = min(ns, j0 + seg);
-      int r = 0;
-      for (int j = j0; j < j1; ++j) r += sm.key[j] > x;
-      if (r) atomicAdd(&sm.rank[i], r);
-    }
-  }
-  __syncthreads();
-  const int n_out = min(ns, K);
-  for (int i = tid; i < ns; i += kT) {
-    const int r = sm.rank[i];
-    if (r < K) sm.out_key[r] = sm.key[i];
-  }
-  for (int i = n_out + tid; i < K; i += kT) sm.out_key[i] = 0ull;
-  __syncthreads();
-  return n_out;
-}
 
 // Block-wide sum of an int (every thread gets the total). Two barriers.
 __device__ int block_sum(ScanSmem& sm, int v) {
@@ -124,6 +103,38 @@ __device__ int block_sum(ScanSmem& sm, int v) {
   return t;
 }
 
+// Ranks the ns distinct keys in sm.key by counting, G threads per key, and
+// writes the K largest in descending order to sm.out (zero beyond ns).
+__device__ void rank_select(ScanSmem& sm, int ns, int K) {
+  const int tid = threadIdx.x;
+  int G = 16;
+  while (G > 1 && ns * G > kT) G >>= 1;
+  const int per = (((ns + G - 1) / G) + 7) & ~7;   // multiple of 8: 16-byte aligned segments
+  for (int x0 = 0; x0 < ns; x0 += kT / G) {
+    const int x = x0 + tid / G, seg = tid % G;
+    uint64_t kx = 0ull;
+    uint32_t cnt = 0u;
+    if (x < ns) {
+      kx = sm.key[x];
+      const int y1 = min(ns, (seg + 1) * per);
+      for (int y = seg * per; y < y1; y += 8) {
+        uint64_t k8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) k8[e] = sm.key[y + e];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cnt += (y + e < y1 && k8[e] > kx) ? 1u : 0u;
+      }
+    }
+    if (G >= 2) cnt += dpp<kDppXor1>(cnt);
+    if (G >= 4) cnt += dpp<kDppXor2>(cnt);
+    if (G >= 8) cnt += lane_xor<4>(cnt);
+    if (G >= 16) cnt += lane_xor<8>(cnt);
+    if (x < ns && seg == 0 && (int)cnt < K) sm.out[cnt] = kx;
+  }
+  for (int i = ns + tid; i < K; i += kT) sm.out[i] = 0ull;
+  __syncthreads();
+}
+
 template <bool BF16, int NV>
 __device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
   using Tr = Traits<BF16>;
@@ -136,179 +147,182 @@ __device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
   const char* rowp = static_cast<const char*>(a.logits) + (size_t)row * (size_t)a.V * ESZ;
   const bool vec_ok = (((uintptr_t)rowp) & 15u) == 0;
   const int K = a.K;
+  auto id0 = [&](int it) { return s0 + (it * kT + tid) * EPV; };
 
-  // -- load the slice: vector it of thread t covers elements s0 + (it*kT + t)*EPV ..
+  // -- the slice, at most kMaxNV vectors per thread; absent elements get the lowest key
   u32x4_t q[NV];
 #pragma unroll
   for (int it = 0; it < NV; ++it) {
-    const int e0 = s0 + (it * kT + tid) * EPV;
+    const int e0 = id0(it);
     if (vec_ok && e0 + EPV <= s1) {
       q[it] = *reinterpret_cast<const u32x4_t*>(rowp + (size_t)e0 * ESZ);
     } else {
-      uint32_t wv[4];
-      const u32x4_t nf = Tr::neg_fill();
-      wv[0] = nf.x; wv[1] = nf.y; wv[2] = nf.z; wv[3] = nf.w;
-      if (e0 < s1) {
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          if (e0 + e < s1) {
-            const uint32_t r = BF16 ? (uint32_t)(reinterpret_cast<const uint16_t*>(rowp)[e0 + e])
-                                    : reinterpret_cast<const uint32_t*>(rowp)[e0 + e];
-            if (BF16)
-              wv[e >> 1] = (wv[e >> 1] & ~(0xFFFFu << ((e & 1) * 16))) | (r << ((e & 1) * 16));
-            else
-              wv[e] = r;
-          }
+      uint32_t wv[4] = {Tr::fill_word(), Tr::fill_word(), Tr::fill_word(), Tr::fill_word()};
+      #pragma unroll 1
+      for (int e = 0; e < EPV; ++e) {
+        if (e0 + e < s1) {
+          const uint32_t r = BF16 ? (uint32_t)(reinterpret_cast<const uint16_t*>(rowp)[e0 + e])
+                                  : reinterpret_cast<const uint32_t*>(rowp)[e0 + e];
+          const int wi = BF16 ? e >> 1 : e, sh = BF16 ? (e & 1) * 16 : 0;
+          const uint32_t msk = BF16 ? (0xFFFFu << sh) : 0xFFFFFFFFu;
+          const uint32_t nw = (wv[wi] & ~msk) | (r << sh);
+          wv[0] = wi == 0 ? nw : wv[0];
+          wv[1] = wi == 1 ? nw : wv[1];
+          wv[2] = wi == 2 ? nw : wv[2];
+          wv[3] = wi == 3 ? nw : wv[3];
         }
       }
       q[it] = u32x4_t{wv[0], wv[1], wv[2], wv[3]};
     }
   }
-  // -- lane maxima on the signed view (positive values order correctly)
-  int vm[NV];
-  int lmax = -0x7FFFFFFF;
+  // -- largest key per vector and per lane
+  uint32_t vk[NV];
+  uint32_t lk = 0u;
 #pragma unroll
   for (int it = 0; it < NV; ++it) {
-    vm[it] = Tr::vmax(q[it]);
-    lmax = max(lmax, vm[it]);
+    vk[it] = Tr::vec_key_max(q[it]);
+    lk = max(lk, vk[it]);
   }
-  // -- bound: each active wave's m-th largest positive lane maximum. A wave
-  //    is active when its first lane holds an element of the slice.
+  // -- bound: every active wave vouches for m lanes whose largest key >= its t
   const int nthr_valid = min(kT, (s1 - s0 + EPV - 1) / EPV);
   const int nact = (nthr_valid + kWave - 1) / kWave;
-  const int m = (K + nact - 1) / nact;
+  const int m = nact > 0 ? (K + nact - 1) / nact : K;
+  if (nact == 0 && tid == 0) sm.misc[4] = 1;   // empty slice: the exact path yields nothing
   if (w < nact) {
-    const bool pos = lmax > 0;
-    const int npos = __popcll(__ballot(pos));
-    if (npos >= m && m <= kWave) {
-      const uint32_t t = wave_mth_largest((uint32_t)lmax, pos, m, Tr::KBITS == 16 ? 15 : 31);
+    const bool lv = tid < nthr_valid;
+    const int nl = __popcll(__ballot(lv));
+    if (nl >= m && m <= kWave) {
+      const uint32_t t = wave_mth_largest(lk, lv, m, Tr::KBITS);
       if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(&sm.misc[2]), ~t);
     } else if (lane == 0) {
-      atomicOr(&sm.misc[4], 1);   // this wave cannot vouch for m elements
+      atomicOr(&sm.misc[4], 1);
     }
   }
-  for (int i = tid; i < kScanCap; i += kT) sm.rank[i] = 0;
   __syncthreads();
   const bool bound_ok = sm.misc[4] == 0;
-  const int tau = (int)(~(uint32_t)sm.misc[2]);
-  int ns = kScanCap + 1;
+  const uint32_t T = ~(uint32_t)sm.misc[2];
   if (bound_ok) {
-    // -- survivors: elements with signed value >= tau (tau > 0)
+    // hit vectors (largest key >= T) go to LDS, one wave-level append per
+    // vector round; then one thread per element of a hit vector
 #pragma unroll
     for (int it = 0; it < NV; ++it) {
-      const uint64_t hit = __ballot(vm[it] >= tau);
-      if (hit) {
-        const int e0 = s0 + (it * kT + tid) * EPV;
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const uint32_t r = Tr::raw(q[it], e);
-          const bool sv = ((hit >> lane) & 1ull) && Tr::sval(r) >= tau && e0 + e < s1;
-          const uint64_t b = __ballot(sv);
-          if (b) {
-            int base = 0;
-            if (lane == 0) base = atomicAdd(&sm.misc[3], __popcll(b));
-            base = __builtin_amdgcn_readfirstlane(base);
-            if (sv) {
-              const int p = base + (int)mbcnt64(b);
-              if (p < kScanCap) sm.key[p] = ((uint64_t)Tr::key(r) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(e0 + e));
-            }
+      const bool hit = vk[it] >= T;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(hit);
+      if (bal) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&sm.misc[5], __popcll(bal));
+        base = __builtin_amdgcn_readfirstlane(base);
+        if (hit) {
+          const int hv = base + (int)mbcnt64(bal);
+          if (hv < kHitCap) {
+            sm.hitq[hv] = q[it];
+            sm.hitid[hv] = id0(it);
           }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (bound_ok) {
+    const int nh = min(sm.misc[5], kHitCap);
+    for (int t = tid; t < nh * EPV; t += kT) {
+      const int hv = t / EPV, e = t - hv * EPV;
+      const int idx = sm.hitid[hv] + e;
+      const uint32_t kk = Tr::key(Tr::raw(sm.hitq[hv], e));
+      const bool sv = idx < s1 && kk >= T;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(sv);
+      int base = 0;
+      if (lane == 0 && bal) base = atomicAdd(&sm.misc[3], __popcll(bal));
+      base = __builtin_amdgcn_readfirstlane(base);
+      if (sv) {
+        const int p = base + (int)mbcnt64(bal);
+        if (p < kScanCap) sm.key[p] = ((uint64_t)kk << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
+      }
+    }
+  }
+  __syncthreads();
+  int ns = sm.misc[3];
+  if (!bound_ok || sm.misc[5] > kHitCap || ns > kScanCap) {
+    // -- exact path: Th = K-th largest key (bitwise search on block counts),
+    //    then among keys == Th the largest complemented ids (lowest ids)
+    int nvalid = 0;
+#pragma unroll
+    for (int it = 0; it < NV; ++it) nvalid += max(0, min(EPV, s1 - id0(it)));
+    const int need = min(K, block_sum(sm, nvalid));
+    uint32_t Th = 0;
+    for (int b = Tr::KBITS - 1; b >= 0; --b) {
+      const uint32_t cand = Th | (1u << b);
+      int n = 0;
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        const int e0 = id0(it);
+        #pragma unroll 1
+        for (int e = 0; e < EPV; ++e) n += (e0 + e < s1 && Tr::key(Tr::raw(q[it], e)) >= cand) ? 1 : 0;
+      }
+      if (block_sum(sm, n) >= need) Th = cand;
+    }
+    int ngt = 0;
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int e0 = id0(it);
+      #pragma unroll 1
+      for (int e = 0; e < EPV; ++e) ngt += (e0 + e < s1 && Tr::key(Tr::raw(q[it], e)) > Th) ? 1 : 0;
+    }
+    const int take = need - block_sum(sm, ngt);   // ties at Th to take, lowest ids first
+    uint32_t Ui = 0;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = Ui | (1u << b);
+      int n = 0;
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        const int e0 = id0(it);
+        #pragma unroll 1
+        for (int e = 0; e < EPV; ++e)
+          n += (e0 + e < s1 && Tr::key(Tr::raw(q[it], e)) == Th && 0xFFFFFFFFu - (uint32_t)(e0 + e) >= cand) ? 1 : 0;
+      }
+      if (block_sum(sm, n) >= take) Ui = cand;
+    }
+    if (tid == 0) sm.misc[3] = 0;
+    __syncthreads();
+    int c = 0;
+#pragma unroll
+    for (int it = 0; it < NV; ++it) {
+      const int e0 = id0(it);
+      #pragma unroll 1
+      for (int e = 0; e < EPV; ++e) {
+        const uint32_t kk = Tr::key(Tr::raw(q[it], e));
+        const uint32_t ci = 0xFFFFFFFFu - (uint32_t)(e0 + e);
+        c += (e0 + e < s1 && (kk > Th || (kk == Th && ci >= Ui))) ? 1 : 0;
+      }
+    }
+    if (c) {
+      int p = atomicAdd(&sm.misc[3], c);
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        const int e0 = id0(it);
+        #pragma unroll 1
+        for (int e = 0; e < EPV; ++e) {
+          const uint32_t kk = Tr::key(Tr::raw(q[it], e));
+          const uint32_t ci = 0xFFFFFFFFu - (uint32_t)(e0 + e);
+          if (e0 + e < s1 && (kk > Th || (kk == Th && ci >= Ui))) sm.key[p++] = ((uint64_t)kk << 32) | ci;
         }
       }
     }
     __syncthreads();
     ns = sm.misc[3];
   }
-  if (!bound_ok || ns > kScanCap) {
-    // -- exact path: K-th largest value key by a bitwise search, then the
-    //    keys above it and the lowest ids among the keys equal to it
-    int nvalid = 0;
-#pragma unroll
-    for (int it = 0; it < NV; ++it) {
-      const int e0 = s0 + (it * kT + tid) * EPV;
-      nvalid += max(0, min(EPV, s1 - e0));
-    }
-    const int need = min(K, block_sum(sm, nvalid));
-    uint32_t T = 0;
-    for (int b = Tr::KBITS - 1; b >= 0; --b) {
-      const uint32_t c = T | (1u << b);
-      int n = 0;
-#pragma unroll
-      for (int it = 0; it < NV; ++it) {
-        const int e0 = s0 + (it * kT + tid) * EPV;
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) n += (e0 + e < s1 && Tr::key(Tr::raw(q[it], e)) >= c);
-      }
-      if (block_sum(sm, n) >= need) T = c;
-    }
-    // keys strictly above T (fewer than need), in any order
-    if (tid == 0) sm.misc[3] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < NV; ++it) {
-      const int e0 = s0 + (it * kT + tid) * EPV;
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const uint32_t kk = Tr::key(Tr::raw(q[it], e));
-        if (e0 + e < s1 && kk > T) {
-          const int p = atomicAdd(&sm.misc[3], 1);
-          sm.key[p] = ((uint64_t)kk << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(e0 + e));
-        }
-      }
-    }
-    __syncthreads();
-    const int ngt = sm.misc[3];
-    int take = need - ngt;   // keys equal to T, lowest ids first
-    // ids grow with (it, thread, e): walk the vector rounds in order
-#pragma unroll
-    for (int it = 0; it < NV; ++it) {
-      const int e0 = s0 + (it * kT + tid) * EPV;
-      int c = 0;
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) c += (e0 + e < s1 && Tr::key(Tr::raw(q[it], e)) == T);
-      // exclusive prefix of c over threads in tid order
-      const int wtot = wave_sum_i32(c);
-      uint32_t x = (uint32_t)c;   // inclusive scan within the wave by shifts
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t y = (uint32_t)__shfl_up((int)x, o, kWave);
-        if (lane >= o) x += y;
-      }
-      if (lane == 0) sm.wsum[w] = wtot;
-      __syncthreads();
-      int before = 0, all = 0;
-      for (int i = 0; i < kWaves; ++i) {
-        before += i < w ? sm.wsum[i] : 0;
-        all += sm.wsum[i];
-      }
-      int r = before + (int)x - c;
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const uint32_t kk = Tr::key(Tr::raw(q[it], e));
-        if (e0 + e < s1 && kk == T) {
-          if (r < take) sm.key[ngt + (need - ngt - take) + r] =
-              ((uint64_t)kk << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(e0 + e));
-          ++r;
-        }
-      }
-      __syncthreads();
-      take -= min(all, take);   // 0 once every needed key is taken; later rounds write nothing
-    }
-    ns = need;
-    __syncthreads();
-  }
-  const int n = lds_rank_select(sm, ns, K);
-  (void)n;
+  rank_select(sm, ns, K);
   if (a.S == 1) {
     int32_t* ids = a.cand_ids + (size_t)row * K;
     float* vals = a.cand_logit + (size_t)row * K;
     for (int i = tid; i < K; i += kT) {
-      const uint64_t x = sm.out_key[i];
+      const uint64_t x = sm.out[i];
       ids[i] = x ? (int32_t)(0xFFFFFFFFu - (uint32_t)x) : -1;
       vals[i] = x ? Tr::value((uint32_t)(x >> 32)) : -__builtin_huge_valf();
     }
   } else {
     uint64_t* lst = a.lists + ((size_t)row * a.S + sl) * K;
-    for (int i = tid; i < K; i += kT) lst[i] = sm.out_key[i];
+    for (int i = tid; i < K; i += kT) lst[i] = sm.out[i];
   }
 }
 
@@ -421,30 +435,23 @@ __global__ __launch_bounds__(256) void head_valu_bf16(const uint16_t* __restrict
   h[idx] = acc;
 }
 
-constexpr int kNvOptions[] = {2, 4, 8, 12, 16, 20};
-
 }  // namespace
 
 ScanPlan scan_plan(int rows, int V, int K, bool bf16) {
   ScanPlan p{};
   const int epv = bf16 ? 8 : 4;
-  const int max_nv = 20;
-  // slices per row: as few as fit in registers (max_nv vectors per thread)
-  const long long per_wg = (long long)kT * epv * max_nv;
+  // slices per row: as few as keep every thread at <= kMaxNV vectors
+  const long long per_wg = (long long)kT * epv * kMaxNV;
   p.S = (int)((V + per_wg - 1) / per_wg);
-  // slice length: multiple of the vector width
   long long sl = ((long long)V + p.S - 1) / p.S;
-  sl = (sl + epv - 1) / epv * epv;
+  sl = (sl + epv - 1) / epv * epv;   // slice length: multiple of the vector width
   p.slice = (int)sl;
   const int nvec = (int)((sl + epv - 1) / epv);
-  const int need_nv = (nvec + kT - 1) / kT;
-  p.nv = 0;
-  for (int o : kNvOptions)
-    if (o >= need_nv) { p.nv = o; break; }
+  p.nv = (nvec + kT - 1) / kT;
   p.n_scan = rows * p.S;
   p.merge_ept = (p.S * K + kT - 1) / kT <= 8 ? 8 : 16;
   p.list_bytes = p.S > 1 ? (size_t)rows * p.S * K * sizeof(uint64_t) : 0;
-  p.ok = p.nv > 0 && (long long)p.S * K <= 16LL * kT;
+  p.ok = p.nv >= 1 && p.nv <= kMaxNV && (long long)p.S * K <= 16LL * kT;
   return p;
 }
 
@@ -461,12 +468,11 @@ hipError_t launch_scan(const ScanPlan& p, bool bf16, const ScanArgs& args_in, hi
   if (grid == 0) return hipSuccess;
 #define DT_SCAN(B, NVV) hipLaunchKernelGGL((scan_kernel<B, NVV>), dim3(grid), dim3(kT), 0, s, a)
   switch (p.nv) {
+    case 1: if (bf16) DT_SCAN(true, 1); else DT_SCAN(false, 1); break;
     case 2: if (bf16) DT_SCAN(true, 2); else DT_SCAN(false, 2); break;
+    case 3: if (bf16) DT_SCAN(true, 3); else DT_SCAN(false, 3); break;
     case 4: if (bf16) DT_SCAN(true, 4); else DT_SCAN(false, 4); break;
-    case 8: if (bf16) DT_SCAN(true, 8); else DT_SCAN(false, 8); break;
-    case 12: if (bf16) DT_SCAN(true, 12); else DT_SCAN(false, 12); break;
-    case 16: if (bf16) DT_SCAN(true, 16); else DT_SCAN(false, 16); break;
-    default: if (bf16) DT_SCAN(true, 20); else DT_SCAN(false, 20); break;
+    default: if (bf16) DT_SCAN(true, 5); else DT_SCAN(false, 5); break;
   }
 #undef DT_SCAN
   return hipGetLastError();
@@ -493,7 +499,7 @@ hipError_t launch_head(bool bf16, const void* H, const void* Pt, float* h, int M
   a.r = r;
   a.n_head = (r / 16) * ((M + 15) / 16);
   a.n_scan = 0;
-  hipLaunchKernelGGL((scan_kernel<true, 2>), dim3(a.n_head), dim3(kT), 0, s, a);
+  hipLaunchKernelGGL((scan_kernel<true, 1>), dim3(a.n_head), dim3(kT), 0, s, a);
   return hipGetLastError();
 }
 

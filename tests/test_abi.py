@@ -57,11 +57,12 @@ def ws_size(lib, d):
 def test_workspace_size_values(lib):
     st, n = ws_size(lib, dims())
     assert st == C.OK
-    # a 151936-entry bf16 row fits one workgroup's registers: no slice lists
-    assert n == 256
-    # fp32 rows of that length take two slices per row: 16 rows x 2 x 64 keys
+    # a 151936-entry bf16 row spans 4 slices of <= 1024 threads x 5 vectors x 8
+    # values: 16 rows x 4 sorted lists x 64 keys of 8 bytes
+    assert n == 16 * 4 * 64 * 8
+    # fp32 rows of that length take 8 slices (4 values per vector)
     st, n = ws_size(lib, dims(logits_dtype=C.F32))
-    assert st == C.OK and n == 16 * 2 * 64 * 8
+    assert st == C.OK and n == 16 * 8 * 64 * 8
     st, n = ws_size(lib, dims(V=1024, L=6, K=8, W=3, B=16, r=16, D=0, logits_dtype=C.F32, weight_dtype=C.F32))
     assert st == C.OK and n >= 6 * 4
 
