@@ -141,61 +141,63 @@ def main():
     torch.cuda.synchronize()
     us_eager = e0.elapsed_time(e1) * 1000.0 / ne
 
-    # ---- per-kernel durations with HIP events (step entry points) ----------------
-    names = ["head_states", "topk_candidates", "expand_depth", "select_topB", "tree_mask"]
-    evs = {n: [] for n in names}
+    # ---- per-stage kernel durations, live, with HIP events on the launch stream --
+    # The library records four events around the launches of each round
+    # (scan with head tiles | candidate merge | tree kernel); eager rounds.
     nk = min(K, 256)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nk)]
     torch.cuda.synchronize()
     for t in range(nk):
-        s = t % R
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-        marks[0].record(stream)
-        if cfg.D > 0:
-            ops.head_states(dims, hin[s], dhead.Pt, rb.h)
-        marks[1].record(stream)
-        ops.topk_candidates(dims, logits[s], rb.cand_ids, rb.cand_logit, rb.ws)
-        marks[2].record(stream)
-        rb.st.next_depth = 1
-        ops.expand_depth(dims, dhead, rb.cand_ids, rb.cand_logit, rb.h if cfg.D > 0 else hin[s], rb, 1, cfg.L)
-        marks[3].record(stream)
-        ops.select_topB(dims, rb)
-        marks[4].record(stream)
-        ops.tree_mask(dims, rb.n_sel, rb.parent, rb.mask)
-        marks[5].record(stream)
-        torch.cuda.synchronize()
-        for i, n in enumerate(names):
-            evs[n].append(marks[i].elapsed_time(marks[i + 1]) * 1000.0)
-    kern_us = {n: float(np.mean(v[4:])) if len(v) > 8 else float(np.mean(v)) for n, v in evs.items()}
+        ops.set_stage_events(ev[t])
+        ops.build_round(dims, dhead, logits[t % R], hin[t % R], rb)
+    ops.set_stage_events(None)
+    torch.cuda.synchronize()
+    stage_names = ["scan_kernel", "merge_kernel", "tree_kernel"]
+    per = {n: [] for n in stage_names}
+    tot = []
+    for t in range(4, nk):
+        for i, n in enumerate(stage_names):
+            per[n].append(ev[t][i].elapsed_time(ev[t][i + 1]) * 1000.0)
+        tot.append(ev[t][0].elapsed_time(ev[t][3]) * 1000.0)
+    kern_us = {n: float(np.mean(v)) for n, v in per.items()}
 
-    # algorithmic bytes / flops per launch
+    # algorithmic bytes / flops per launch (the minimal traffic of each stage)
     n, L, V, Kc, W, B, r, D = cfg.n_req, cfg.L, cfg.V, cfg.K, cfg.W, cfg.B, cfg.r, cfg.D
     lsz = 2 if cfg.logits_dtype == "bf16" else 4
     wsz = 2 if cfg.weight_dtype == "bf16" else 4
+    rows = n * L
+    # slices per row of the logits scan: the workspace holds their sorted lists
+    S_sl = max(1, rb.ws_bytes // (rows * Kc * 8)) if rb.ws_bytes > 256 else 1
     alg = {
-        "topk_candidates": {"bytes": n * L * V * lsz + n * L * Kc * 8, "flops": 0},
-        "head_states": {"bytes": n * L * D * wsz + r * D * wsz + n * L * r * 4, "flops": 2 * n * L * D * r},
-        "expand_depth": {"bytes": n * L * Kc * (r * wsz + 8) + n * (L - 1) * W * r * wsz + r * r * wsz
-                         + n * L * r * 4 + n * L * W * 16,
-                         "flops": 2 * n * L * W * Kc * r + 2 * n * (L - 1) * W * r * r},
-        "select_topB": {"bytes": n * L * W * 16 + n * B * 20, "flops": 0},
-        "tree_mask": {"bytes": n * B * 4 + n * B * ((B + 63) // 64) * 8, "flops": 0},
+        # a1 logits scan + a0 head projection (H, P read once; h written)
+        "scan_kernel": {"bytes": rows * V * lsz + (rows * D * wsz + r * D * wsz + rows * r * 4 if D > 0 else 0)
+                        + (rows * S_sl * Kc * 8 if S_sl > 1 else rows * Kc * 8),
+                        "flops": 2 * rows * D * r},
+        "merge_kernel": {"bytes": (rows * S_sl * Kc * 8 + rows * Kc * 8) if S_sl > 1 else 0, "flops": 0},
+        # a2..a5: U rows of every candidate, E rows of the kept nodes, A, h, candidates, outputs
+        "tree_kernel": {"bytes": rows * Kc * r * wsz + n * (L - 1) * W * r * wsz + r * r * wsz + rows * r * 4
+                        + rows * Kc * 8 + n * L * W * 16 + n * B * (20 + ((B + 63) // 64) * 8),
+                        "flops": 2 * n * L * W * Kc * r + 2 * n * (L - 1) * W * r * r},
     }
-    HBM_PEAK = 8000.0   # GB/s
+    HBM_PEAK = 8000.0   # GB/s, MI355X HBM3E
     kernels = {}
-    for k in names:
-        if k == "head_states" and D == 0:
-            continue
+    for k in stage_names:
         us = kern_us[k]
-        gbs = alg[k]["bytes"] / (us * 1e-6) / 1e9
-        kernels[k] = {"us": round(us, 3), "alg_bytes": alg[k]["bytes"], "GB_s": round(gbs, 1),
-                      "hbm_frac": round(gbs / HBM_PEAK, 4), "alg_flops": alg[k]["flops"]}
+        gbs = alg[k]["bytes"] / (us * 1e-6) / 1e9 if us > 0 else 0.0
+        kernels[k] = {"us": round(us, 3), "alg_bytes": alg[k]["bytes"], "GB_s": round(gbs, 2),
+                      "hbm_frac": round(gbs / HBM_PEAK, 5), "alg_flops": alg[k]["flops"]}
     dom = max(kernels, key=lambda k: kernels[k]["us"])
     dk = kernels[dom]
     roofline = {"kernel": dom, "bound": "hbm", "achieved": dk["GB_s"], "peak": HBM_PEAK, "unit": "GB/s",
                 "frac": dk["hbm_frac"], "traffic": None}
-    scan = kernels["topk_candidates"]
-    roofline_scan = {"kernel": "topk_candidates", "bound": "hbm", "achieved": scan["GB_s"], "peak": HBM_PEAK,
-                     "unit": "GB/s", "frac": scan["hbm_frac"], "traffic": None}
+    sk = kernels["scan_kernel"]
+    roofline_scan = {"kernel": "scan_kernel", "bound": "hbm", "achieved": sk["GB_s"], "peak": HBM_PEAK,
+                     "unit": "GB/s", "frac": sk["hbm_frac"], "traffic": None}
+    round_bytes = alg["scan_kernel"]["bytes"] + alg["tree_kernel"]["bytes"]
+    ideal_us = round_bytes / (HBM_PEAK * 1e9) * 1e6
+    round_stats = {"p50_us": round(float(np.percentile(tot, 50)), 3), "p99_us": round(float(np.percentile(tot, 99)), 3),
+                   "ideal_us_at_hbm_peak": round(ideal_us, 3), "alg_bytes": round_bytes,
+                   "round_roofline_frac": round(ideal_us / us_round, 5)}
 
     # ---- CPU oracle baseline on a bounded sample -------------------------------
     cpu = None
@@ -223,6 +225,7 @@ def main():
         "roofline": roofline,
         "roofline_scan": roofline_scan,
         "kernels": kernels,
+        "round": round_stats,
         "us_per_round_eager": round(us_eager, 3),
         "host_seconds_timed": round(t_host, 4),
         "cpu_baseline": cpu,

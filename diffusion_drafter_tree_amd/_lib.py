@@ -57,6 +57,7 @@ SIGNATURES = {
     "dartree_build_round": (c_int32, [PD, PH, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, PS,
                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_size_t, c_void_p]),
+    "dartree_set_stage_events": (c_int32, [POINTER(c_void_p), c_int32]),
 }
 
 _lib = None

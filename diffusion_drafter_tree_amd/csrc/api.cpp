@@ -13,6 +13,12 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t g_stage_ev[4] = {nullptr, nullptr, nullptr, nullptr};
+thread_local bool g_stage_on = false;
+
+void stage_mark(int i, hipStream_t s) {
+  if (g_stage_on) (void)hipEventRecord(g_stage_ev[i], s);
+}
 
 dartree_status fail(dartree_status s, const char* fmt, ...) {
   va_list ap;
@@ -192,6 +198,20 @@ const char* dartree_last_error(void) { return g_err; }
 
 int32_t dartree_version(void) { return 1; }
 
+dartree_status dartree_set_stage_events(void* const* events, int32_t n) {
+  g_err[0] = 0;
+  if (n == 0) {
+    g_stage_on = false;
+    return DARTREE_OK;
+  }
+  if (n != 4 || !events) return fail(DARTREE_ERR_INVALID_ARGUMENT, "stage events: need n = 4 handles (or n = 0)");
+  for (int i = 0; i < 4; ++i)
+    if (!events[i]) return fail(DARTREE_ERR_INVALID_ARGUMENT, "stage event %d is NULL", i);
+  for (int i = 0; i < 4; ++i) g_stage_ev[i] = static_cast<hipEvent_t>(events[i]);
+  g_stage_on = true;
+  return DARTREE_OK;
+}
+
 dartree_status dartree_workspace_size(const dartree_dims* dims, size_t* bytes) {
   g_err[0] = 0;
   TRY(check_dims(dims));
@@ -357,17 +377,21 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
     sa.n_head = (dims->r / 16) * ((rows + 15) / 16);
   }
   hipError_t e;
+  stage_mark(0, s);
   if (dims->D > 0 && !fuse_head) {
     e = dartree::launch_head_valu(wbf, H_or_h, head->Pt, h, rows, dims->D, dims->r, s);
     if (e != hipSuccess) return hip_fail(e, "head launch");
   }
   e = dartree::launch_scan(w.plan, lbf, sa, s);
   if (e != hipSuccess) return hip_fail(e, "scan launch");
+  stage_mark(1, s);
   e = dartree::launch_merge(w.plan, rows, dims->K, lbf, sa.lists, cand_ids, cand_logit, s);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
+  stage_mark(2, s);
   // launch 2: expansion, selection, emission and mask, one workgroup per request
   e = dartree::launch_tree(tp, ta, s);
   if (e != hipSuccess) return hip_fail(e, "tree launch");
+  stage_mark(3, s);
   st->next_depth = dims->L + 1;
   return DARTREE_OK;
 }

@@ -66,9 +66,11 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within 8
 constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within 16
 
+// Every pattern used here is a permutation inside each 16-lane row, so all
+// lanes have a source and no old value is needed.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
 __device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
@@ -77,33 +79,80 @@ __device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
 // Exact lane exchanges x[lane ^ J] for the sorting networks. Strides 1..8
 // stay inside a 16-lane row (one or two DPP moves: quad xor 3 followed by a
 // half-row mirror is xor 4, a row mirror followed by a half-row mirror is
-// xor 8); stride 16 is a ds_swizzle swap of 16-lane groups; stride 32 goes
-// through ds_bpermute.
+// xor 8); strides 16 and 32 use the gfx950 permlane swaps: with the same
+// register as both operands, v_permlane16_swap returns the even rows copied
+// over the odd ones and the odd rows copied over the even ones (and
+// v_permlane32_swap the same for the two halves), so one select per lane
+// picks the partner's value.
 constexpr int kDppXor3 = 0x1B;        // quad_perm [3,2,1,0]
 template <int J>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
-  if constexpr (J == 1) return dpp<kDppXor1>(v);
-  else if constexpr (J == 2) return dpp<kDppXor2>(v);
-  else if constexpr (J == 4) return dpp<kDppHalfMirror>(dpp<kDppXor3>(v));
-  else if constexpr (J == 8) return dpp<kDppHalfMirror>(dpp<kDppMirror>(v));
-  else if constexpr (J == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
-  else return (uint32_t)__builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ J) << 2), (int)v);
+  if constexpr (J == 1) {
+    return dpp<kDppXor1>(v);
+  } else if constexpr (J == 2) {
+    return dpp<kDppXor2>(v);
+  } else if constexpr (J == 4) {
+    return dpp<kDppHalfMirror>(dpp<kDppXor3>(v));
+  } else if constexpr (J == 8) {
+    return dpp<kDppHalfMirror>(dpp<kDppMirror>(v));
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (__lane_id() & 16) ? r[0] : r[1];
+  } else {
+    static_assert(J == 32, "stride");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (__lane_id() & 32) ? r[0] : r[1];
+  }
 }
 
 // One compare-exchange stage of a bitonic network over 64-bit keys (hi, lo)
 // held one per lane; after the stage (K, J) every block of K lanes is
-// ordered descending where lane & K == 0 and ascending elsewhere.
+// ordered descending where lane & K == 0 and ascending elsewhere. Written
+// with selects only (no branches).
 template <int K, int J>
 __device__ __forceinline__ void bitonic_stage(uint32_t& hi, uint32_t& lo) {
-  const int lane = __lane_id();
+  const uint32_t lane = __lane_id();
   const uint32_t ph = lane_xor<J>(hi), pl = lane_xor<J>(lo);
   const uint64_t me = ((uint64_t)hi << 32) | lo, pa = ((uint64_t)ph << 32) | pl;
-  const bool take_max = ((lane & J) == 0) == ((lane & K) == 0);
-  if (take_max ? (pa > me) : (pa < me)) {
-    hi = ph;
-    lo = pl;
-  }
+  const bool gt = pa > me;
+  const bool take_max = (((lane / J) ^ (lane / K)) & 1u) == 0u;
+  const bool pick = gt == take_max;   // equal keys: either value is right
+  hi = pick ? ph : hi;
+  lo = pick ? pl : lo;
 }
+// The same network over 32-bit keys.
+template <int K, int J>
+__device__ __forceinline__ void bitonic_stage32(uint32_t& k) {
+  const uint32_t lane = __lane_id();
+  const uint32_t pk = lane_xor<J>(k);
+  const bool take_max = (((lane / J) ^ (lane / K)) & 1u) == 0u;
+  k = take_max ? max(k, pk) : min(k, pk);
+}
+// Sorts the wave's 64 32-bit keys descending (lane 0 holds the largest).
+__device__ __forceinline__ void wave_sort_desc32(uint32_t& k) {
+  bitonic_stage32<2, 1>(k);
+  bitonic_stage32<4, 2>(k);
+  bitonic_stage32<4, 1>(k);
+  bitonic_stage32<8, 4>(k);
+  bitonic_stage32<8, 2>(k);
+  bitonic_stage32<8, 1>(k);
+  bitonic_stage32<16, 8>(k);
+  bitonic_stage32<16, 4>(k);
+  bitonic_stage32<16, 2>(k);
+  bitonic_stage32<16, 1>(k);
+  bitonic_stage32<32, 16>(k);
+  bitonic_stage32<32, 8>(k);
+  bitonic_stage32<32, 4>(k);
+  bitonic_stage32<32, 2>(k);
+  bitonic_stage32<32, 1>(k);
+  bitonic_stage32<64, 32>(k);
+  bitonic_stage32<64, 16>(k);
+  bitonic_stage32<64, 8>(k);
+  bitonic_stage32<64, 4>(k);
+  bitonic_stage32<64, 2>(k);
+  bitonic_stage32<64, 1>(k);
+}
+
 // Sorts the wave's 64 keys descending (lane 0 holds the largest).
 __device__ __forceinline__ void wave_sort_desc(uint32_t& hi, uint32_t& lo) {
   bitonic_stage<2, 1>(hi, lo);

@@ -61,9 +61,9 @@ struct FX {
   static constexpr size_t sk_bytes = 8 * (kSkCap + 4);
   static constexpr size_t o_sk = o_zp;                // survivors reuse the Z partials (P3 vs P1/P2)
   static constexpr size_t o_as = o_zp + (zp_bytes > sk_bytes ? zp_bytes : sk_bytes);
-  static constexpr size_t o_ec = o_as + 4 * 16 * ASTR;  // [2][KC][RT], written by direct loads
-  static constexpr size_t o_hb = o_ec + 2 * 2 * KC * RT;  // [2][RT]
-  static constexpr size_t o_ck = o_hb + 2 * 4 * RT;
+  static constexpr size_t o_ec = o_as + 2 * 4 * 16 * ASTR;  // [KC][RT], written by direct loads
+  static constexpr size_t o_hb = o_ec + 2 * KC * RT;          // [RT]
+  static constexpr size_t o_ck = o_hb + 4 * RT;
   static constexpr size_t o_win = o_ck + 4 * 16 * KC;
   static constexpr size_t o_misc = o_win + 8 * 16;
   static constexpr size_t fixed = o_misc + 4 * 16;
@@ -118,9 +118,9 @@ struct FLay {
   LDS uint16_t* Sm;
   LDS uint16_t* Sl;
   LDS float* Zp;       // [KQ][16][ZSTR]
-  LDS float* AS;       // [16][ASTR]
-  LDS uint16_t* EC;    // [2][KC][RT] E rows of a depth's candidates (by depth parity)
-  LDS float* hb;       // [2][RT] h row of a depth
+  LDS float* AS;       // [2][16][ASTR] A*S over the two halves of the state
+  LDS uint16_t* EC;    // [KC][RT] E rows of the depth's candidates
+  LDS float* hb;       // [RT] h row of the depth
   LDS float* cumK;     // [16][KC]
   LDS uint64_t* sk;    // [kSkCap + 4] survivor keys
   LDS uint64_t* win;   // [16] the depth's survivors by rank
@@ -275,42 +275,55 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   __syncthreads();
 
   // ---- register-resident operands and the prefetch ---------------------------
+  // Wave w works on half hk = w / 8 of the state (k-steps 4hk..4hk+3, each 32
+  // wide) and, within it, on rows 32a..32a+31 of A*S (a = w % 8, two 16-row
+  // tiles with A resident in registers) and on one Z tile: candidate tile
+  // a % NT over the KSQ k-steps of its k-group a / NT (waves beyond NT*KQ/2
+  // per half have no Z tile). The pass over the half starts at the Z k-group,
+  // so the Z steps are the first KSQ steps.
+  constexpr int ZPH = C::NT * (C::KQ / 2);   // Z waves per half
   const int sub = (lane >> 4) * 8;
-  const bool zw = w < C::NT * C::KQ;   // this wave computes a Z tile
-  const int z_nt = w % C::NT, z_kq = w / C::NT;
-  const int kofs = zw ? z_kq * C::KSQ : 0;   // first k-step of this wave's pass
-  u16x8_t areg[8];
+  const int hk = w >> 3, aw = w & 7;
+  const bool zw = aw < ZPH;
+  const int z_nt = aw % C::NT, z_kg = aw / C::NT;
+  const int z_kq = hk * (C::KQ / 2) + z_kg;               // global k-group of the Z partial
+  const int zrot = zw ? z_kg * C::KSQ : 0;                // first local k-step of the pass
+  auto kstep = [&](int i) { return hk * 4 + ((i + zrot) & 3); };
+  u16x8_t areg[2][4];
   u16x8_t ureg[C::KSQ];   // U fragments of the depth being expanded, then of the next
   auto load_u = [&](u16x8_t (&dst)[C::KSQ], int d) {
     if (zw) {
       const int row = s.cid[(d - 1) * KC + z_nt * 16 + (lane & 15)];
       const uint16_t* src = U + (size_t)row * RT + sub;
 #pragma unroll
-      for (int i = 0; i < C::KSQ; ++i) dst[i] = *reinterpret_cast<const u16x8_t*>(src + (z_kq * C::KSQ + i) * 32);
+      for (int i = 0; i < C::KSQ; ++i) dst[i] = *reinterpret_cast<const u16x8_t*>(src + kstep(i) * 32);
     }
   };
   // E rows of depth d's candidates and the h row of depth d go straight from
-  // global memory into the depth's LDS buffers (lane l of a wave writes 16
-  // bytes at the wave's base + 16 l), no registers involved.
+  // global memory into LDS (lane l of a wave writes 16 bytes at the wave's
+  // base + 16 l), no registers involved. Issued when a depth starts (the
+  // previous depth's state update has read the buffers), consumed by the
+  // depth's state update.
   auto load_eh = [&](int d) {
-    LDS uint16_t* eb = s.EC + (size_t)(d & 1) * KC * RT;
 #pragma unroll
     for (int i = 0; i < C::NEV; ++i) {
       const int v0 = w * kWave + i * kT;   // first vector of this wave
       if (v0 < C::NEVEC) {
         const int v = v0 + lane;
         const int k = v / (RT / 8), c = (v % (RT / 8)) * 8;
-        __builtin_amdgcn_global_load_lds(E + (size_t)s.cid[(d - 1) * KC + k] * RT + c, eb + (size_t)v0 * 8, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(E + (size_t)s.cid[(d - 1) * KC + k] * RT + c, s.EC + (size_t)v0 * 8, 16, 0, 0);
       }
     }
-    if (w == 0) __builtin_amdgcn_global_load_lds(hq + (size_t)d * RT + lane * 4, s.hb + (d & 1) * RT, 16, 0, 0);
+    if (w == 0) __builtin_amdgcn_global_load_lds(hq + (size_t)d * RT + lane * 4, s.hb, 16, 0, 0);
   };
   if (expand) {
-    const uint16_t* arow = A + (size_t)(w * 16 + (lane & 15)) * RT + sub;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) areg[i] = *reinterpret_cast<const u16x8_t*>(arow + ((i + kofs) & 7) * 32);
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t* arow = A + (size_t)(aw * 32 + t * 16 + (lane & 15)) * RT + sub;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) areg[t][i] = *reinterpret_cast<const u16x8_t*>(arow + kstep(i) * 32);
+    }
     load_u(ureg, a.d0);
-    if (a.d0 < L) load_eh(a.d0);
     vmcnt_zero();
   }
   lds_sync();
@@ -319,57 +332,56 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   for (int d = a.d0; d <= a.d1; ++d) {
     const bool need_state = d < L;
     const int par = d & 1;
-    // P1: contractions, then the next depth's prefetch
-    {
-      // One pass over the parents' split states: each 32-wide k-step feeds the
-      // wave's A*S tile and, for the k-steps of its k-group, its Z tile (the
-      // operand fragment is the same for both). The pass starts at the
-      // wave's k-group (A fragments are held in that rotated order), so the
-      // Z steps are the first KSQ steps. Lanes of absent parents read nothing
-      // and contribute zeros.
-      const int p = lane & 15;
-      const bool pv = p < Wp;
-      const LDS uint16_t* rl = s.Sl + p * SSTR + sub;
-      const LDS uint16_t* rm = s.Sm + p * SSTR + sub;
-      const LDS uint16_t* rh = s.Sh + p * SSTR + sub;
-      const u16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
-      u16x8_t f[2][3];
-      auto ld = [&](int i, u16x8_t (&dst)[3]) {
-        const int o = ((i + kofs) & 7) * 32;
-        dst[0] = pv ? *reinterpret_cast<const LDS u16x8_t*>(rl + o) : zero;
-        dst[1] = pv ? *reinterpret_cast<const LDS u16x8_t*>(rm + o) : zero;
-        dst[2] = pv ? *reinterpret_cast<const LDS u16x8_t*>(rh + o) : zero;
-      };
-      ld(0, f[0]);
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, zacc = {0.f, 0.f, 0.f, 0.f};
+    // P1: the depth's E/h prefetch, the Z tiles, the next depth's U prefetch
+    if (need_state) load_eh(d);
+    const int p16 = lane & 15;
+    const bool pv = p16 < Wp;
+    const LDS uint16_t* rl = s.Sl + p16 * SSTR + sub;
+    const LDS uint16_t* rm = s.Sm + p16 * SSTR + sub;
+    const LDS uint16_t* rh = s.Sh + p16 * SSTR + sub;
+    const u16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
+    // split-state fragment of local k-step i (lanes of absent parents: zeros)
+    auto ld = [&](int i, u16x8_t (&dst)[3]) {
+      const int o = kstep(i) * 32;
+      dst[0] = pv ? *reinterpret_cast<const LDS u16x8_t*>(rl + o) : zero;
+      dst[1] = pv ? *reinterpret_cast<const LDS u16x8_t*>(rm + o) : zero;
+      dst[2] = pv ? *reinterpret_cast<const LDS u16x8_t*>(rh + o) : zero;
+    };
+    if (zw) {
+      u16x8_t f[C::KSQ][3];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i + 1 < 8) ld(i + 1, f[(i + 1) & 1]);
-        if (i < C::KSQ && zw) {
-          zacc = mfma_bf16(f[i & 1][0], ureg[i], zacc);
-          zacc = mfma_bf16(f[i & 1][1], ureg[i], zacc);
-          zacc = mfma_bf16(f[i & 1][2], ureg[i], zacc);
-        }
-        if (need_state) {
-          acc = mfma_bf16(areg[i], f[i & 1][0], acc);
-          acc = mfma_bf16(areg[i], f[i & 1][1], acc);
-          acc = mfma_bf16(areg[i], f[i & 1][2], acc);
-        }
-      }
-      if (zw) {
+      for (int i = 0; i < C::KSQ; ++i) ld(i, f[i]);
+      f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s.Zp[(z_kq * 16 + (lane >> 4) * 4 + i) * C::ZSTR + z_nt * 16 + (lane & 15)] = zacc[i];
+      for (int i = 0; i < C::KSQ; ++i) {
+        zacc = mfma_bf16(f[i][0], ureg[i], zacc);
+        zacc = mfma_bf16(f[i][1], ureg[i], zacc);
+        zacc = mfma_bf16(f[i][2], ureg[i], zacc);
       }
-      if (need_state) *reinterpret_cast<LDS f32x4_t*>(s.AS + p * ASTR + w * 16 + (lane >> 4) * 4) = acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s.Zp[(z_kq * 16 + (lane >> 4) * 4 + i) * C::ZSTR + z_nt * 16 + (lane & 15)] = zacc[i];
     }
-    if (d < a.d1) {
-      load_u(ureg, d + 1);   // the Z MFMAs above were the last readers
-      if (d + 1 < L) load_eh(d + 1);
-    }
+    if (d < a.d1) load_u(ureg, d + 1);   // the Z MFMAs above were the last readers
     lds_sync();
 
-    // P2: log-softmax and keys (kept in registers); the bound T
+    // P2: A*S of the parents (for the state update) on the matrix cores while
+    // the parents' waves do the log-softmax and keys; the bound T
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    if (need_state) {
+      u16x8_t f[2][3];
+      ld(0, f[0]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i + 1 < 4) ld(i + 1, f[(i + 1) & 1]);
+        acc0 = mfma_bf16(areg[0][i], f[i & 1][0], acc0);
+        acc1 = mfma_bf16(areg[1][i], f[i & 1][0], acc1);
+        acc0 = mfma_bf16(areg[0][i], f[i & 1][1], acc0);
+        acc1 = mfma_bf16(areg[1][i], f[i & 1][1], acc1);
+        acc0 = mfma_bf16(areg[0][i], f[i & 1][2], acc0);
+        acc1 = mfma_bf16(areg[1][i], f[i & 1][2], acc1);
+      }
+    }
     const float bd = a.beta * (float)d;
     uint32_t kh = 0u, kl = 0u;
     if (w < Wp) {
@@ -396,16 +408,16 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
         kh = f32_key(cum + bd);
         kl = ~(((uint32_t)tok << 10) | ((uint32_t)p << 6) | (uint32_t)lane);
       }
-      // the largest 16-bit prefix t of the high words with at least W of the
-      // wave's keys at or above t << 16 (K >= W keys are valid; invalid lanes
-      // hold 0 and never count since t >= 1 << 16 once any bit is set)
-      const uint64_t vmask = __ballot(v);
-      uint32_t t = 0u;
-      for (int b = 15; b >= 0; --b) {
-        const uint32_t c = (t | (1u << b)) << 16;
-        if (__popcll(__builtin_amdgcn_ballot_w64(kh >= c) & vmask) >= W) t |= 1u << b;
-      }
-      if (lane == 0) lds_max((LDS unsigned*)&s.misc[par], t << 16);
+      // the W-th largest high word of the wave's keys is its bound
+      uint32_t sk32 = kh;
+      wave_sort_desc32(sk32);
+      const uint32_t t = readlane(sk32, W - 1);
+      if (lane == 0) lds_max((LDS unsigned*)&s.misc[par], t);
+    }
+    if (need_state) {
+      LDS float* asr = s.AS + (hk * 16 + p16) * ASTR + aw * 32 + (lane >> 4) * 4;
+      *reinterpret_cast<LDS f32x4_t*>(asr) = acc0;
+      *reinterpret_cast<LDS f32x4_t*>(asr + 16) = acc1;
     }
     lds_sync();
 
@@ -456,6 +468,7 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       // the other parity's bound and count are free again (read one depth ago)
       if (tid < 2) s.misc[(par ^ 1) + 2 * tid] = 0;
     }
+    vmcnt_zero();   // this wave's E/h prefetch for the state update has landed
     lds_sync();
 
     // P4: states of the survivors, one wave each; path ranks of the level
@@ -463,9 +476,11 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       const uint32_t lo = ~(uint32_t)s.win[w];
       const int k = lo & 63, p = (lo >> 6) & 15;
       const int j0 = lane * 4;
-      const f32x4_t as4 = *reinterpret_cast<const LDS f32x4_t*>(s.AS + p * ASTR + j0);
-      const u32x2_t e2 = *reinterpret_cast<const LDS u32x2_t*>(s.EC + ((size_t)par * KC + k) * RT + j0);
-      const f32x4_t h4 = *reinterpret_cast<const LDS f32x4_t*>(s.hb + par * RT + j0);
+      const f32x4_t a0 = *reinterpret_cast<const LDS f32x4_t*>(s.AS + p * ASTR + j0);
+      const f32x4_t a1 = *reinterpret_cast<const LDS f32x4_t*>(s.AS + (16 + p) * ASTR + j0);
+      const f32x4_t as4 = a0 + a1;
+      const u32x2_t e2 = *reinterpret_cast<const LDS u32x2_t*>(s.EC + (size_t)k * RT + j0);
+      const f32x4_t h4 = *reinterpret_cast<const LDS f32x4_t*>(s.hb + j0);
       const float ev[4] = {bf16_to_f32(e2.x & 0xFFFFu), bf16_to_f32(e2.x >> 16), bf16_to_f32(e2.y & 0xFFFFu),
                            bf16_to_f32(e2.y >> 16)};
       float v[4];
@@ -486,7 +501,6 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       level_lex_wave(s, d, W, nk, tk, ps);
     }
     Wp = nk;
-    vmcnt_zero();   // this wave's prefetch for the next depth has landed
     lds_sync();
   }
   __syncthreads();

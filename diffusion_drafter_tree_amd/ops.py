@@ -174,3 +174,20 @@ def run_steps(dims: C.Dims, head: DeviceHead, logits: torch.Tensor, H_or_h: torc
         expand_depth(dims, head, rb.cand_ids, rb.cand_logit, h, rb, d0, d1, stream)
     select_topB(dims, rb, stream)
     tree_mask(dims, rb.n_sel, rb.parent, rb.mask, stream)
+
+
+def set_stage_events(events: Optional[list]):
+    """Profiling hook: record the given four torch.cuda.Event objects around the
+    stages of every following build_round on this thread (scan, merge, tree
+    kernel); None clears it. Argument marshalling only."""
+    lib = C.load()
+    if not events:
+        _check(lib.dartree_set_stage_events(None, 0), "set_stage_events")
+        return
+    if len(events) != 4:
+        raise ValueError("need four events")
+    for e in events:
+        if int(e.cuda_event) == 0:   # torch creates the HIP event on its first record
+            e.record()
+    arr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(int(e.cuda_event)) for e in events])
+    _check(lib.dartree_set_stage_events(arr, 4), "set_stage_events")

@@ -195,6 +195,17 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
                                    int32_t* parent, float* score, int32_t* slot, uint64_t* mask, void* ws,
                                    size_t ws_bytes, void* stream);
 
+/* Profiling hook (not part of a round's computation). When set, every
+ * following dartree_build_round on this thread records events[0] before its
+ * first launch, events[1] after the logits scan (with the head tiles),
+ * events[2] after the candidate merge (recorded also when no merge runs) and
+ * events[3] after the tree kernel, each on the call's stream, so that
+ * hipEventElapsedTime gives the time of each stage. `events` holds n = 4
+ * hipEvent_t handles (passed as void*) created by the caller and kept alive
+ * while set; n = 0 (events may be NULL) clears the hook. Returns
+ * INVALID_ARGUMENT for any other n or NULL handles. */
+dartree_status dartree_set_stage_events(void* const* events, int32_t n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -143,3 +143,12 @@ def test_binding_config_dims_match_header_limits():
         d = ops.make_dims(I.CONFIGS[name])
         st, _ = ws_size(C.load(), d)
         assert st == C.OK, (name, C.last_error())
+
+
+def test_stage_event_hook_validates_on_host(lib):
+    assert lib.dartree_set_stage_events(None, 0) == C.OK
+    assert lib.dartree_set_stage_events(None, 4) == C.ERR_INVALID_ARGUMENT
+    arr = (ctypes.c_void_p * 4)(0x10, None, 0x30, 0x40)
+    assert lib.dartree_set_stage_events(arr, 4) == C.ERR_INVALID_ARGUMENT
+    assert "NULL" in C.last_error()
+    assert lib.dartree_set_stage_events(arr, 3) == C.ERR_INVALID_ARGUMENT
