@@ -54,16 +54,15 @@ struct FX {
   static constexpr int NEVEC = KC * RT / 8;                  // 16-byte vectors of E rows
   static constexpr int NEV = NEVEC >= kT ? NEVEC / kT : 1;   // per thread
   static constexpr size_t o_sh = 0;
-  static constexpr size_t o_sm = o_sh + 2 * 16 * SSTR;
-  static constexpr size_t o_sl = o_sm + 2 * 16 * SSTR;
+  static constexpr size_t o_sl = o_sh + 2 * 16 * SSTR;
   static constexpr size_t o_zp = o_sl + 2 * 16 * SSTR;
   static constexpr size_t zp_bytes = 4 * KQ * 16 * ZSTR;
   static constexpr size_t sk_bytes = 8 * (kSkCap + 4);
   static constexpr size_t o_sk = o_zp;                // survivors reuse the Z partials (P3 vs P1/P2)
   static constexpr size_t o_as = o_zp + (zp_bytes > sk_bytes ? zp_bytes : sk_bytes);
-  static constexpr size_t o_ec = o_as + 2 * 4 * 16 * ASTR;  // [KC][RT], written by direct loads
-  static constexpr size_t o_hb = o_ec + 2 * KC * RT;          // [RT]
-  static constexpr size_t o_ck = o_hb + 4 * RT;
+  static constexpr size_t o_ec = o_as + 2 * 4 * 16 * ASTR;  // [2][KC][RT], written by direct loads
+  static constexpr size_t o_hb = o_ec + 2 * 2 * KC * RT;      // [2][RT]
+  static constexpr size_t o_ck = o_hb + 2 * 4 * RT;
   static constexpr size_t o_win = o_ck + 4 * 16 * KC;
   static constexpr size_t o_misc = o_win + 8 * 16;
   static constexpr size_t fixed = o_misc + 4 * 16;
@@ -93,7 +92,7 @@ __host__ __device__ inline VOff voff(int L, int KC, int W, int B, size_t fixed) 
   o.cum = take(4 * LW);
   o.sb = take(4 * LW);
   o.cnt = take(4 * 32);
-  o.nkey = take(8 * LW);
+  o.nkey = take(8 * (LW + 8));
   o.sf = take(4 * LW);
   o.eix = take(4 * LW);
   o.nd = take(4 * 32);
@@ -114,13 +113,12 @@ size_t fixed_bytes(int KC) {
 }
 
 struct FLay {
-  LDS uint16_t* Sh;    // [16][SSTR] split parent states
-  LDS uint16_t* Sm;
-  LDS uint16_t* Sl;
+  LDS uint16_t* Sh;    // [16][SSTR] parent states, fp16 high part
+  LDS uint16_t* Sl;    // [16][SSTR] fp16 low part (the rest of the fp32 value)
   LDS float* Zp;       // [KQ][16][ZSTR]
   LDS float* AS;       // [2][16][ASTR] A*S over the two halves of the state
-  LDS uint16_t* EC;    // [KC][RT] E rows of the depth's candidates
-  LDS float* hb;       // [RT] h row of the depth
+  LDS uint16_t* EC;    // [2][KC][RT] E rows of a depth's candidates (by depth parity)
+  LDS float* hb;       // [2][RT] h row of a depth (by depth parity)
   LDS float* cumK;     // [16][KC]
   LDS uint64_t* sk;    // [kSkCap + 4] survivor keys
   LDS uint64_t* win;   // [16] the depth's survivors by rank
@@ -150,7 +148,6 @@ __device__ __forceinline__ FLay make_flay(const VOff& o) {
   LDS char* b = (LDS char*)smem;
   FLay s;
   s.Sh = (LDS uint16_t*)(b + C::o_sh);
-  s.Sm = (LDS uint16_t*)(b + C::o_sm);
   s.Sl = (LDS uint16_t*)(b + C::o_sl);
   s.Zp = (LDS float*)(b + C::o_zp);
   s.AS = (LDS float*)(b + C::o_as);
@@ -179,15 +176,39 @@ __device__ __forceinline__ FLay make_flay(const VOff& o) {
   return s;
 }
 
-// split of 4 consecutive state values into the three bf16 planes (8 bytes each)
+// two fp32 values to fp16, rounding toward zero (v_cvt_pkrtz_f16_f32)
+__device__ __forceinline__ h16x2_t pkrtz(float a, float b) {
+  typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(h16x2_t, (fp16x2_t)__builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// Two fp16 parts of 4 consecutive fp32 state values (8 bytes per plane):
+// hi = the value truncated to fp16, lo = the remainder (exact in fp32)
+// truncated to fp16; hi + lo carries 22 significant bits (relative error at
+// most 2^-22 for |s| >= 2^-14, absolute at most 2^-25 below).
 __device__ __forceinline__ void split_store4(const FLay& s, int row, int j0, const float (&v)[4]) {
-  uint32_t h[4], m[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) split3(v[i], h[i], m[i], l[i]);
+  const h16x2_t h01 = pkrtz(v[0], v[1]);
+  const h16x2_t h23 = pkrtz(v[2], v[3]);
+  const h16x2_t l01 = pkrtz(v[0] - (float)h01.x, v[1] - (float)h01.y);
+  const h16x2_t l23 = pkrtz(v[2] - (float)h23.x, v[3] - (float)h23.y);
   const int o = row * SSTR + j0;
-  *reinterpret_cast<LDS u32x2_t*>(s.Sh + o) = u32x2_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-  *reinterpret_cast<LDS u32x2_t*>(s.Sm + o) = u32x2_t{m[0] | (m[1] << 16), m[2] | (m[3] << 16)};
-  *reinterpret_cast<LDS u32x2_t*>(s.Sl + o) = u32x2_t{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+  *reinterpret_cast<LDS u32x2_t*>(s.Sh + o) =
+      u32x2_t{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+  *reinterpret_cast<LDS u32x2_t*>(s.Sl + o) =
+      u32x2_t{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
+}
+
+// 8 bf16 weights as fp16 (exact for every bf16 value of magnitude >= 2^-17
+// or zero; smaller ones are truncated by at most 2^-25)
+__device__ __forceinline__ h16x8_t bf16x8_to_f16(u16x8_t x) {
+  h16x8_t r;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const h16x2_t p = pkrtz(bf16_to_f32(x[i]), bf16_to_f32(x[i + 1]));
+    r[i] = p.x;
+    r[i + 1] = p.y;
+  }
+  return r;
 }
 
 // tanh(x) = 1 - 2 / (2^(2 x log2 e) + 1) on the hardware exp2 and reciprocal
@@ -289,8 +310,8 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   const int z_kq = hk * (C::KQ / 2) + z_kg;               // global k-group of the Z partial
   const int zrot = zw ? z_kg * C::KSQ : 0;                // first local k-step of the pass
   auto kstep = [&](int i) { return hk * 4 + ((i + zrot) & 3); };
-  u16x8_t areg[2][4];
-  u16x8_t ureg[C::KSQ];   // U fragments of the depth being expanded, then of the next
+  h16x8_t areg[2][4];   // A fragments as fp16
+  u16x8_t ureg[C::KSQ];   // U fragments (bf16) of the depth being expanded, then of the next
   auto load_u = [&](u16x8_t (&dst)[C::KSQ], int d) {
     if (zw) {
       const int row = s.cid[(d - 1) * KC + z_nt * 16 + (lane & 15)];
@@ -300,30 +321,33 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
     }
   };
   // E rows of depth d's candidates and the h row of depth d go straight from
-  // global memory into LDS (lane l of a wave writes 16 bytes at the wave's
-  // base + 16 l), no registers involved. Issued when a depth starts (the
-  // previous depth's state update has read the buffers), consumed by the
-  // depth's state update.
+  // global memory into the depth's LDS buffers (lane l of a wave writes 16
+  // bytes at the wave's base + 16 l), no registers involved. Issued one
+  // depth ahead; each wave waits for its own before the barrier that
+  // precedes the state update that reads them.
   auto load_eh = [&](int d) {
+    LDS uint16_t* eb = s.EC + (size_t)(d & 1) * KC * RT;
 #pragma unroll
     for (int i = 0; i < C::NEV; ++i) {
       const int v0 = w * kWave + i * kT;   // first vector of this wave
       if (v0 < C::NEVEC) {
         const int v = v0 + lane;
         const int k = v / (RT / 8), c = (v % (RT / 8)) * 8;
-        __builtin_amdgcn_global_load_lds(E + (size_t)s.cid[(d - 1) * KC + k] * RT + c, s.EC + (size_t)v0 * 8, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(E + (size_t)s.cid[(d - 1) * KC + k] * RT + c, eb + (size_t)v0 * 8, 16, 0, 0);
       }
     }
-    if (w == 0) __builtin_amdgcn_global_load_lds(hq + (size_t)d * RT + lane * 4, s.hb, 16, 0, 0);
+    if (w == 0)
+      __builtin_amdgcn_global_load_lds(hq + (size_t)d * RT + lane * 4, s.hb + (size_t)(d & 1) * RT, 16, 0, 0);
   };
   if (expand) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const uint16_t* arow = A + (size_t)(aw * 32 + t * 16 + (lane & 15)) * RT + sub;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) areg[t][i] = *reinterpret_cast<const u16x8_t*>(arow + kstep(i) * 32);
+      for (int i = 0; i < 4; ++i) areg[t][i] = bf16x8_to_f16(*reinterpret_cast<const u16x8_t*>(arow + kstep(i) * 32));
     }
     load_u(ureg, a.d0);
+    if (a.d0 < L) load_eh(a.d0);
     vmcnt_zero();
   }
   lds_sync();
@@ -332,87 +356,90 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   for (int d = a.d0; d <= a.d1; ++d) {
     const bool need_state = d < L;
     const int par = d & 1;
-    // P1: the depth's E/h prefetch, the Z tiles, the next depth's U prefetch
-    if (need_state) load_eh(d);
+    // P1: the Z tiles (the critical path: nothing else is issued here)
     const int p16 = lane & 15;
-    const bool pv = p16 < Wp;
-    const LDS uint16_t* rl = s.Sl + p16 * SSTR + sub;
-    const LDS uint16_t* rm = s.Sm + p16 * SSTR + sub;
-    const LDS uint16_t* rh = s.Sh + p16 * SSTR + sub;
-    const u16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
-    // split-state fragment of local k-step i (lanes of absent parents: zeros)
-    auto ld = [&](int i, u16x8_t (&dst)[3]) {
+    // Lanes of absent parents (p >= Wp) read parent 0's row: their results
+    // land only in rows / columns of absent parents, which nobody reads, and
+    // the loads stay branch-free.
+    const int prow = p16 < Wp ? p16 : 0;
+    const LDS uint16_t* rl = s.Sl + prow * SSTR + sub;
+    const LDS uint16_t* rh = s.Sh + prow * SSTR + sub;
+    // fp16 state fragment (low, high part) of local k-step i
+    auto ld = [&](int i, h16x8_t (&dst)[2]) {
       const int o = kstep(i) * 32;
-      dst[0] = pv ? *reinterpret_cast<const LDS u16x8_t*>(rl + o) : zero;
-      dst[1] = pv ? *reinterpret_cast<const LDS u16x8_t*>(rm + o) : zero;
-      dst[2] = pv ? *reinterpret_cast<const LDS u16x8_t*>(rh + o) : zero;
+      dst[0] = *reinterpret_cast<const LDS h16x8_t*>(rl + o);
+      dst[1] = *reinterpret_cast<const LDS h16x8_t*>(rh + o);
     };
     if (zw) {
-      u16x8_t f[C::KSQ][3];
+      h16x8_t f[C::KSQ][2], uf[C::KSQ];
 #pragma unroll
-      for (int i = 0; i < C::KSQ; ++i) ld(i, f[i]);
+      for (int i = 0; i < C::KSQ; ++i) {
+        ld(i, f[i]);
+        uf[i] = bf16x8_to_f16(ureg[i]);
+      }
       f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < C::KSQ; ++i) {
-        zacc = mfma_bf16(f[i][0], ureg[i], zacc);
-        zacc = mfma_bf16(f[i][1], ureg[i], zacc);
-        zacc = mfma_bf16(f[i][2], ureg[i], zacc);
+        zacc = mfma_f16(f[i][0], uf[i], zacc);
+        zacc = mfma_f16(f[i][1], uf[i], zacc);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         s.Zp[(z_kq * 16 + (lane >> 4) * 4 + i) * C::ZSTR + z_nt * 16 + (lane & 15)] = zacc[i];
     }
-    if (d < a.d1) load_u(ureg, d + 1);   // the Z MFMAs above were the last readers
     lds_sync();
 
     // P2: A*S of the parents (for the state update) on the matrix cores while
-    // the parents' waves do the log-softmax and keys; the bound T
+    // the parents' waves do the log-softmax and keys; the bound T. For a
+    // parent's wave both run in one branch-free block whose schedule
+    // interleaves the 24 MFMAs with the vector work.
+    // the next depth's prefetch drains behind this phase's work: U fragments
+    // (the Z MFMAs of P1 were their last readers) and E/h rows
+    vmcnt_zero();   // this wave's loads of one depth ago (E/h of this depth) have landed
+    if (d < a.d1) load_u(ureg, d + 1);
+    if (d + 1 < L && d < a.d1) load_eh(d + 1);
     f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     if (need_state) {
-      u16x8_t f[2][3];
+      h16x8_t f[2][2];
       ld(0, f[0]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (i + 1 < 4) ld(i + 1, f[(i + 1) & 1]);
-        acc0 = mfma_bf16(areg[0][i], f[i & 1][0], acc0);
-        acc1 = mfma_bf16(areg[1][i], f[i & 1][0], acc1);
-        acc0 = mfma_bf16(areg[0][i], f[i & 1][1], acc0);
-        acc1 = mfma_bf16(areg[1][i], f[i & 1][1], acc1);
-        acc0 = mfma_bf16(areg[0][i], f[i & 1][2], acc0);
-        acc1 = mfma_bf16(areg[1][i], f[i & 1][2], acc1);
+        acc0 = mfma_f16(areg[0][i], f[i & 1][0], acc0);
+        acc1 = mfma_f16(areg[1][i], f[i & 1][0], acc1);
+        acc0 = mfma_f16(areg[0][i], f[i & 1][1], acc0);
+        acc1 = mfma_f16(areg[1][i], f[i & 1][1], acc1);
       }
     }
     const float bd = a.beta * (float)d;
     uint32_t kh = 0u, kl = 0u;
     if (w < Wp) {
       const int p = w;
-      const bool v = lane < KC;
-      float z = -__builtin_huge_valf();
-      int tok = 0;
-      if (v) {
-        float zs = 0.f;
+      const bool v = KC == kWave ? true : lane < KC;
+      const int kk = v ? lane : 0;
+      float zs = 0.f;
 #pragma unroll
-        for (int qq = 0; qq < C::KQ; ++qq) zs += s.Zp[(qq * 16 + p) * C::ZSTR + lane];
-        z = zs + s.clog[(d - 1) * KC + lane];
-        tok = s.cid[(d - 1) * KC + lane];
-      }
+      for (int qq = 0; qq < C::KQ; ++qq) zs += s.Zp[(qq * 16 + p) * C::ZSTR + kk];
+      const float z = v ? zs + s.clog[(d - 1) * KC + kk] : -__builtin_huge_valf();
+      const int tok = s.cid[(d - 1) * KC + kk];
       const float cp = d == 1 ? 0.f : s.lv_cum[(d - 2) * W + p];
       // exp and log on the hardware exp2/log2 (relative error about 1e-7
       // where it matters: terms near the maximum dominate the sum)
       const float m = wave_max_f32(z);
       const float ssum = wave_sum_f32(v ? __builtin_amdgcn_exp2f((z - m) * 1.4426950408889634f) : 0.f);
       const float lse = m + __builtin_amdgcn_logf(ssum) * 0.6931471805599453f;
-      if (v) {
-        const float cum = cp + fminf(z - lse, 0.f);
-        s.cumK[p * KC + lane] = cum;
-        kh = f32_key(cum + bd);
-        kl = ~(((uint32_t)tok << 10) | ((uint32_t)p << 6) | (uint32_t)lane);
+      const float cum = cp + fminf(z - lse, 0.f);
+      if (v) s.cumK[p * KC + lane] = cum;
+      kh = v ? f32_key(cum + bd) : 0u;
+      kl = v ? ~(((uint32_t)tok << 10) | ((uint32_t)p << 6) | (uint32_t)lane) : 0u;
+      if (p == 0) {
+        // Bound T: the W-th largest high word among the children of the
+        // level's first parent (the one with the best score, its W best
+        // children alone reach T). K >= W children are valid.
+        uint32_t sk32 = kh;
+        wave_sort_desc32(sk32);
+        if (lane == 0) s.misc[par] = (int)readlane(sk32, W - 1);
       }
-      // the W-th largest high word of the wave's keys is its bound
-      uint32_t sk32 = kh;
-      wave_sort_desc32(sk32);
-      const uint32_t t = readlane(sk32, W - 1);
-      if (lane == 0) lds_max((LDS unsigned*)&s.misc[par], t);
     }
     if (need_state) {
       LDS float* asr = s.AS + (hk * 16 + p16) * ASTR + aw * 32 + (lane >> 4) * 4;
@@ -468,7 +495,6 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       // the other parity's bound and count are free again (read one depth ago)
       if (tid < 2) s.misc[(par ^ 1) + 2 * tid] = 0;
     }
-    vmcnt_zero();   // this wave's E/h prefetch for the state update has landed
     lds_sync();
 
     // P4: states of the survivors, one wave each; path ranks of the level
@@ -479,8 +505,8 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       const f32x4_t a0 = *reinterpret_cast<const LDS f32x4_t*>(s.AS + p * ASTR + j0);
       const f32x4_t a1 = *reinterpret_cast<const LDS f32x4_t*>(s.AS + (16 + p) * ASTR + j0);
       const f32x4_t as4 = a0 + a1;
-      const u32x2_t e2 = *reinterpret_cast<const LDS u32x2_t*>(s.EC + (size_t)k * RT + j0);
-      const f32x4_t h4 = *reinterpret_cast<const LDS f32x4_t*>(s.hb + j0);
+      const u32x2_t e2 = *reinterpret_cast<const LDS u32x2_t*>(s.EC + ((size_t)par * KC + k) * RT + j0);
+      const f32x4_t h4 = *reinterpret_cast<const LDS f32x4_t*>(s.hb + par * RT + j0);
       const float ev[4] = {bf16_to_f32(e2.x & 0xFFFFu), bf16_to_f32(e2.x >> 16), bf16_to_f32(e2.y & 0xFFFFu),
                            bf16_to_f32(e2.y >> 16)};
       float v[4];
@@ -542,69 +568,75 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
         __builtin_amdgcn_wave_barrier();
       }
     }
-    __syncthreads();
   }
-  const int N = L * W;
-  for (int i = tid; i < N; i += kT) {
-    const int d = i / W + 1, sl = i - (d - 1) * W;
+  // Node keys (0 for empty slots), zero-padded to a multiple of 8.
+  const int N = L * W, N8 = (N + 7) & ~7;
+  for (int i = tid; i < N8; i += kT) {
     uint64_t key = 0ull;
-    if (sl < s.lv_cnt[d - 1]) {
-      const uint32_t tok = (uint32_t)s.lv_tok[i] & 0x3FFFFu;
-      const uint32_t ps = d == 1 ? 0u : ((uint32_t)s.lv_ps[i] & 0x1FFu);
-      key = ((uint64_t)f32_key(s.lv_sb[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (((uint32_t)d << 27) | (tok << 9) | ps));
+    if (i < N) {
+      const int d = i / W + 1, sl = i - (d - 1) * W;
+      if (sl < s.lv_cnt[d - 1]) {
+        const uint32_t tok = (uint32_t)s.lv_tok[i] & 0x3FFFFu;
+        const uint32_t ps = d == 1 ? 0u : ((uint32_t)s.lv_ps[i] & 0x1FFu);
+        key = ((uint64_t)f32_key(s.lv_sb[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (((uint32_t)d << 27) | (tok << 9) | ps));
+      }
     }
     s.nkey[i] = key;
-    s.sf[i] = 0;
   }
-  if (tid < 32) s.nd[tid] = 0;
-  __syncthreads();
+  if (tid < 32) s.nd[tid] = 0;   // per level: bit (path rank) set when the node is selected
+  lds_sync();
   {
-    // rank of each node = number of larger keys; G threads per node
-    int G = 8;
+    // rank of each node = number of larger keys, G threads per node, eight
+    // keys per step; a node is selected when its rank is below B
+    int G = 16;
     while (G > 1 && N * G > kT) G >>= 1;
-    const int per = (N + G - 1) / G;
+    const int per = ((N + G - 1) / G + 7) & ~7;
     const int x = tid / G, seg = tid - x * G;
     uint64_t kx = 0ull;
-    int cnt = 0;
+    uint32_t cnt = 0u;
     if (x < N) {
       kx = s.nkey[x];
-      const int y1 = min(N, (seg + 1) * per);
-      for (int y = seg * per; y < y1; ++y) cnt += s.nkey[y] > kx;
+      const int y1 = min(N8, (seg + 1) * per);
+      for (int y = seg * per; y < y1; y += 8) {
+        uint64_t k8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) k8[e] = s.nkey[y + e];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cnt += k8[e] > kx ? 1u : 0u;
+      }
     }
-    uint32_t c2 = (uint32_t)cnt;
-    if (G >= 2) c2 += dpp<kDppXor1>(c2);
-    if (G >= 4) c2 += dpp<kDppXor2>(c2);
-    if (G >= 8) c2 += lane_xor<4>(c2);
-    if (x < N && seg == 0 && kx != 0ull && (int)c2 < B) {
-      s.sf[x] = 1;
-      lds_add(&s.nd[x / W], 1);
-    }
+    const uint32_t rk = group_sum(cnt, G);
+    if (x < N && seg == 0 && kx != 0ull && (int)rk < B) lds_or(&s.nd[x / W], 1 << s.lv_lex[x]);
   }
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int d = 0; d < L; ++d) {
-      s.base[d] = acc;
-      acc += s.nd[d];
-    }
-    s.base[L] = acc;
+  lds_sync();
+  // emitted index: selected nodes of earlier levels, then selected nodes of
+  // the level with a smaller path rank (breadth-first order = path order)
+  uint32_t lvm[32];
+#pragma unroll
+  for (int i = 0; i < 32; i += 4) {
+    const u32x4_t v4 = *reinterpret_cast<const LDS u32x4_t*>(s.nd + i);
+    lvm[i] = v4.x;
+    lvm[i + 1] = v4.y;
+    lvm[i + 2] = v4.z;
+    lvm[i + 3] = v4.w;
   }
-  __syncthreads();
-  const int n = s.base[L];
-  // emitted index: level base + selected nodes of the level with a smaller path rank
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) n += __popc(lvm[i]);
   for (int i = tid; i < N; i += kT) {
+    const int d = i / W + 1;
+    const uint32_t m = s.nd[d - 1];
+    const int lx = s.lv_lex[i];
     int e = -1;
-    if (s.sf[i]) {
-      const int d = i / W + 1;
-      const int row = (d - 1) * W, cnt = s.lv_cnt[d - 1];
-      const int my = s.lv_lex[i];
-      int rk = 0;
-      for (int sl = 0; sl < cnt; ++sl) rk += s.sf[row + sl] && s.lv_lex[row + sl] < my;
-      e = s.base[d - 1] + rk;
+    if (i - (d - 1) * W < s.lv_cnt[d - 1] && ((m >> lx) & 1u)) {
+      int base = 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) base += j < d - 1 ? __popc(lvm[j]) : 0;
+      e = base + __popc(m & ((1u << lx) - 1u));
     }
     s.eix[i] = e;
   }
-  __syncthreads();
+  lds_sync();
   int32_t* o_tok = a.tok + (size_t)q * B;
   int32_t* o_dep = a.depth + (size_t)q * B;
   int32_t* o_par = a.parent + (size_t)q * B;
@@ -632,36 +664,31 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   }
   if (tid == 0) a.n_sel[q] = n;
   if (!a.do_mask) return;
-  __syncthreads();
+  lds_sync();
 
   // ---- ancestor mask ------------------------------------------------------------------
   const int words = (B + 63) / 64;
   uint64_t* mq = a.mask + (size_t)q * B * words;
   if (words == 1) {
-    // pointer doubling: after round k, mb covers a node and its 2^k - 1
-    // nearest ancestors and ab points at its 2^k-th ancestor
-    if (tid < 64) {
-      s.mb[tid] = tid < n ? (1ull << tid) : 0ull;
-      s.ab[tid] = tid < n ? s.epar[tid] : -1;
-    }
-    __syncthreads();
-    int cur = 0;
-    for (int span = 1; span < L; span *= 2) {
-      if (tid < 64) {
-        const int an = s.ab[cur * 64 + tid];
-        uint64_t mm = s.mb[cur * 64 + tid];
-        int nx = -1;
-        if (an >= 0 && an < tid) {
-          mm |= s.mb[cur * 64 + an];
-          nx = s.ab[cur * 64 + an];
+    // one wave, pointer doubling with lane shuffles: after round k, mb covers
+    // a node and its 2^k - 1 nearest ancestors and an is its 2^k-th ancestor
+    if (w == 0) {
+      int an = lane < n ? s.epar[lane] : -1;
+      uint64_t mb = lane < n ? (1ull << lane) : 0ull;
+      for (int span = 1; span < L; span *= 2) {
+        const int src = (an >= 0 && an < lane) ? an : lane;
+        const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)mb, src, kWave);
+        const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(mb >> 32), src, kWave);
+        const int an2 = __shfl(an, src, kWave);
+        if (src != lane) {
+          mb |= ((uint64_t)hi << 32) | lo;
+          an = an2;
+        } else {
+          an = -1;
         }
-        s.mb[(cur ^ 1) * 64 + tid] = mm;
-        s.ab[(cur ^ 1) * 64 + tid] = nx;
       }
-      __syncthreads();
-      cur ^= 1;
+      if (lane < B) mq[lane] = mb;
     }
-    if (tid < B) mq[tid] = s.mb[cur * 64 + tid];
   } else {
     for (int t = tid; t < B * words; t += kT) {
       const int i = t / words, wd = t - i * words;
