@@ -355,7 +355,20 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
   const float* hin = static_cast<const float*>(H_or_h);
   dartree::TreeArgs ta = tree_args(dims, head, cand_ids, cand_logit, dims->D > 0 ? h : hin, st, 1, dims->L);
   set_tree_out(ta, n_sel, tok, depth, parent, score, slot, mask);
-  dartree::TreePlan tp;
+  // the block-decoding tree kernel merges the scan's slice lists itself
+  uint64_t* lists = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + w.lists_off);
+  if (w.plan.S > 1) {
+    ta.lists = lists;
+    ta.S = w.plan.S;
+    ta.lbf16 = lbf;
+    ta.cand_ids_out = cand_ids;
+    ta.cand_logit_out = cand_logit;
+  }
+  dartree::TreePlan tp = dartree::tree_plan(ta);
+  if (!(tp.ok && tp.mode == 3)) {
+    ta.lists = nullptr;
+    ta.S = 0;
+  }
   TRY(check_tree_plan(ta, &tp));
   // launch 1: the logits scan, with the head projection tiles riding along
   dartree::ScanArgs sa{};
@@ -363,7 +376,7 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
   sa.rows = rows;
   sa.V = dims->V;
   sa.K = dims->K;
-  sa.lists = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + w.lists_off);
+  sa.lists = lists;
   sa.cand_ids = cand_ids;
   sa.cand_logit = cand_logit;
   const bool fuse_head = dims->D > 0 && dartree::head_mfma_ok(wbf, H_or_h, head->Pt, dims->D, dims->r);
@@ -385,8 +398,10 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
   e = dartree::launch_scan(w.plan, lbf, sa, s);
   if (e != hipSuccess) return hip_fail(e, "scan launch");
   stage_mark(1, s);
-  e = dartree::launch_merge(w.plan, rows, dims->K, lbf, sa.lists, cand_ids, cand_logit, s);
-  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  if (!ta.lists) {
+    e = dartree::launch_merge(w.plan, rows, dims->K, lbf, sa.lists, cand_ids, cand_logit, s);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
   stage_mark(2, s);
   // launch 2: expansion, selection, emission and mask, one workgroup per request
   e = dartree::launch_tree(tp, ta, s);

@@ -107,6 +107,10 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
   }
 }
 
+// x[63 - lane]: a row mirror (lane ^ 15) followed by the exchanges of 16-lane
+// rows and 32-lane halves.
+__device__ __forceinline__ uint32_t lane_rev(uint32_t v) { return lane_xor<32>(lane_xor<16>(dpp<kDppMirror>(v))); }
+
 // One compare-exchange stage of a bitonic network over 64-bit keys (hi, lo)
 // held one per lane; after the stage (K, J) every block of K lanes is
 // ordered descending where lane & K == 0 and ascending elsewhere. Written

@@ -44,6 +44,14 @@ struct TreeArgs {
   const void* U;
   const int32_t* cand_ids;    // [n][L][K]
   const float* cand_logit;    // [n][L][K]
+  // when set (block-decoding kernel only): the scan's S sorted slice lists
+  // [n][L][S][K] of 64-bit keys; the kernel merges them into the candidates
+  // and writes cand_ids / cand_logit itself
+  const uint64_t* lists;
+  int32_t* cand_ids_out;      // written with the merged candidates
+  float* cand_logit_out;
+  int S;
+  bool lbf16;                 // logits were bf16 (key width of the lists)
   const float* h;             // [n][L][r]
   int32_t* st_tok;            // [n][L][W]
   int32_t* st_parent;         // [n][L][W]

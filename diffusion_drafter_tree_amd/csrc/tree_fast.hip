@@ -43,6 +43,7 @@ constexpr int ASTR = RT + 4;       // A*S row stride (floats)
 constexpr int kWMax = 16;
 constexpr int kSkCap = 1024;       // survivor keys (>= 16 parents x 64 candidates)
 constexpr size_t kMaxSmem = 160 * 1024;
+constexpr int kMaxMergeS = 8;     // slice lists merged in the prologue
 
 // Fixed LDS region (compile-time offsets, in bytes).
 template <int KC>
@@ -258,44 +259,7 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   const float* clog_g = a.cand_logit + (size_t)q * L * KC;
   const bool expand = a.d0 <= a.d1;
 
-  // ---- prologue ------------------------------------------------------------
-  if (tid < 16) s.misc[tid] = 0;
-  if (tid < 32) s.lv_cnt[tid] = tid < L ? min(max(a.st_count[(size_t)q * L + tid], 0), W) : 0;
-  for (int i = tid; i < L * W; i += kT) {
-    const int d = i / W + 1;
-    const bool here = expand && d >= a.d0 && d <= a.d1;
-    if (!here && (a.do_select || (expand && d == a.d0 - 1))) {
-      s.lv_tok[i] = a.st_tok[lw + i];
-      s.lv_ps[i] = d == 1 ? 0 : a.st_parent[lw + i];
-      s.lv_sb[i] = a.st_sbeta[lw + i];
-      s.lv_cum[i] = a.st_cum[lw + i];
-    }
-  }
-  int Wp = 1;
-  if (expand) {
-    for (int i = tid; i < L * KC; i += kT) {
-      const int c = cid_g[i];
-      s.cid[i] = (c < 0 || c >= a.V) ? 0 : c;
-      s.clog[i] = clog_g[i];
-    }
-    if (a.d0 > 1) Wp = min(max(a.st_count[(size_t)q * L + a.d0 - 2], 1), W);
-    const float* st = a.st_state + (size_t)q * W * RT;
-    for (int i = tid; i < 16 * RT / 4; i += kT) {
-      const int p = i / (RT / 4), j0 = (i % (RT / 4)) * 4;
-      float v[4] = {0.f, 0.f, 0.f, 0.f};
-      if (a.d0 == 1 && p == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = hq[j0 + e];
-      } else if (a.d0 > 1 && p < Wp) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = st[p * RT + j0 + e];
-      }
-      split_store4(s, p, j0, v);
-    }
-  }
-  __syncthreads();
-
-  // ---- register-resident operands and the prefetch ---------------------------
+  // ---- wave roles ------------------------------------------------------------
   // Wave w works on half hk = w / 8 of the state (k-steps 4hk..4hk+3, each 32
   // wide) and, within it, on rows 32a..32a+31 of A*S (a = w % 8, two 16-row
   // tiles with A resident in registers) and on one Z tile: candidate tile
@@ -310,6 +274,116 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   const int z_kq = hk * (C::KQ / 2) + z_kg;               // global k-group of the Z partial
   const int zrot = zw ? z_kg * C::KSQ : 0;                // first local k-step of the pass
   auto kstep = [&](int i) { return hk * 4 + ((i + zrot) & 3); };
+
+  // ---- prologue ------------------------------------------------------------
+  // Global loads are issued first, in the order the work needs them: this
+  // wave's slice lists, its A fragments, the root state row.
+  uint64_t ks[kMaxMergeS];
+  const bool merge_here = expand && a.lists != nullptr;
+  if (merge_here && w < L) {
+    const uint64_t* lst = a.lists + (size_t)(q * L + w) * a.S * KC;
+#pragma unroll
+    for (int sl = 0; sl < kMaxMergeS; ++sl) ks[sl] = (sl < a.S && lane < KC) ? lst[sl * KC + lane] : 0ull;
+  }
+  u16x8_t araw[2][4];
+  if (expand) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t* arow = A + (size_t)(aw * 32 + t * 16 + (lane & 15)) * RT + sub;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) araw[t][i] = *reinterpret_cast<const u16x8_t*>(arow + kstep(i) * 32);
+    }
+  }
+  f32x4_t h0 = {0.f, 0.f, 0.f, 0.f};
+  if (expand && a.d0 == 1 && tid < RT / 4) h0 = *reinterpret_cast<const f32x4_t*>(hq + tid * 4);
+
+  if (tid < 16) s.misc[tid] = 0;
+  if (tid < 32) {
+    // counts of levels expanded by this launch are set by the depth loop
+    int c = 0;
+    if (tid < L && !(expand && tid + 1 >= a.d0 && tid + 1 <= a.d1))
+      c = min(max(a.st_count[(size_t)q * L + tid], 0), W);
+    s.lv_cnt[tid] = c;
+  }
+  for (int i = tid; i < L * W; i += kT) {
+    const int d = i / W + 1;
+    const bool here = expand && d >= a.d0 && d <= a.d1;
+    if (!here && (a.do_select || (expand && d == a.d0 - 1))) {
+      s.lv_tok[i] = a.st_tok[lw + i];
+      s.lv_ps[i] = d == 1 ? 0 : a.st_parent[lw + i];
+      s.lv_sb[i] = a.st_sbeta[lw + i];
+      s.lv_cum[i] = a.st_cum[lw + i];
+    }
+  }
+  int Wp = 1;
+  if (merge_here) {
+    // Candidates of each position: the K best of the scan's S sorted slice
+    // lists, one wave per row. The lists are merged pairwise in registers:
+    // the elementwise maximum of one descending list and the other reversed
+    // holds the K best of both as a bitonic sequence, which six half-cleaner
+    // stages sort descending. Keys are (value key << 32) | ~id, so the order
+    // is value descending, id ascending.
+    for (int row = w; row < L; row += kWaves) {
+      if (row != w) {
+        const uint64_t* lst = a.lists + (size_t)(q * L + row) * a.S * KC;
+#pragma unroll
+        for (int sl = 0; sl < kMaxMergeS; ++sl) ks[sl] = (sl < a.S && lane < KC) ? lst[sl * KC + lane] : 0ull;
+      }
+      uint32_t ah = (uint32_t)(ks[0] >> 32), al = (uint32_t)ks[0];
+#pragma unroll
+      for (int sl = 1; sl < kMaxMergeS; ++sl) {
+        if (sl < a.S) {
+          const uint32_t bh = lane_rev(ks[sl] >> 32), bl = lane_rev((uint32_t)ks[sl]);
+          const bool tb = (((uint64_t)bh << 32) | bl) > (((uint64_t)ah << 32) | al);
+          ah = tb ? bh : ah;
+          al = tb ? bl : al;
+          bitonic_stage<64, 32>(ah, al);
+          bitonic_stage<64, 16>(ah, al);
+          bitonic_stage<64, 8>(ah, al);
+          bitonic_stage<64, 4>(ah, al);
+          bitonic_stage<64, 2>(ah, al);
+          bitonic_stage<64, 1>(ah, al);
+        }
+      }
+      if (lane < KC) {
+        const bool ok = (ah | al) != 0u;
+        const int id = ok ? (int)(0xFFFFFFFFu - al) : -1;
+        const float val = ok ? (a.lbf16 ? bf16_key_to_f32(ah) : key_to_f32(ah)) : -__builtin_huge_valf();
+        s.cid[row * KC + lane] = (id < 0 || id >= a.V) ? 0 : id;
+        s.clog[row * KC + lane] = val;
+        a.cand_ids_out[(size_t)(q * L + row) * KC + lane] = id;
+        a.cand_logit_out[(size_t)(q * L + row) * KC + lane] = val;
+      }
+    }
+  } else if (expand) {
+    for (int i = tid; i < L * KC; i += kT) {
+      const int c = cid_g[i];
+      s.cid[i] = (c < 0 || c >= a.V) ? 0 : c;
+      s.clog[i] = clog_g[i];
+    }
+  }
+  if (expand) {
+    // parents of the first expanded depth: the root (state h_0) or the stored level
+    if (a.d0 > 1) Wp = min(max(a.st_count[(size_t)q * L + a.d0 - 2], 1), W);
+    const float* st = a.st_state + (size_t)q * W * RT;
+    for (int i = tid; i < 16 * RT / 4; i += kT) {
+      const int p = i / (RT / 4), j0 = (i % (RT / 4)) * 4;
+      float v[4] = {0.f, 0.f, 0.f, 0.f};
+      if (a.d0 == 1 && p == 0) {
+        v[0] = h0[0];
+        v[1] = h0[1];
+        v[2] = h0[2];
+        v[3] = h0[3];
+      } else if (a.d0 > 1 && p < Wp) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = st[p * RT + j0 + e];
+      }
+      split_store4(s, p, j0, v);
+    }
+  }
+  __syncthreads();
+
+  // ---- register-resident operands and the prefetch ---------------------------
   h16x8_t areg[2][4];   // A fragments as fp16
   u16x8_t ureg[C::KSQ];   // U fragments (bf16) of the depth being expanded, then of the next
   auto load_u = [&](u16x8_t (&dst)[C::KSQ], int d) {
@@ -340,14 +414,12 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       __builtin_amdgcn_global_load_lds(hq + (size_t)d * RT + lane * 4, s.hb + (size_t)(d & 1) * RT, 16, 0, 0);
   };
   if (expand) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint16_t* arow = A + (size_t)(aw * 32 + t * 16 + (lane & 15)) * RT + sub;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) areg[t][i] = bf16x8_to_f16(*reinterpret_cast<const u16x8_t*>(arow + kstep(i) * 32));
-    }
     load_u(ureg, a.d0);
     if (a.d0 < L) load_eh(a.d0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) areg[t][i] = bf16x8_to_f16(araw[t][i]);
     vmcnt_zero();
   }
   lds_sync();
@@ -715,7 +787,7 @@ TreePlan tree_fast_plan(const TreeArgs& a) {
   const bool al = ((((uintptr_t)a.A) | ((uintptr_t)a.E) | ((uintptr_t)a.U) | ((uintptr_t)a.h) |
                     ((uintptr_t)a.st_state)) & 15u) == 0;
   if (!a.bf16 || a.r != RT || !(a.K == 16 || a.K == 32 || a.K == 64) || a.W > kWMax || a.W < 1 || a.V < a.K ||
-      a.L > 31 || a.B > 1024 || !al)
+      a.L > 31 || a.B > 1024 || !al || (a.lists && a.S > kMaxMergeS))
     return p;
   p.mode = 3;
   p.kq = 16 / (a.K / 16) > 8 ? 8 : 16 / (a.K / 16);
