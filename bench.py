@@ -143,7 +143,7 @@ def main():
 
     # ---- per-stage kernel durations, live, with HIP events on the launch stream --
     # The library records four events around the launches of each round
-    # (scan with head tiles | candidate merge | tree kernel); eager rounds.
+    # (scan with head tiles | candidate merge, when separate | tree kernel); eager rounds.
     nk = min(K, 256)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nk)]
     torch.cuda.synchronize()
@@ -152,11 +152,14 @@ def main():
         ops.build_round(dims, dhead, logits[t % R], hin[t % R], rb)
     ops.set_stage_events(None)
     torch.cuda.synchronize()
-    stage_names = ["scan_kernel", "merge_kernel", "tree_kernel"]
+    info = ops.round_plan(dims)
+    # event intervals: scan (0-1), separate merge (1-2, when the plan has one), tree (2-3)
+    stages = [("scan_kernel", 0)] + ([("merge_kernel", 1)] if info["merge_separate"] else []) + [("tree_kernel", 2)]
+    stage_names = [n for n, _ in stages]
     per = {n: [] for n in stage_names}
     tot = []
     for t in range(4, nk):
-        for i, n in enumerate(stage_names):
+        for n, i in stages:
             per[n].append(ev[t][i].elapsed_time(ev[t][i + 1]) * 1000.0)
         tot.append(ev[t][0].elapsed_time(ev[t][3]) * 1000.0)
     kern_us = {n: float(np.mean(v)) for n, v in per.items()}
@@ -166,17 +169,21 @@ def main():
     lsz = 2 if cfg.logits_dtype == "bf16" else 4
     wsz = 2 if cfg.weight_dtype == "bf16" else 4
     rows = n * L
-    # slices per row of the logits scan: the workspace holds their sorted lists
-    S_sl = max(1, rb.ws_bytes // (rows * Kc * 8)) if rb.ws_bytes > 256 else 1
+    # slices per row of the logits scan, each leaving a sorted list of K keys (8 B each)
+    S_sl = info["scan_slices"]
+    lists_bytes = rows * S_sl * Kc * 8 if S_sl > 1 else 0
+    cand_bytes = rows * Kc * 8   # candidate ids + logits, written once, read by the tree kernel
     alg = {
         # a1 logits scan + a0 head projection (H, P read once; h written)
         "scan_kernel": {"bytes": rows * V * lsz + (rows * D * wsz + r * D * wsz + rows * r * 4 if D > 0 else 0)
-                        + (rows * S_sl * Kc * 8 if S_sl > 1 else rows * Kc * 8),
+                        + (lists_bytes if S_sl > 1 else cand_bytes),
                         "flops": 2 * rows * D * r},
-        "merge_kernel": {"bytes": (rows * S_sl * Kc * 8 + rows * Kc * 8) if S_sl > 1 else 0, "flops": 0},
-        # a2..a5: U rows of every candidate, E rows of the kept nodes, A, h, candidates, outputs
+        "merge_kernel": {"bytes": lists_bytes + cand_bytes, "flops": 0},
+        # a2..a5: U rows of every candidate, E rows of the kept nodes, A, h, candidates (or the
+        # slice lists it merges), the supertree levels and the outputs
         "tree_kernel": {"bytes": rows * Kc * r * wsz + n * (L - 1) * W * r * wsz + r * r * wsz + rows * r * 4
-                        + rows * Kc * 8 + n * L * W * 16 + n * B * (20 + ((B + 63) // 64) * 8),
+                        + (lists_bytes + cand_bytes if S_sl > 1 and not info["merge_separate"] else cand_bytes)
+                        + n * L * W * 16 + n * B * (20 + ((B + 63) // 64) * 8),
                         "flops": 2 * n * L * W * Kc * r + 2 * n * (L - 1) * W * r * r},
     }
     HBM_PEAK = 8000.0   # GB/s, MI355X HBM3E
@@ -225,6 +232,7 @@ def main():
         "roofline": roofline,
         "roofline_scan": roofline_scan,
         "kernels": kernels,
+        "plan": info,
         "round": round_stats,
         "us_per_round_eager": round(us_eager, 3),
         "host_seconds_timed": round(t_host, 4),

@@ -32,6 +32,11 @@ class Head(ctypes.Structure):
     _fields_ = [("A", c_void_p), ("E", c_void_p), ("U", c_void_p), ("Pt", c_void_p)]
 
 
+class RoundInfo(ctypes.Structure):
+    _fields_ = [("n_launches", c_int32), ("scan_slices", c_int32), ("scan_workgroups", c_int32),
+                ("merge_separate", c_int32), ("tree_kernel", c_int32), ("tree_lds_bytes", c_int32)]
+
+
 class Supertree(ctypes.Structure):
     _fields_ = [("tok", c_void_p), ("parent_slot", c_void_p), ("cum", c_void_p), ("sbeta", c_void_p),
                 ("count", c_void_p), ("state", c_void_p), ("next_depth", c_int32)]
@@ -47,6 +52,7 @@ SIGNATURES = {
     "dartree_last_error": (c_char_p, []),
     "dartree_version": (c_int32, []),
     "dartree_workspace_size": (c_int32, [PD, POINTER(c_size_t)]),
+    "dartree_round_plan": (c_int32, [PD, POINTER(RoundInfo)]),
     "dartree_workspace_init": (c_int32, [PD, c_void_p, c_size_t, c_void_p]),
     "dartree_head_states": (c_int32, [PD, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dartree_topk_candidates": (c_int32, [PD, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),

@@ -179,6 +179,26 @@ dartree_status check_tree_plan(const dartree::TreeArgs& a, dartree::TreePlan* p)
   return DARTREE_OK;
 }
 
+// The launches of a round: the scan, then either the block-decoding tree
+// kernel merging the scan's slice lists in its prologue, or (other plans) a
+// separate merge launch ahead of the tree kernel.
+dartree_status plan_round(const WsLayout& w, bool lbf, uint64_t* lists, int32_t* cand_ids, float* cand_logit,
+                          dartree::TreeArgs& ta, dartree::TreePlan* tp) {
+  if (w.plan.S > 1) {
+    ta.lists = lists;
+    ta.S = w.plan.S;
+    ta.lbf16 = lbf;
+    ta.cand_ids_out = cand_ids;
+    ta.cand_logit_out = cand_logit;
+  }
+  *tp = dartree::tree_plan(ta);
+  if (!(tp->ok && tp->mode == 3)) {
+    ta.lists = nullptr;
+    ta.S = 0;
+  }
+  return check_tree_plan(ta, tp);
+}
+
 }  // namespace
 
 extern "C" {
@@ -197,6 +217,31 @@ const char* dartree_status_string(dartree_status s) {
 const char* dartree_last_error(void) { return g_err; }
 
 int32_t dartree_version(void) { return 1; }
+
+dartree_status dartree_round_plan(const dartree_dims* dims, dartree_round_info* info) {
+  g_err[0] = 0;
+  TRY(check_dims(dims));
+  if (!info) return fail(DARTREE_ERR_INVALID_ARGUMENT, "info is NULL");
+  WsLayout w = ws_layout(dims);
+  if (!w.plan.ok) return fail(DARTREE_ERR_UNSUPPORTED, "no top-K plan for V=%d K=%d", dims->V, dims->K);
+  dartree_supertree st{};
+  dartree::TreeArgs ta = tree_args(dims, nullptr, nullptr, nullptr, nullptr, &st, 1, dims->L);
+  set_tree_out(ta, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, reinterpret_cast<uint64_t*>(256));
+  dartree::TreePlan tp;
+  alignas(16) static uint64_t dummy_lists[2];
+  TRY(plan_round(w, dims->logits_dtype == DARTREE_BF16, dummy_lists, nullptr, nullptr, ta, &tp));
+  const bool merge_sep = w.plan.S > 1 && ta.lists == nullptr;
+  info->scan_slices = w.plan.S;
+  info->merge_separate = merge_sep ? 1 : 0;
+  const int rows = dims->n_req * dims->L;
+  const bool head_fused = dims->D > 0 && dartree::head_mfma_ok(dims->weight_dtype == DARTREE_BF16,
+                                                               dummy_lists, dummy_lists, dims->D, dims->r);
+  info->n_launches = 2 + (merge_sep ? 1 : 0) + ((dims->D > 0 && !head_fused) ? 1 : 0);
+  info->scan_workgroups = w.plan.n_scan + (head_fused ? (dims->r / 16) * ((rows + 15) / 16) : 0);
+  info->tree_kernel = tp.mode == 3 ? 1 : 0;
+  info->tree_lds_bytes = (int32_t)tp.smem;
+  return DARTREE_OK;
+}
 
 dartree_status dartree_set_stage_events(void* const* events, int32_t n) {
   g_err[0] = 0;
@@ -355,21 +400,9 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
   const float* hin = static_cast<const float*>(H_or_h);
   dartree::TreeArgs ta = tree_args(dims, head, cand_ids, cand_logit, dims->D > 0 ? h : hin, st, 1, dims->L);
   set_tree_out(ta, n_sel, tok, depth, parent, score, slot, mask);
-  // the block-decoding tree kernel merges the scan's slice lists itself
   uint64_t* lists = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + w.lists_off);
-  if (w.plan.S > 1) {
-    ta.lists = lists;
-    ta.S = w.plan.S;
-    ta.lbf16 = lbf;
-    ta.cand_ids_out = cand_ids;
-    ta.cand_logit_out = cand_logit;
-  }
-  dartree::TreePlan tp = dartree::tree_plan(ta);
-  if (!(tp.ok && tp.mode == 3)) {
-    ta.lists = nullptr;
-    ta.S = 0;
-  }
-  TRY(check_tree_plan(ta, &tp));
+  dartree::TreePlan tp;
+  TRY(plan_round(w, lbf, lists, cand_ids, cand_logit, ta, &tp));
   // launch 1: the logits scan, with the head projection tiles riding along
   dartree::ScanArgs sa{};
   sa.logits = logits;

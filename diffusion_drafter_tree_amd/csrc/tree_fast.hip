@@ -61,12 +61,12 @@ struct FX {
   static constexpr size_t sk_bytes = 8 * (kSkCap + 4);
   static constexpr size_t o_sk = o_zp;                // survivors reuse the Z partials (P3 vs P1/P2)
   static constexpr size_t o_as = o_zp + (zp_bytes > sk_bytes ? zp_bytes : sk_bytes);
-  static constexpr size_t o_ec = o_as + 2 * 4 * 16 * ASTR;  // [2][KC][RT], written by direct loads
-  static constexpr size_t o_hb = o_ec + 2 * 2 * KC * RT;      // [2][RT]
-  static constexpr size_t o_ck = o_hb + 2 * 4 * RT;
+  static constexpr size_t o_ec = o_as + 2 * 4 * 16 * ASTR;  // [KC][RT]
+  static constexpr size_t o_hb = o_ec + 2 * KC * RT;          // [RT]
+  static constexpr size_t o_ck = o_hb + 4 * RT;
   static constexpr size_t o_win = o_ck + 4 * 16 * KC;
   static constexpr size_t o_misc = o_win + 8 * 16;
-  static constexpr size_t fixed = o_misc + 4 * 16;
+  static constexpr size_t fixed = o_misc + 4 * 32;
 };
 
 // Variable LDS region (depends on L, W, B).
@@ -118,12 +118,12 @@ struct FLay {
   LDS uint16_t* Sl;    // [16][SSTR] fp16 low part (the rest of the fp32 value)
   LDS float* Zp;       // [KQ][16][ZSTR]
   LDS float* AS;       // [2][16][ASTR] A*S over the two halves of the state
-  LDS uint16_t* EC;    // [2][KC][RT] E rows of a depth's candidates (by depth parity)
-  LDS float* hb;       // [2][RT] h row of a depth (by depth parity)
+  LDS uint16_t* EC;    // [KC][RT] E rows of the depth's candidates
+  LDS float* hb;       // [RT] h row of the depth
   LDS float* cumK;     // [16][KC]
   LDS uint64_t* sk;    // [kSkCap + 4] survivor keys
   LDS uint64_t* win;   // [16] the depth's survivors by rank
-  LDS int* misc;       // [16]
+  LDS int* misc;       // [32]: bounds and survivor counts by depth parity; 16..31 level keys
   LDS int* cid;        // [L][KC]
   LDS float* clog;     // [L][KC]
   LDS int* lv_tok;     // [L][W]
@@ -223,14 +223,24 @@ __device__ __forceinline__ float tanh_fast(float x) {
 // (parent's path rank, token) among the level's cnt nodes. One wave.
 __device__ __forceinline__ void level_lex_wave(const FLay& s, int d, int W, int cnt, const uint32_t tok,
                                                const int ps) {
+  // The level's keys (parent's lexicographic rank, token) go through LDS
+  // (one wave writes, then every lane reads all of them back); a lane's rank
+  // is the number of smaller keys. Keys are distinct: two children of one
+  // parent carry distinct tokens.
   const int lane = lane_id();
   uint32_t k2 = 0xFFFFFFFFu;
   if (lane < cnt) {
     const int lp = d == 1 ? 0 : s.lv_lex[(d - 2) * W + min(max(ps, 0), W - 1)];
     k2 = ((uint32_t)lp << 18) | (tok & 0x3FFFFu);
   }
+  LDS uint32_t* kb = reinterpret_cast<LDS uint32_t*>(s.misc + 16);
+  if (lane < 16) kb[lane] = k2;
   int rk = 0;
-  for (int c = 0; c < cnt; ++c) rk += readlane(k2, c) < k2;
+#pragma unroll
+  for (int c = 0; c < 16; c += 4) {
+    const u32x4_t kk = *reinterpret_cast<const LDS u32x4_t*>(kb + c);
+    rk += (kk.x < k2) + (kk.y < k2) + (kk.z < k2) + (kk.w < k2);
+  }
   if (lane < cnt) s.lv_lex[(d - 1) * W + lane] = rk;
 }
 
@@ -297,7 +307,7 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   f32x4_t h0 = {0.f, 0.f, 0.f, 0.f};
   if (expand && a.d0 == 1 && tid < RT / 4) h0 = *reinterpret_cast<const f32x4_t*>(hq + tid * 4);
 
-  if (tid < 16) s.misc[tid] = 0;
+  if (tid < 32) s.misc[tid] = 0;
   if (tid < 32) {
     // counts of levels expanded by this launch are set by the depth loop
     int c = 0;
@@ -384,43 +394,52 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   __syncthreads();
 
   // ---- register-resident operands and the prefetch ---------------------------
+  // Every global load of the depth loop goes to registers: the compiler then
+  // counts them in issue order and waits for exactly the ones a use needs
+  // (loads straight into LDS would make it wait for all of them at the first
+  // use of any). One share of the next depth's loads is issued per phase: a
+  // wave's vector-memory issue stalls once the loads it has in flight pile
+  // up. The U fragments (share i of KSQ) feed the next depth's Z tiles; the E
+  // rows (share i of NEV, 16 bytes a lane) and the h row (wave 0) are written
+  // into LDS one depth later, before the state update that reads them. Every
+  // depth issues all shares (past the last needed depth they reload the last
+  // one): with loads on every path the waits stay exact across the loop.
   h16x8_t areg[2][4];   // A fragments as fp16
   u16x8_t ureg[C::KSQ];   // U fragments (bf16) of the depth being expanded, then of the next
-  auto load_u = [&](u16x8_t (&dst)[C::KSQ], int d) {
+  u16x8_t ereg[C::NEV];   // E rows (bf16) staged for the next depth's state update
+  f32x4_t hreg = {0.f, 0.f, 0.f, 0.f};   // wave 0: the h row staged with them
+  auto load_u1 = [&](int d, int i) {
     if (zw) {
       const int row = s.cid[(d - 1) * KC + z_nt * 16 + (lane & 15)];
-      const uint16_t* src = U + (size_t)row * RT + sub;
-#pragma unroll
-      for (int i = 0; i < C::KSQ; ++i) dst[i] = *reinterpret_cast<const u16x8_t*>(src + kstep(i) * 32);
+      ureg[i] = *reinterpret_cast<const u16x8_t*>(U + (size_t)row * RT + sub + kstep(i) * 32);
     }
   };
-  // E rows of depth d's candidates and the h row of depth d go straight from
-  // global memory into the depth's LDS buffers (lane l of a wave writes 16
-  // bytes at the wave's base + 16 l), no registers involved. Issued one
-  // depth ahead; each wave waits for its own before the barrier that
-  // precedes the state update that reads them.
-  auto load_eh = [&](int d) {
-    LDS uint16_t* eb = s.EC + (size_t)(d & 1) * KC * RT;
+  auto load_e1 = [&](int d, int i) {
+    const int v0 = w * kWave + i * kT;   // first 16-byte vector of this wave's share
+    if (v0 < C::NEVEC) {
+      const int v = v0 + lane;
+      const int k = v / (RT / 8), c = (v % (RT / 8)) * 8;
+      ereg[i] = *reinterpret_cast<const u16x8_t*>(E + (size_t)s.cid[(d - 1) * KC + k] * RT + c);
+    }
+    if (i == 0 && w == 0) hreg = *reinterpret_cast<const f32x4_t*>(hq + (size_t)min(d, L - 1) * RT + lane * 4);
+  };
+  auto store_e = [&]() {
 #pragma unroll
     for (int i = 0; i < C::NEV; ++i) {
-      const int v0 = w * kWave + i * kT;   // first vector of this wave
-      if (v0 < C::NEVEC) {
-        const int v = v0 + lane;
-        const int k = v / (RT / 8), c = (v % (RT / 8)) * 8;
-        __builtin_amdgcn_global_load_lds(E + (size_t)s.cid[(d - 1) * KC + k] * RT + c, eb + (size_t)v0 * 8, 16, 0, 0);
-      }
+      const int v0 = w * kWave + i * kT;
+      if (v0 < C::NEVEC) *reinterpret_cast<LDS u16x8_t*>(s.EC + (size_t)(v0 + lane) * 8) = ereg[i];
     }
-    if (w == 0)
-      __builtin_amdgcn_global_load_lds(hq + (size_t)d * RT + lane * 4, s.hb + (size_t)(d & 1) * RT, 16, 0, 0);
+    if (w == 0) *reinterpret_cast<LDS f32x4_t*>(s.hb + lane * 4) = hreg;
   };
   if (expand) {
-    load_u(ureg, a.d0);
-    if (a.d0 < L) load_eh(a.d0);
+#pragma unroll
+    for (int i = 0; i < C::KSQ; ++i) load_u1(a.d0, i);
+#pragma unroll
+    for (int i = 0; i < C::NEV; ++i) load_e1(a.d0, i);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) areg[t][i] = bf16x8_to_f16(araw[t][i]);
-    vmcnt_zero();
   }
   lds_sync();
 
@@ -428,7 +447,8 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   for (int d = a.d0; d <= a.d1; ++d) {
     const bool need_state = d < L;
     const int par = d & 1;
-    // P1: the Z tiles (the critical path: nothing else is issued here)
+    // P1: the Z tiles, then the first KSQ k-steps of this wave's A*S on the
+    // same state fragments (the rest follows in P3a; the state update reads it)
     const int p16 = lane & 15;
     // Lanes of absent parents (p >= Wp) read parent 0's row: their results
     // land only in rows / columns of absent parents, which nobody reads, and
@@ -442,49 +462,60 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       dst[0] = *reinterpret_cast<const LDS h16x8_t*>(rl + o);
       dst[1] = *reinterpret_cast<const LDS h16x8_t*>(rh + o);
     };
-    if (zw) {
-      h16x8_t f[C::KSQ][2], uf[C::KSQ];
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};   // A*S, two row tiles
+    auto as_mfma = [&](auto ic, const h16x8_t (&fr)[2]) {
+      constexpr int i = decltype(ic)::value;
+      acc0 = mfma_f16(areg[0][i], fr[0], acc0);
+      acc1 = mfma_f16(areg[1][i], fr[0], acc1);
+      acc0 = mfma_f16(areg[0][i], fr[1], acc0);
+      acc1 = mfma_f16(areg[1][i], fr[1], acc1);
+    };
+    // the remaining k-steps of A*S, then A*S out to LDS
+    auto as_finish = [&]() {
+      h16x8_t f[4 - C::KSQ][2];
 #pragma unroll
-      for (int i = 0; i < C::KSQ; ++i) {
-        ld(i, f[i]);
-        uf[i] = bf16x8_to_f16(ureg[i]);
+      for (int i = C::KSQ; i < 4; ++i) ld(i, f[i - C::KSQ]);
+      as_mfma(std::integral_constant<int, C::KSQ>{}, f[0]);
+      as_mfma(std::integral_constant<int, C::KSQ + 1>{}, f[1]);
+      if constexpr (C::KSQ == 1) as_mfma(std::integral_constant<int, 3>{}, f[2]);
+      LDS float* asr = s.AS + (hk * 16 + p16) * ASTR + aw * 32 + (lane >> 4) * 4;
+      *reinterpret_cast<LDS f32x4_t*>(asr) = acc0;
+      *reinterpret_cast<LDS f32x4_t*>(asr + 16) = acc1;
+    };
+    {
+      h16x8_t f[C::KSQ][2];
+#pragma unroll
+      for (int i = 0; i < C::KSQ; ++i) ld(i, f[i]);
+      if (zw) {
+        h16x8_t uf[C::KSQ];
+#pragma unroll
+        for (int i = 0; i < C::KSQ; ++i) uf[i] = bf16x8_to_f16(ureg[i]);
+        f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < C::KSQ; ++i) {
+          zacc = mfma_f16(f[i][0], uf[i], zacc);
+          zacc = mfma_f16(f[i][1], uf[i], zacc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s.Zp[(z_kq * 16 + (lane >> 4) * 4 + i) * C::ZSTR + z_nt * 16 + (lane & 15)] = zacc[i];
       }
-      f32x4_t zacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < C::KSQ; ++i) {
-        zacc = mfma_f16(f[i][0], uf[i], zacc);
-        zacc = mfma_f16(f[i][1], uf[i], zacc);
+      __builtin_amdgcn_sched_barrier(0);   // the Z results go out before the A*S work is issued
+      if (need_state) {
+        as_mfma(std::integral_constant<int, 0>{}, f[0]);
+        if constexpr (C::KSQ > 1) as_mfma(std::integral_constant<int, 1>{}, f[C::KSQ > 1 ? 1 : 0]);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s.Zp[(z_kq * 16 + (lane >> 4) * 4 + i) * C::ZSTR + z_nt * 16 + (lane & 15)] = zacc[i];
     }
     lds_sync();
 
-    // P2: A*S of the parents (for the state update) on the matrix cores while
-    // the parents' waves do the log-softmax and keys; the bound T. For a
-    // parent's wave both run in one branch-free block whose schedule
-    // interleaves the 24 MFMAs with the vector work.
-    // the next depth's prefetch drains behind this phase's work: U fragments
-    // (the Z MFMAs of P1 were their last readers) and E/h rows
-    vmcnt_zero();   // this wave's loads of one depth ago (E/h of this depth) have landed
-    if (d < a.d1) load_u(ureg, d + 1);
-    if (d + 1 < L && d < a.d1) load_eh(d + 1);
-    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    if (need_state) {
-      h16x8_t f[2][2];
-      ld(0, f[0]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i + 1 < 4) ld(i + 1, f[(i + 1) & 1]);
-        acc0 = mfma_f16(areg[0][i], f[i & 1][0], acc0);
-        acc1 = mfma_f16(areg[1][i], f[i & 1][0], acc1);
-        acc0 = mfma_f16(areg[0][i], f[i & 1][1], acc0);
-        acc1 = mfma_f16(areg[1][i], f[i & 1][1], acc1);
-      }
-    }
+    // P2: the parents' waves do the log-softmax and keys (the slot-0 parent's
+    // wave, at raised issue priority, also the bound T: the critical path),
+    // then every other wave the rest of its A*S (the slot-0 wave does its
+    // share in P3b), then the first share of the next depth's U fragments
+    // (the Z MFMAs of P1 were the last readers of the registers).
     const float bd = a.beta * (float)d;
     uint32_t kh = 0u, kl = 0u;
+    if (w == 0) __builtin_amdgcn_s_setprio(2);
     if (w < Wp) {
       const int p = w;
       const bool v = KC == kWave ? true : lane < KC;
@@ -513,11 +544,21 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
         if (lane == 0) s.misc[par] = (int)readlane(sk32, W - 1);
       }
     }
-    if (need_state) {
-      LDS float* asr = s.AS + (hk * 16 + p16) * ASTR + aw * 32 + (lane >> 4) * 4;
-      *reinterpret_cast<LDS f32x4_t*>(asr) = acc0;
-      *reinterpret_cast<LDS f32x4_t*>(asr + 16) = acc1;
+    if (w == 0) __builtin_amdgcn_s_setprio(0);
+    // the level before this one: its path ranks, by a wave without a parent
+    // (the state update of the level, one depth ago, had no spare wave)
+    if (a.do_select && a.d0 == 1 && d >= 2 && w == kWaves - 1) {
+      uint32_t tk = 0u;
+      int ps = 0;
+      if (lane < Wp) {
+        const uint32_t lo = ~(uint32_t)s.win[lane];
+        tk = lo >> 10;
+        ps = (lo >> 6) & 15;
+      }
+      level_lex_wave(s, d - 1, W, Wp, tk, ps);
     }
+    if (need_state && w != 0) as_finish();
+    load_u1(min(d + 1, a.d1), 0);
     lds_sync();
 
     // P3: survivors (high word >= T) compacted, then ranked by counting
@@ -530,17 +571,26 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       base = __builtin_amdgcn_readfirstlane(base);
       if (sv) s.sk[base + (int)mbcnt64(bal)] = ((uint64_t)kh << 32) | kl;
     }
+    if (C::KSQ > 1) load_u1(min(d + 1, a.d1), 1);
     lds_sync();
     const int nk = min(W, Wp * KC);
     {
-      const int ns = min(s.misc[2 + par], kSkCap);
-      int G = 16;
-      while (G > 1 && ns * G > kT) G >>= 1;
-      const int per = (ns + G - 1) / G;
-      const int x = tid / G, seg = tid - x * G;
+      // G = 2^lg threads per survivor (up to 16), as many as eight waves hold:
+      // every instruction a wave executes takes its SIMD's issue cycles, so a
+      // few busy waves (two per SIMD) rank faster than all sixteen. Ranking
+      // threads start at wave 4 (wave 0 finishes its A*S meanwhile); past 768
+      // survivors they wrap around to waves 0..3.
+      const int ns = min(__builtin_amdgcn_readfirstlane(s.misc[2 + par]), kSkCap);
+      int lg = 4;
+      while (lg > 0 && (ns << lg) > 8 * kWave) --lg;
+      const int G = 1 << lg;
+      const int per = (ns + G - 1) >> lg;
+      const int rt = (tid + kT - 4 * kWave) & (kT - 1);
+      const int x = rt >> lg, seg = rt & (G - 1);
       uint64_t kx = 0ull;
       uint32_t cnt = 0u;
-      if (x < ns) {
+      const bool wave_ranks = (rt & ~(kWave - 1)) < (ns << lg);   // other waves hold no survivor's group
+      if (wave_ranks && x < ns) {
         kx = s.sk[x];
         const int y0 = seg * per, y1 = min(ns, y0 + per);
         for (int y = y0; y < y1; y += 4) {
@@ -551,7 +601,7 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
           for (int e = 0; e < 4; ++e) cnt += (y + e < y1 && k4[e] > kx) ? 1u : 0u;
         }
       }
-      const int rk = (int)group_sum(cnt, G);
+      const int rk = wave_ranks ? (int)group_sum(cnt, G) : W;
       if (x < ns && seg == 0 && rk < W) {
         const uint32_t lo = ~(uint32_t)kx;
         const int k = lo & 63, p = (lo >> 6) & 15;
@@ -567,6 +617,10 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       // the other parity's bound and count are free again (read one depth ago)
       if (tid < 2) s.misc[(par ^ 1) + 2 * tid] = 0;
     }
+    if (need_state && w == 0) as_finish();
+    // this depth's staged E/h rows into LDS, then the next depth's first E share
+    store_e();
+    load_e1(min(d + 1, L), 0);
     lds_sync();
 
     // P4: states of the survivors, one wave each; path ranks of the level
@@ -577,8 +631,8 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       const f32x4_t a0 = *reinterpret_cast<const LDS f32x4_t*>(s.AS + p * ASTR + j0);
       const f32x4_t a1 = *reinterpret_cast<const LDS f32x4_t*>(s.AS + (16 + p) * ASTR + j0);
       const f32x4_t as4 = a0 + a1;
-      const u32x2_t e2 = *reinterpret_cast<const LDS u32x2_t*>(s.EC + ((size_t)par * KC + k) * RT + j0);
-      const f32x4_t h4 = *reinterpret_cast<const LDS f32x4_t*>(s.hb + par * RT + j0);
+      const u32x2_t e2 = *reinterpret_cast<const LDS u32x2_t*>(s.EC + (size_t)k * RT + j0);
+      const f32x4_t h4 = *reinterpret_cast<const LDS f32x4_t*>(s.hb + j0);
       const float ev[4] = {bf16_to_f32(e2.x & 0xFFFFu), bf16_to_f32(e2.x >> 16), bf16_to_f32(e2.y & 0xFFFFu),
                            bf16_to_f32(e2.y >> 16)};
       float v[4];
@@ -588,7 +642,9 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       if (d == a.d1)
         *reinterpret_cast<f32x4_t*>(a.st_state + ((size_t)q * W + w) * RT + j0) = f32x4_t{v[0], v[1], v[2], v[3]};
     }
-    if (a.do_select && a.d0 == 1 && w == kWaves - 1) {
+#pragma unroll
+    for (int i = 1; i < C::NEV; ++i) load_e1(min(d + 1, L), i);
+    if (a.do_select && a.d0 == 1 && d == a.d1 && w == kWaves - 1) {
       uint32_t tk = 0u;
       int ps = 0;
       if (lane < nk) {
@@ -601,6 +657,7 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
     Wp = nk;
     lds_sync();
   }
+  vmcnt_zero();   // the last depth's loads for a following one (unused) land before LDS is reused
   __syncthreads();
 
   // ---- the expanded levels to global memory ---------------------------------------

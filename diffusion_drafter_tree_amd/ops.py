@@ -71,6 +71,14 @@ def workspace_size(dims: C.Dims) -> int:
     return int(n.value)
 
 
+def round_plan(dims: C.Dims) -> dict:
+    """How build_round runs for these sizes (launch count, scan slices and
+    workgroups, where the slice lists are merged, which tree kernel, its LDS)."""
+    info = C.RoundInfo()
+    _check(C.load().dartree_round_plan(ctypes.byref(dims), ctypes.byref(info)), "round_plan")
+    return {f: int(getattr(info, f)) for f, _ in C.RoundInfo._fields_}
+
+
 class RoundBuffers:
     """Every device output of a round for one config, plus the workspace."""
 

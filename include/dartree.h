@@ -195,6 +195,23 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
                                    int32_t* parent, float* score, int32_t* slot, uint64_t* mask, void* ws,
                                    size_t ws_bytes, void* stream);
 
+/* How dartree_build_round runs for these sizes; a host-only query (no device
+ * work, no allocation), valid whenever dartree_workspace_size succeeds.
+ *   n_launches      kernel launches per round (2: scan, tree; 3 with a separate
+ *                   merge of the scan's slice lists or a separate head projection)
+ *   scan_slices     vocabulary slices per logits row (1 = one workgroup per row)
+ *   scan_workgroups workgroups of the scan launch, head projection tiles included
+ *   merge_separate  1 when the slice lists are merged by their own launch,
+ *                   0 when the tree kernel merges them (or there is one slice)
+ *   tree_kernel     1 = block-decoding kernel (K <= 64, W <= 16, r = 256, bf16
+ *                   weights), 0 = general kernel
+ *   tree_lds_bytes  dynamic LDS of the tree launch
+ * Errors: INVALID_ARGUMENT (bad dims or NULL info), UNSUPPORTED (no plan). */
+typedef struct {
+  int32_t n_launches, scan_slices, scan_workgroups, merge_separate, tree_kernel, tree_lds_bytes;
+} dartree_round_info;
+dartree_status dartree_round_plan(const dartree_dims* dims, dartree_round_info* info);
+
 /* Profiling hook (not part of a round's computation). When set, every
  * following dartree_build_round on this thread records events[0] before its
  * first launch, events[1] after the logits scan (with the head tiles),

@@ -152,3 +152,23 @@ def test_stage_event_hook_validates_on_host(lib):
     assert lib.dartree_set_stage_events(arr, 4) == C.ERR_INVALID_ARGUMENT
     assert "NULL" in C.last_error()
     assert lib.dartree_set_stage_events(arr, 3) == C.ERR_INVALID_ARGUMENT
+
+
+def test_round_plan_query(lib):
+    from diffusion_drafter_tree_amd import ops
+    info = ops.round_plan(ops.make_dims(I.CONFIGS["qwen3_4b"]))
+    # bf16 weights, K=64, W=12, r=256: the block-decoding kernel merges the slice lists itself
+    assert info["tree_kernel"] == 1 and info["merge_separate"] == 0 and info["n_launches"] == 2
+    assert info["scan_slices"] > 1
+    assert info["scan_workgroups"] == 16 * info["scan_slices"] + (256 // 16) * 1
+    assert 0 < info["tree_lds_bytes"] <= 160 * 1024
+    # r=512 and K=512: the general tree kernel, with the merge as its own launch
+    big = ops.round_plan(ops.make_dims(I.CONFIGS["stress_64req"]))
+    assert big["tree_kernel"] == 0 and big["merge_separate"] == (1 if big["scan_slices"] > 1 else 0)
+    assert big["n_launches"] == 2 + big["merge_separate"]
+    tiny = ops.round_plan(ops.make_dims(I.CONFIGS["tiny"]))
+    assert tiny["scan_slices"] == 1 and tiny["merge_separate"] == 0 and tiny["n_launches"] == 2
+    assert lib.dartree_round_plan(ctypes.byref(ops.make_dims(I.CONFIGS["tiny"])), None) == C.ERR_INVALID_ARGUMENT
+    d = ops.make_dims(I.CONFIGS["tiny"])
+    d.beta = 0.5
+    assert lib.dartree_round_plan(ctypes.byref(d), ctypes.byref(C.RoundInfo())) == C.ERR_INVALID_ARGUMENT
