@@ -173,10 +173,12 @@ def main():
     S_sl = info["scan_slices"]
     lists_bytes = rows * S_sl * Kc * 8 if S_sl > 1 else 0
     cand_bytes = rows * Kc * 8   # candidate ids + logits, written once, read by the tree kernel
+    # the scan launch stages A (bf16 in) as fp16 MFMA fragments (out) for the block-decoding kernel
+    a_stage = 2 * r * r * 2 if (info["tree_kernel"] and cfg.weight_dtype == "bf16" and r == 256) else 0
     alg = {
         # a1 logits scan + a0 head projection (H, P read once; h written)
         "scan_kernel": {"bytes": rows * V * lsz + (rows * D * wsz + r * D * wsz + rows * r * 4 if D > 0 else 0)
-                        + (lists_bytes if S_sl > 1 else cand_bytes),
+                        + (lists_bytes if S_sl > 1 else cand_bytes) + a_stage,
                         "flops": 2 * rows * D * r},
         "merge_kernel": {"bytes": lists_bytes + cand_bytes, "flops": 0},
         # a2..a5: U rows of every candidate, E rows of the kept nodes, A, h, candidates (or the

@@ -68,7 +68,7 @@ dartree_status check_dims(const dartree_dims* d) {
 
 struct WsLayout {
   dartree::ScanPlan plan;
-  size_t lists_off, total;
+  size_t lists_off, afrag_off, total;   // afrag_off = 0: no A fragment copy
 };
 
 WsLayout ws_layout(const dartree_dims* d) {
@@ -76,7 +76,14 @@ WsLayout ws_layout(const dartree_dims* d) {
   const int rows = d->n_req * d->L;
   w.plan = dartree::scan_plan(rows, d->V, d->K, d->logits_dtype == DARTREE_BF16);
   w.lists_off = 0;
-  w.total = w.plan.list_bytes;
+  w.total = (w.plan.list_bytes + 255) & ~(size_t)255;
+  // bf16 weights of rank 256: room for the fp16 A fragments the scan launch
+  // stages for the block-decoding tree kernel
+  if (d->weight_dtype == DARTREE_BF16 && d->r == 256) {
+    if (w.total == 0) w.total = 256;
+    w.afrag_off = w.total;
+    w.total += dartree::kAFragBytes;
+  }
   if (w.total == 0) w.total = 256;
   return w;
 }
@@ -237,7 +244,8 @@ dartree_status dartree_round_plan(const dartree_dims* dims, dartree_round_info* 
   const bool head_fused = dims->D > 0 && dartree::head_mfma_ok(dims->weight_dtype == DARTREE_BF16,
                                                                dummy_lists, dummy_lists, dims->D, dims->r);
   info->n_launches = 2 + (merge_sep ? 1 : 0) + ((dims->D > 0 && !head_fused) ? 1 : 0);
-  info->scan_workgroups = w.plan.n_scan + (head_fused ? (dims->r / 16) * ((rows + 15) / 16) : 0);
+  info->scan_workgroups = w.plan.n_scan + (head_fused ? (dims->r / 16) * ((rows + 15) / 16) : 0) +
+                          ((tp.mode == 3 && w.afrag_off) ? dartree::kAFragWaves : 0);
   info->tree_kernel = tp.mode == 3 ? 1 : 0;
   info->tree_lds_bytes = (int32_t)tp.smem;
   return DARTREE_OK;
@@ -403,6 +411,9 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
   uint64_t* lists = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + w.lists_off);
   dartree::TreePlan tp;
   TRY(plan_round(w, lbf, lists, cand_ids, cand_logit, ta, &tp));
+  uint16_t* a_frag = (tp.mode == 3 && w.afrag_off) ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + w.afrag_off)
+                                                   : nullptr;
+  ta.a_frag = a_frag;
   // launch 1: the logits scan, with the head projection tiles riding along
   dartree::ScanArgs sa{};
   sa.logits = logits;
@@ -410,6 +421,11 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
   sa.V = dims->V;
   sa.K = dims->K;
   sa.lists = lists;
+  if (a_frag) {
+    sa.A = static_cast<const uint16_t*>(head->A);
+    sa.a_frag = a_frag;
+    sa.n_afrag = dartree::kAFragWaves;
+  }
   sa.cand_ids = cand_ids;
   sa.cand_logit = cand_logit;
   const bool fuse_head = dims->D > 0 && dartree::head_mfma_ok(wbf, H_or_h, head->Pt, dims->D, dims->r);

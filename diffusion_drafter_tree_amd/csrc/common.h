@@ -241,6 +241,25 @@ __device__ __forceinline__ uint32_t wave_mth_largest(uint32_t v, bool valid, int
   return t;
 }
 
+// two fp32 values to fp16, rounding toward zero (v_cvt_pkrtz_f16_f32)
+__device__ __forceinline__ h16x2_t pkrtz(float a, float b) {
+  typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(h16x2_t, (fp16x2_t)__builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// 8 bf16 weights as fp16 (exact for every bf16 value of magnitude >= 2^-17
+// or zero; smaller ones are truncated by at most 2^-25)
+__device__ __forceinline__ h16x8_t bf16x8_to_f16(u16x8_t x) {
+  h16x8_t r;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const h16x2_t p = pkrtz(bf16_to_f32(x[i]), bf16_to_f32(x[i + 1]));
+    r[i] = p.x;
+    r[i + 1] = p.y;
+  }
+  return r;
+}
+
 // Workgroup barrier for LDS traffic only: this wave's LDS operations are
 // complete when it arrives, its outstanding global loads (also those that
 // write LDS directly) are not waited for. A wave that needs its direct-to-LDS

@@ -19,7 +19,15 @@ struct ScanArgs {
   const uint16_t* Pt;   // [r][D]
   float* h;             // [M][r]
   int M, D, r, n_head;
+  // staging of A (bf16 [256][256]) as fp16 MFMA fragments for the
+  // block-decoding tree kernel: n_afrag = 16 workgroups (one per tree wave)
+  // write a_frag[wave][tile][k-step][lane][8], 0 for none
+  const uint16_t* A;
+  uint16_t* a_frag;
+  int n_afrag;
 };
+constexpr int kAFragWaves = 16;                        // tree waves holding A fragments
+constexpr size_t kAFragBytes = (size_t)256 * 256 * 2;  // one fp16 copy of A
 struct ScanPlan {
   int S, slice, nv, n_scan, merge_ept;
   size_t list_bytes;
@@ -48,6 +56,9 @@ struct TreeArgs {
   // [n][L][S][K] of 64-bit keys; the kernel merges them into the candidates
   // and writes cand_ids / cand_logit itself
   const uint64_t* lists;
+  // when set (block-decoding kernel only): A as fp16 fragments staged by the
+  // scan launch (layout of ScanArgs::a_frag); otherwise loaded from A
+  const uint16_t* a_frag;
   int32_t* cand_ids_out;      // written with the merged candidates
   float* cand_logit_out;
   int S;

@@ -369,6 +369,20 @@ __device__ void head_block(const ScanArgs& a, HeadSmem& sm, int tile) {
   }
 }
 
+// One tree wave's A fragments as fp16: for tile t (16 rows) and local
+// k-step kl of its half of the state, lane l holds row 32 aw + 16 t + (l & 15),
+// columns 32 (4 hk + kl) + 8 (l >> 4) .. + 7; stored contiguously per
+// (wave, tile, k-step) so the tree kernel reads 1 KB runs.
+__device__ void afrag_block(const ScanArgs& a, int tw) {
+  const int hk = tw >> 3, aw = tw & 7;
+  for (int v = threadIdx.x; v < 2 * 4 * kWave; v += kT) {
+    const int t = v >> 8, kl = (v >> 6) & 3, l = v & 63;
+    const int row = aw * 32 + t * 16 + (l & 15), col = (hk * 4 + kl) * 32 + (l >> 4) * 8;
+    const u16x8_t x = *reinterpret_cast<const u16x8_t*>(a.A + (size_t)row * 256 + col);
+    *reinterpret_cast<h16x8_t*>(a.a_frag + ((size_t)((tw * 2 + t) * 4 + kl) * kWave + l) * 8) = bf16x8_to_f16(x);
+  }
+}
+
 template <bool BF16, int NV>
 __global__ __launch_bounds__(kT) void scan_kernel(ScanArgs a) {
   __shared__ KernelSmem smem;
@@ -377,8 +391,10 @@ __global__ __launch_bounds__(kT) void scan_kernel(ScanArgs a) {
     if (threadIdx.x < 8) smem.scan.misc[threadIdx.x] = 0;
     __syncthreads();
     scan_block<BF16, NV>(a, smem.scan, b);
-  } else {
+  } else if (b < a.n_scan + a.n_head) {
     head_block(a, smem.head, b - a.n_scan);
+  } else {
+    afrag_block(a, b - a.n_scan - a.n_head);
   }
 }
 
@@ -464,7 +480,7 @@ hipError_t launch_scan(const ScanPlan& p, bool bf16, const ScanArgs& args_in, hi
   a.S = p.S;
   a.slice = p.slice;
   a.n_scan = p.n_scan;
-  const int grid = a.n_scan + a.n_head;
+  const int grid = a.n_scan + a.n_head + a.n_afrag;
   if (grid == 0) return hipSuccess;
 #define DT_SCAN(B, NVV) hipLaunchKernelGGL((scan_kernel<B, NVV>), dim3(grid), dim3(kT), 0, s, a)
   switch (p.nv) {

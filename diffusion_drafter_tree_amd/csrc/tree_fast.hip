@@ -177,11 +177,6 @@ __device__ __forceinline__ FLay make_flay(const VOff& o) {
   return s;
 }
 
-// two fp32 values to fp16, rounding toward zero (v_cvt_pkrtz_f16_f32)
-__device__ __forceinline__ h16x2_t pkrtz(float a, float b) {
-  typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(h16x2_t, (fp16x2_t)__builtin_amdgcn_cvt_pkrtz(a, b));
-}
 
 // Two fp16 parts of 4 consecutive fp32 state values (8 bytes per plane):
 // hi = the value truncated to fp16, lo = the remainder (exact in fp32)
@@ -199,18 +194,6 @@ __device__ __forceinline__ void split_store4(const FLay& s, int row, int j0, con
       u32x2_t{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
 }
 
-// 8 bf16 weights as fp16 (exact for every bf16 value of magnitude >= 2^-17
-// or zero; smaller ones are truncated by at most 2^-25)
-__device__ __forceinline__ h16x8_t bf16x8_to_f16(u16x8_t x) {
-  h16x8_t r;
-#pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    const h16x2_t p = pkrtz(bf16_to_f32(x[i]), bf16_to_f32(x[i + 1]));
-    r[i] = p.x;
-    r[i + 1] = p.y;
-  }
-  return r;
-}
 
 // tanh(x) = 1 - 2 / (2^(2 x log2 e) + 1) on the hardware exp2 and reciprocal
 // (each within about 1 ulp): absolute error a few 1e-7, saturating to +-1.
@@ -295,8 +278,17 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
 #pragma unroll
     for (int sl = 0; sl < kMaxMergeS; ++sl) ks[sl] = (sl < a.S && lane < KC) ? lst[sl * KC + lane] : 0ull;
   }
+  // A fragments: 1 KB contiguous runs of the fp16 copy the scan launch
+  // staged, or (without it) 16 rows x 16 bytes of A per load, converted below
   u16x8_t araw[2][4];
-  if (expand) {
+  if (expand && a.a_frag) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        araw[t][i] = *reinterpret_cast<const u16x8_t*>(
+            a.a_frag + ((size_t)((w * 2 + t) * 4 + ((i + zrot) & 3)) * kWave + lane) * 8);
+  } else if (expand) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const uint16_t* arow = A + (size_t)(aw * 32 + t * 16 + (lane & 15)) * RT + sub;
@@ -436,10 +428,17 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
     for (int i = 0; i < C::KSQ; ++i) load_u1(a.d0, i);
 #pragma unroll
     for (int i = 0; i < C::NEV; ++i) load_e1(a.d0, i);
+    if (a.a_frag) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) areg[t][i] = bf16x8_to_f16(araw[t][i]);
+        for (int i = 0; i < 4; ++i) areg[t][i] = __builtin_bit_cast(h16x8_t, araw[t][i]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) areg[t][i] = bf16x8_to_f16(araw[t][i]);
+    }
   }
   lds_sync();
 
@@ -739,30 +738,27 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   }
   lds_sync();
   // emitted index: selected nodes of earlier levels, then selected nodes of
-  // the level with a smaller path rank (breadth-first order = path order)
-  uint32_t lvm[32];
+  // the level with a smaller path rank (breadth-first order = path order).
+  // One wave counts the selected nodes of the levels before each level
+  // (lane d: levels 0..d-1; lane 32: all of them).
+  if (w == 0) {
+    int acc = 0;
 #pragma unroll
-  for (int i = 0; i < 32; i += 4) {
-    const u32x4_t v4 = *reinterpret_cast<const LDS u32x4_t*>(s.nd + i);
-    lvm[i] = v4.x;
-    lvm[i + 1] = v4.y;
-    lvm[i + 2] = v4.z;
-    lvm[i + 3] = v4.w;
+    for (int i = 0; i < 32; i += 4) {
+      const u32x4_t v4 = *reinterpret_cast<const LDS u32x4_t*>(s.nd + i);
+      acc += (i < lane ? __popc(v4.x) : 0) + (i + 1 < lane ? __popc(v4.y) : 0) + (i + 2 < lane ? __popc(v4.z) : 0) +
+             (i + 3 < lane ? __popc(v4.w) : 0);
+    }
+    if (lane <= 32) s.base[lane] = acc;
   }
-  int n = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) n += __popc(lvm[i]);
+  lds_sync();
+  const int n = s.base[32];
   for (int i = tid; i < N; i += kT) {
     const int d = i / W + 1;
     const uint32_t m = s.nd[d - 1];
     const int lx = s.lv_lex[i];
     int e = -1;
-    if (i - (d - 1) * W < s.lv_cnt[d - 1] && ((m >> lx) & 1u)) {
-      int base = 0;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) base += j < d - 1 ? __popc(lvm[j]) : 0;
-      e = base + __popc(m & ((1u << lx) - 1u));
-    }
+    if (i - (d - 1) * W < s.lv_cnt[d - 1] && ((m >> lx) & 1u)) e = s.base[d - 1] + __popc(m & ((1u << lx) - 1u));
     s.eix[i] = e;
   }
   lds_sync();

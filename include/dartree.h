@@ -200,7 +200,9 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
  *   n_launches      kernel launches per round (2: scan, tree; 3 with a separate
  *                   merge of the scan's slice lists or a separate head projection)
  *   scan_slices     vocabulary slices per logits row (1 = one workgroup per row)
- *   scan_workgroups workgroups of the scan launch, head projection tiles included
+ *   scan_workgroups workgroups of the scan launch, head projection tiles and
+ *                   (with the block-decoding tree kernel) the 16 that stage A
+ *                   as fp16 MFMA fragments in the workspace included
  *   merge_separate  1 when the slice lists are merged by their own launch,
  *                   0 when the tree kernel merges them (or there is one slice)
  *   tree_kernel     1 = block-decoding kernel (K <= 64, W <= 16, r = 256, bf16

@@ -58,11 +58,16 @@ def test_workspace_size_values(lib):
     st, n = ws_size(lib, dims())
     assert st == C.OK
     # a 151936-entry bf16 row spans 4 slices of <= 1024 threads x 5 vectors x 8
-    # values: 16 rows x 4 sorted lists x 64 keys of 8 bytes
-    assert n == 16 * 4 * 64 * 8
+    # values: 16 rows x 4 sorted lists x 64 keys of 8 bytes, then an fp16 copy
+    # of A (256 x 256) for bf16 weights of rank 256
+    afrag = 256 * 256 * 2
+    assert n == 16 * 4 * 64 * 8 + afrag
     # fp32 rows of that length take 8 slices (4 values per vector)
     st, n = ws_size(lib, dims(logits_dtype=C.F32))
-    assert st == C.OK and n == 16 * 8 * 64 * 8
+    assert st == C.OK and n == 16 * 8 * 64 * 8 + afrag
+    # fp32 weights: no A copy
+    st, n = ws_size(lib, dims(weight_dtype=C.F32))
+    assert st == C.OK and n == 16 * 4 * 64 * 8
     st, n = ws_size(lib, dims(V=1024, L=6, K=8, W=3, B=16, r=16, D=0, logits_dtype=C.F32, weight_dtype=C.F32))
     assert st == C.OK and n >= 6 * 4
 
@@ -160,7 +165,8 @@ def test_round_plan_query(lib):
     # bf16 weights, K=64, W=12, r=256: the block-decoding kernel merges the slice lists itself
     assert info["tree_kernel"] == 1 and info["merge_separate"] == 0 and info["n_launches"] == 2
     assert info["scan_slices"] > 1
-    assert info["scan_workgroups"] == 16 * info["scan_slices"] + (256 // 16) * 1
+    # 16 rows x slices, 16 head projection tiles, 16 workgroups staging A fragments
+    assert info["scan_workgroups"] == 16 * info["scan_slices"] + (256 // 16) * 1 + 16
     assert 0 < info["tree_lds_bytes"] <= 160 * 1024
     # r=512 and K=512: the general tree kernel, with the merge as its own launch
     big = ops.round_plan(ops.make_dims(I.CONFIGS["stress_64req"]))
