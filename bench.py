@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="if > 0: run only this many eager rounds (for rocprofv3) and exit")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="if > 0: one plain device copy of this many MiB first (calibrates rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE against a known byte count)")
     return ap.parse_args()
 
 
@@ -65,6 +68,14 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] inputs ready: {R} rounds ({R * logits[0].numel() * logits[0].element_size() / 1e6:.0f} MB of "
           f"logits) in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    if args.copy_mb > 0:
+        src = torch.ones(args.copy_mb << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy: {args.copy_mb} MiB read, {args.copy_mb} MiB written", file=sys.stderr,
+              flush=True)
+        del src, dst
     rb = ops.RoundBuffers(cfg)
     dims = rb.dims
     stream = torch.cuda.current_stream()
@@ -144,11 +155,14 @@ def main():
     # ---- per-stage kernel durations, live, with HIP events on the launch stream --
     # The library records four events around the launches of each round
     # (scan with head tiles | candidate merge, when separate | tree kernel); eager rounds.
+    # Events are created with hipEventDisableSystemFence (timing only: no
+    # system-scope cache writeback and invalidation when they complete, which
+    # would otherwise sit between the kernels they bracket).
     nk = min(K, 256)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nk)]
+    hev = StageEvents(nk * 4)
     torch.cuda.synchronize()
     for t in range(nk):
-        ops.set_stage_events(ev[t])
+        hev.set(t)
         ops.build_round(dims, dhead, logits[t % R], hin[t % R], rb)
     ops.set_stage_events(None)
     torch.cuda.synchronize()
@@ -160,8 +174,10 @@ def main():
     tot = []
     for t in range(4, nk):
         for n, i in stages:
-            per[n].append(ev[t][i].elapsed_time(ev[t][i + 1]) * 1000.0)
-        tot.append(ev[t][0].elapsed_time(ev[t][3]) * 1000.0)
+            per[n].append(hev.elapsed_us(t, i, i + 1))
+        tot.append(hev.elapsed_us(t, 0, 3))
+    hev.close()
+    event_kind = hev.kind
     kern_us = {n: float(np.mean(v)) for n, v in per.items()}
 
     # algorithmic bytes / flops per launch (the minimal traffic of each stage)
@@ -197,11 +213,12 @@ def main():
                       "hbm_frac": round(gbs / HBM_PEAK, 5), "alg_flops": alg[k]["flops"]}
     dom = max(kernels, key=lambda k: kernels[k]["us"])
     dk = kernels[dom]
+    traffic = measured_traffic(cfg.name)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": dk["GB_s"], "peak": HBM_PEAK, "unit": "GB/s",
-                "frac": dk["hbm_frac"], "traffic": None}
+                "frac": dk["hbm_frac"], "traffic": traffic.get(dom)}
     sk = kernels["scan_kernel"]
     roofline_scan = {"kernel": "scan_kernel", "bound": "hbm", "achieved": sk["GB_s"], "peak": HBM_PEAK,
-                     "unit": "GB/s", "frac": sk["hbm_frac"], "traffic": None}
+                     "unit": "GB/s", "frac": sk["hbm_frac"], "traffic": traffic.get("scan_kernel")}
     round_bytes = alg["scan_kernel"]["bytes"] + alg["tree_kernel"]["bytes"]
     ideal_us = round_bytes / (HBM_PEAK * 1e9) * 1e6
     round_stats = {"p50_us": round(float(np.percentile(tot, 50)), 3), "p99_us": round(float(np.percentile(tot, 99)), 3),
@@ -234,6 +251,7 @@ def main():
         "roofline": roofline,
         "roofline_scan": roofline_scan,
         "kernels": kernels,
+        "stage_timing": event_kind,
         "plan": info,
         "round": round_stats,
         "us_per_round_eager": round(us_eager, 3),
@@ -241,6 +259,94 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+KERNEL_SOURCES = {
+    "tree_kernel": ["diffusion_drafter_tree_amd/csrc/tree_fast.hip", "diffusion_drafter_tree_amd/csrc/common.h",
+                    "diffusion_drafter_tree_amd/csrc/kernels.h"],
+    "scan_kernel": ["diffusion_drafter_tree_amd/csrc/scan.hip", "diffusion_drafter_tree_amd/csrc/common.h",
+                    "diffusion_drafter_tree_amd/csrc/kernels.h"],
+}
+
+
+def measured_traffic(cfg_name):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary of this workload, per kernel, only while the kernel's sources still
+    hash to the value recorded with the counters (else the kernel is absent)."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", f"hbm_traffic_{cfg_name}.md")
+    out = {}
+    if not os.path.exists(path):
+        return out
+    rec = None
+    for line in open(path):
+        if line.startswith("traffic-json:"):
+            rec = json.loads(line.split(":", 1)[1])
+    for k, files in KERNEL_SOURCES.items():
+        if not rec or k not in rec:
+            continue
+        h = hashlib.sha256()
+        for f in files:
+            h.update(open(os.path.join(root, f), "rb").read())
+        if h.hexdigest()[:16] == rec[k]["src_sha256"]:
+            out[k] = rec[k]["bytes"]
+    return out
+
+
+class StageEvents:
+    """Four timing events per round for the library's stage hook: HIP events
+    created with hipEventDisableSystemFence through the HIP runtime the process
+    already uses (the one torch loaded), else torch's events."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.n = n
+        self.hip = None
+        self.kind = "torch.cuda.Event"
+        try:
+            hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            evs = []
+            for _ in range(n):
+                e = ctypes.c_void_p()
+                if hip.hipEventCreateWithFlags(ctypes.byref(e), 0x20000000) != 0:   # hipEventDisableSystemFence
+                    raise OSError("hipEventCreateWithFlags failed")
+                evs.append(e.value)
+            self.hip, self.evs = hip, evs
+            self.kind = "hipEvent (DisableSystemFence)"
+        except OSError:
+            import torch
+            self.evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    def set(self, t):
+        from diffusion_drafter_tree_amd import _lib as C
+        from diffusion_drafter_tree_amd import ops
+        if self.hip is None:
+            ops.set_stage_events(self.evs[4 * t:4 * t + 4])
+            return
+        arr = (self.ct.c_void_p * 4)(*self.evs[4 * t:4 * t + 4])
+        st = C.load().dartree_set_stage_events(arr, 4)
+        if st != 0:
+            raise RuntimeError("dartree_set_stage_events: %s" % C.last_error())
+
+    def elapsed_us(self, t, i, j):
+        if self.hip is None:
+            return self.evs[4 * t + i].elapsed_time(self.evs[4 * t + j]) * 1000.0
+        ms = self.ct.c_float(0.0)
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), self.evs[4 * t + i], self.evs[4 * t + j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value * 1000.0
+
+    def close(self):
+        if self.hip is not None:
+            for e in self.evs:
+                self.hip.hipEventDestroy(e)
+            self.hip = None
+            self.evs = []
 
 
 def cpu_baseline(cfg, head, budget_s):
