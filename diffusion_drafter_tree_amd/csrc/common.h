@@ -126,37 +126,52 @@ __device__ __forceinline__ void bitonic_stage(uint32_t& hi, uint32_t& lo) {
   hi = pick ? ph : hi;
   lo = pick ? pl : lo;
 }
-// The same network over 32-bit keys.
-template <int K, int J>
-__device__ __forceinline__ void bitonic_stage32(uint32_t& k) {
-  const uint32_t lane = __lane_id();
-  const uint32_t pk = lane_xor<J>(k);
-  const bool take_max = (((lane / J) ^ (lane / K)) & 1u) == 0u;
-  k = take_max ? max(k, pk) : min(k, pk);
-}
 // Sorts the wave's 64 32-bit keys descending (lane 0 holds the largest).
+// Each merge of width K starts with a flip (lane i against lane i ^ (K-1)),
+// then half-cleaners (lane i against lane i ^ J, J = K/4 .. 1). In every
+// compare-exchange the lower lane of the pair keeps the larger key, so the
+// direction is one lane bit: an all-ones / zero mask per bit, applied with a
+// bitfield select (no lane-mask registers).
 __device__ __forceinline__ void wave_sort_desc32(uint32_t& k) {
-  bitonic_stage32<2, 1>(k);
-  bitonic_stage32<4, 2>(k);
-  bitonic_stage32<4, 1>(k);
-  bitonic_stage32<8, 4>(k);
-  bitonic_stage32<8, 2>(k);
-  bitonic_stage32<8, 1>(k);
-  bitonic_stage32<16, 8>(k);
-  bitonic_stage32<16, 4>(k);
-  bitonic_stage32<16, 2>(k);
-  bitonic_stage32<16, 1>(k);
-  bitonic_stage32<32, 16>(k);
-  bitonic_stage32<32, 8>(k);
-  bitonic_stage32<32, 4>(k);
-  bitonic_stage32<32, 2>(k);
-  bitonic_stage32<32, 1>(k);
-  bitonic_stage32<64, 32>(k);
-  bitonic_stage32<64, 16>(k);
-  bitonic_stage32<64, 8>(k);
-  bitonic_stage32<64, 4>(k);
-  bitonic_stage32<64, 2>(k);
-  bitonic_stage32<64, 1>(k);
+  const uint32_t lane = __lane_id();
+  uint32_t m[6];
+#pragma unroll
+  for (int b = 0; b < 6; ++b) m[b] = 0u - ((lane >> b) & 1u);
+  auto cx = [&](uint32_t pk, int b) {
+    const uint32_t mx = max(k, pk), mn = min(k, pk);
+    k = (mn & m[b]) | (mx & ~m[b]);
+  };
+  auto x16 = [&](uint32_t v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (r[0] & m[4]) | (r[1] & ~m[4]);
+  };
+  auto x32 = [&](uint32_t v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (r[0] & m[5]) | (r[1] & ~m[5]);
+  };
+  auto x4 = [&](uint32_t v) { return dpp<kDppHalfMirror>(dpp<kDppXor3>(v)); };
+  auto x8 = [&](uint32_t v) { return dpp<kDppHalfMirror>(dpp<kDppMirror>(v)); };
+  cx(dpp<kDppXor1>(k), 0);
+  cx(dpp<kDppXor3>(k), 1);
+  cx(dpp<kDppXor1>(k), 0);
+  cx(dpp<kDppHalfMirror>(k), 2);
+  cx(dpp<kDppXor2>(k), 1);
+  cx(dpp<kDppXor1>(k), 0);
+  cx(dpp<kDppMirror>(k), 3);
+  cx(x4(k), 2);
+  cx(dpp<kDppXor2>(k), 1);
+  cx(dpp<kDppXor1>(k), 0);
+  cx(x16(dpp<kDppMirror>(k)), 4);
+  cx(x8(k), 3);
+  cx(x4(k), 2);
+  cx(dpp<kDppXor2>(k), 1);
+  cx(dpp<kDppXor1>(k), 0);
+  cx(x32(x16(dpp<kDppMirror>(k))), 5);
+  cx(x16(k), 4);
+  cx(x8(k), 3);
+  cx(x4(k), 2);
+  cx(dpp<kDppXor2>(k), 1);
+  cx(dpp<kDppXor1>(k), 0);
 }
 
 // Sorts the wave's 64 keys descending (lane 0 holds the largest).
@@ -199,25 +214,51 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   v = min(v, dpp<kDppMirror>(v));
   return min(min(readlane(v, 0), readlane(v, 16)), min(readlane(v, 32), readlane(v, 48)));
 }
+// Wave-wide max / sum: four butterfly steps inside each 16-lane row, then two
+// row broadcasts (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2
+// and 3) leave the total in lane 63, each step one VALU instruction with its
+// DPP operand fused (the s_nop 1 covers the two wait states a DPP read needs
+// after a VALU write). Fixed pattern: every call combines in the same order,
+// so results are reproducible bit for bit.
 __device__ __forceinline__ float wave_max_f32(float x) {
-  uint32_t v = __float_as_uint(x);
-  v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp<kDppXor1>(v))));
-  v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp<kDppXor2>(v))));
-  v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp<kDppHalfMirror>(v))));
-  v = __float_as_uint(fmaxf(__uint_as_float(v), __uint_as_float(dpp<kDppMirror>(v))));
-  return fmaxf(fmaxf(__uint_as_float(readlane(v, 0)), __uint_as_float(readlane(v, 16))),
-               fmaxf(__uint_as_float(readlane(v, 32)), __uint_as_float(readlane(v, 48))));
+  float r;
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %1, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %1, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %1, %1, %1 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %1, %1, %1 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %1, %1, %1 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_readlane_b32 %0, %1, 63"
+      : "=s"(r), "+v"(x));
+  return r;
 }
-// Fixed-pattern sum: every call adds in the same order, so results are
-// reproducible bit for bit.
 __device__ __forceinline__ float wave_sum_f32(float x) {
-  uint32_t v = __float_as_uint(x);
-  v = __float_as_uint(__uint_as_float(v) + __uint_as_float(dpp<kDppXor1>(v)));
-  v = __float_as_uint(__uint_as_float(v) + __uint_as_float(dpp<kDppXor2>(v)));
-  v = __float_as_uint(__uint_as_float(v) + __uint_as_float(dpp<kDppHalfMirror>(v)));
-  v = __float_as_uint(__uint_as_float(v) + __uint_as_float(dpp<kDppMirror>(v)));
-  return (__uint_as_float(readlane(v, 0)) + __uint_as_float(readlane(v, 16))) +
-         (__uint_as_float(readlane(v, 32)) + __uint_as_float(readlane(v, 48)));
+  float r;
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %1, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_add_f32_dpp %1, %1, %1 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_readlane_b32 %0, %1, 63"
+      : "=s"(r), "+v"(x));
+  return r;
 }
 __device__ __forceinline__ int wave_sum_i32(int x) {
   uint32_t v = (uint32_t)x;

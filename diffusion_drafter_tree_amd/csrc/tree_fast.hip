@@ -540,7 +540,10 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
         // children alone reach T). K >= W children are valid.
         uint32_t sk32 = kh;
         wave_sort_desc32(sk32);
-        if (lane == 0) s.misc[par] = (int)readlane(sk32, W - 1);
+        // the cross-lane read stays outside the one-lane branch: inside it the
+        // compiler may sink the sort's last stage under that lane's mask
+        const int tw = (int)readlane(sk32, W - 1);
+        if (lane == 0) s.misc[par] = tw;
       }
     }
     if (w == 0) __builtin_amdgcn_s_setprio(0);
