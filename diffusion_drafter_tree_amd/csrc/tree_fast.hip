@@ -41,6 +41,7 @@ constexpr int RT = 256;            // state width
 constexpr int SSTR = RT + 8;       // split-state row stride (bf16 halves)
 constexpr int ASTR = RT + 4;       // A*S row stride (floats)
 constexpr int kWMax = 16;
+constexpr int kLMax = 31;
 constexpr int kSkCap = 1024;       // survivor keys (>= 16 parents x 64 candidates)
 constexpr size_t kMaxSmem = 160 * 1024;
 constexpr int kMaxMergeS = 8;     // slice lists merged in the prologue
@@ -665,7 +666,9 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   // ---- the expanded levels to global memory ---------------------------------------
   if (expand) {
     const int n0 = (a.d0 - 1) * W, n1 = a.d1 * W;
-    for (int i = n0 + tid; i < n1; i += kT) {
+    // stored by the upper half of the workgroup while the lower half builds
+    // the node keys of the selection below
+    for (int i = n0 + ((tid + kT / 2) & (kT - 1)); i < n1; i += kT) {
       const int d = i / W + 1, sl = i - (d - 1) * W;
       if (sl < s.lv_cnt[d - 1]) {
         a.st_tok[lw + i] = s.lv_tok[i];
@@ -700,7 +703,8 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       }
     }
   }
-  // Node keys (0 for empty slots), zero-padded to a multiple of 8.
+  // Node keys (0 for empty slots), zero-padded to a multiple of 8; the rank
+  // counters (held in eix until the emitted index replaces them) start at 0.
   const int N = L * W, N8 = (N + 7) & ~7;
   for (int i = tid; i < N8; i += kT) {
     uint64_t key = 0ull;
@@ -711,60 +715,64 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
         const uint32_t ps = d == 1 ? 0u : ((uint32_t)s.lv_ps[i] & 0x1FFu);
         key = ((uint64_t)f32_key(s.lv_sb[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (((uint32_t)d << 27) | (tok << 9) | ps));
       }
+      s.eix[i] = 0;
     }
     s.nkey[i] = key;
   }
   if (tid < 32) s.nd[tid] = 0;   // per level: bit (path rank) set when the node is selected
   lds_sync();
   {
-    // rank of each node = number of larger keys, G threads per node, eight
-    // keys per step; a node is selected when its rank is below B
-    int G = 16;
-    while (G > 1 && N * G > kT) G >>= 1;
-    const int per = ((N + G - 1) / G + 7) & ~7;
-    const int x = tid / G, seg = tid - x * G;
-    uint64_t kx = 0ull;
-    uint32_t cnt = 0u;
-    if (x < N) {
-      kx = s.nkey[x];
-      const int y1 = min(N8, (seg + 1) * per);
-      for (int y = seg * per; y < y1; y += 8) {
-        uint64_t k8[8];
+    // Rank of each node = the number of larger keys. Nodes go one per lane
+    // over NW waves, the keys over G = 16 / NW segments, one per group of NW
+    // waves: all lanes of a wave compare against the same keys, read by
+    // broadcast, and the partial counts are added in LDS.
+    const int NW = (N8 + kWave - 1) / kWave;
+    const int G = kWaves / NW;
+    const int seg = w / NW, x = (w - seg * NW) * kWave + lane;
+    if (seg < G) {
+      const uint64_t kx = x < N8 ? s.nkey[x] : ~0ull;
+      const int KS = (((N8 + G - 1) / G) + 7) & ~7;   // keys per segment, a multiple of 8
+      const int y0 = seg * KS, y1 = min(N8, y0 + KS);
+      uint32_t c = 0u;
+      for (int y = y0; y < y1; y += 8) {   // four 16-byte reads in flight per step
+        u64x2_t k2[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) k8[e] = s.nkey[y + e];
+        for (int e = 0; e < 4; ++e) k2[e] = *reinterpret_cast<const LDS u64x2_t*>(s.nkey + y + 2 * e);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cnt += k8[e] > kx ? 1u : 0u;
+        for (int e = 0; e < 4; ++e) c += (k2[e].x > kx ? 1u : 0u) + (k2[e].y > kx ? 1u : 0u);
       }
+      if (x < N && c) lds_add(&s.eix[x], (int)c);
     }
-    const uint32_t rk = group_sum(cnt, G);
-    if (x < N && seg == 0 && kx != 0ull && (int)rk < B) lds_or(&s.nd[x / W], 1 << s.lv_lex[x]);
   }
+  lds_sync();
+  // a node is selected when its rank is below B (empty slots: key 0, never)
+  for (int i = tid; i < N; i += kT)
+    if (s.nkey[i] != 0ull && s.eix[i] < B) lds_or(&s.nd[i / W], 1 << s.lv_lex[i]);
   lds_sync();
   // emitted index: selected nodes of earlier levels, then selected nodes of
   // the level with a smaller path rank (breadth-first order = path order).
-  // One wave counts the selected nodes of the levels before each level
-  // (lane d: levels 0..d-1; lane 32: all of them).
-  if (w == 0) {
-    int acc = 0;
+  // Wave 0 also totals the selection for everyone.
+  for (int i = tid; i < ((N + kWave - 1) & ~(kWave - 1)); i += kT) {
+    const int d = min(i / W + 1, L);
+    int base = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < 32; i += 4) {
-      const u32x4_t v4 = *reinterpret_cast<const LDS u32x4_t*>(s.nd + i);
-      acc += (i < lane ? __popc(v4.x) : 0) + (i + 1 < lane ? __popc(v4.y) : 0) + (i + 2 < lane ? __popc(v4.z) : 0) +
-             (i + 3 < lane ? __popc(v4.w) : 0);
+    for (int j = 0; j < 32; j += 4) {
+      const u32x4_t v4 = *reinterpret_cast<const LDS u32x4_t*>(s.nd + j);
+      const int p0 = __popc(v4.x), p1 = __popc(v4.y), p2 = __popc(v4.z), p3 = __popc(v4.w);
+      base += (j < d - 1 ? p0 : 0) + (j + 1 < d - 1 ? p1 : 0) + (j + 2 < d - 1 ? p2 : 0) + (j + 3 < d - 1 ? p3 : 0);
+      tot += p0 + p1 + p2 + p3;
     }
-    if (lane <= 32) s.base[lane] = acc;
+    if (i == 0) s.base[32] = tot;
+    if (i < N) {
+      const uint32_t m = s.nd[d - 1];
+      const int lx = s.lv_lex[i];
+      int e = -1;
+      if (s.nkey[i] != 0ull && ((m >> lx) & 1u)) e = base + __popc(m & ((1u << lx) - 1u));
+      s.eix[i] = e;
+    }
   }
   lds_sync();
   const int n = s.base[32];
-  for (int i = tid; i < N; i += kT) {
-    const int d = i / W + 1;
-    const uint32_t m = s.nd[d - 1];
-    const int lx = s.lv_lex[i];
-    int e = -1;
-    if (i - (d - 1) * W < s.lv_cnt[d - 1] && ((m >> lx) & 1u)) e = s.base[d - 1] + __popc(m & ((1u << lx) - 1u));
-    s.eix[i] = e;
-  }
-  lds_sync();
   int32_t* o_tok = a.tok + (size_t)q * B;
   int32_t* o_dep = a.depth + (size_t)q * B;
   int32_t* o_par = a.parent + (size_t)q * B;
@@ -843,7 +851,7 @@ TreePlan tree_fast_plan(const TreeArgs& a) {
   const bool al = ((((uintptr_t)a.A) | ((uintptr_t)a.E) | ((uintptr_t)a.U) | ((uintptr_t)a.h) |
                     ((uintptr_t)a.st_state)) & 15u) == 0;
   if (!a.bf16 || a.r != RT || !(a.K == 16 || a.K == 32 || a.K == 64) || a.W > kWMax || a.W < 1 || a.V < a.K ||
-      a.L > 31 || a.B > 1024 || !al || (a.lists && a.S > kMaxMergeS))
+      a.L > kLMax || a.B > 1024 || !al || (a.lists && a.S > kMaxMergeS))
     return p;
   p.mode = 3;
   p.kq = 16 / (a.K / 16) > 8 ? 8 : 16 / (a.K / 16);
