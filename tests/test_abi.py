@@ -178,3 +178,22 @@ def test_round_plan_query(lib):
     d = ops.make_dims(I.CONFIGS["tiny"])
     d.beta = 0.5
     assert lib.dartree_round_plan(ctypes.byref(d), ctypes.byref(C.RoundInfo())) == C.ERR_INVALID_ARGUMENT
+
+
+def test_gpu_parity_cases_cover_the_block_decoding_kernel(lib):
+    """The fast_* GPU parity cases run on the block-decoding tree kernel (the
+    others on the general one), so its shapes are covered: K = 16, 32, 64,
+    W = 1 .. 16, L = 1 .. 31, B up to 256 (several mask words), one and many
+    vocabulary slices."""
+    import importlib.util
+    from diffusion_drafter_tree_amd import ops
+    path = os.path.join(ROOT, "tests", "test_gpu_parity.py")
+    spec = importlib.util.spec_from_file_location("gpu_parity_cases", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert len(mod.FAST) >= 6
+    for name, cfg in mod.SMALL.items():
+        info = ops.round_plan(ops.make_dims(cfg))
+        assert info["tree_kernel"] == (1 if name in mod.FAST else 0), (name, info)
+    slices = {ops.round_plan(ops.make_dims(mod.SMALL[n]))["scan_slices"] for n in mod.FAST}
+    assert 1 in slices and max(slices) > 1

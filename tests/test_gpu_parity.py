@@ -73,7 +73,17 @@ SMALL = {
     "whole_supertree_WL_le_B": I.small_variant("qwen3_4b", n_req=1, V=4000, L=5, K=16, W=4, B=64, r=64, D=64),
     "K_eq_V": I.small_variant("tiny", V=48, K=48, L=4, W=6, B=10, r=16),
     "L1": I.small_variant("qwen3_4b", n_req=2, V=5000, L=1, K=20, W=5, B=3, r=32, D=32),
+    # block-decoding kernel shapes (bf16 weights, r = 256, K in {16, 32, 64}, W <= 16)
+    "fast_K16_W16_L31_B100": I.small_variant("qwen3_4b", n_req=2, V=5000, L=31, K=16, W=16, B=100, r=256, D=64),
+    "fast_K32_W1_beta0": I.small_variant("qwen3_4b", n_req=1, V=4000, L=9, K=32, W=1, B=6, r=256, D=64, beta=0.0),
+    "fast_K64_W12_L6": I.small_variant("qwen3_4b", n_req=2, V=6000, L=6, K=64, W=12, B=40, r=256, D=96),
+    "fast_W16_whole_supertree_B256": I.small_variant("qwen3_4b", n_req=1, V=5000, L=16, K=64, W=16, B=256, r=256,
+                                                     D=64),
+    "fast_L1": I.small_variant("qwen3_4b", n_req=3, V=3000, L=1, K=64, W=8, B=5, r=256, D=32),
+    "fast_multislice_K64": I.small_variant("qwen3_4b", n_req=1, V=100000, L=4, K=64, W=10, B=30, r=256, D=64,
+                                           beta=-5.0),
 }
+FAST = sorted(k for k in SMALL if k.startswith("fast_"))
 
 
 @pytest.mark.parametrize("name", sorted(SMALL))
@@ -81,7 +91,8 @@ def test_small_configs_build_round(name):
     check(SMALL[name].with_(name=name))
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "bf16_multichunk", "f32_multichunk_valu", "wide_W32_K256"])
+@pytest.mark.parametrize("name", ["tiny_f32", "bf16_multichunk", "f32_multichunk_valu", "wide_W32_K256",
+                                  "fast_K64_W12_L6", "fast_K16_W16_L31_B100"])
 def test_step_entry_points_match_fused_round(name):
     cfg = SMALL[name].with_(name=name)
     a, _ = check(cfg, mode="build")
