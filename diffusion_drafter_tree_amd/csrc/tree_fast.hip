@@ -1,9 +1,7 @@
 // Steps a2..a5 for the block-decoding shapes: bf16 weights, state width
 // r = 256, K in {16, 32, 64} candidates per position, W <= 16 per depth.
-// One 1024-thread workgroup per request with the general kernel's arithmetic
-// for the scores (split-bf16 MFMA contractions with exact products, fp32
-// log-softmax), arranged for latency: five barriers per depth and no wait on
-// global memory inside the depth loop.
+// One 1024-thread workgroup per request, arranged for latency: five LDS-only
+// barriers per depth and no wait on global memory inside the depth loop.
 //
 // DARTree (marsggbo blog, section 3.1): at depth d the surviving parents of
 // depth d-1 are scored in one batched head call against their K candidates;
@@ -13,21 +11,29 @@
 // verified under an ancestor mask. Node order everywhere: s_beta descending,
 // then depth, token and parent slot ascending.
 //
+// Numerics: parent states as two fp16 planes (hi + lo, within 2^-20 of the
+// fp32 state), weights as fp16 (exact for bf16 values of magnitude >= 2^-17),
+// products on v_mfma_f32_16x16x32_f16 with fp32 accumulation; fp32
+// log-softmax on the hardware exp2 / log2.
+//
+// Prologue: the scan's sorted slice lists merged per row (one wave per row),
+// A fragments from the fp16 copy the scan launch staged, the root state split.
 // Per depth:
-//   P1  stage the E rows and h row prefetched one depth earlier into LDS; the
-//       contractions Z = S U_C^T (KQ partial tiles) and AS = A S^T (A resident
-//       in registers, wave w owning rows 16w..16w+15); then issue the next
-//       depth's prefetch into registers (U fragments, E rows, h row).
+//   P1  Z = S U_C^T as partial tiles over k-groups (U fragments prefetched one
+//       depth earlier into registers), then the first k-steps of A S^T on the
+//       same state fragments (A resident in registers).
 //   P2  one wave per parent: log-softmax over its K candidates, cum, s_beta,
-//       64-bit keys; the W-th largest high word of the wave's keys by a
-//       ballot bit search, max-reduced over the parents into T. At least W
-//       keys reach T (all of them in the wave that attains it).
-//   P3  keys with high word >= T are compacted, then ranked by counting; the
-//       W smallest ranks are the depth's survivors, in order.
-//   P4  one wave per survivor: its state tanh(A s_parent + E[u] + h_d) split
-//       into three bf16 parts; one wave ranks the level's token paths.
-// The selection, emission and mask after the depth loop follow the general
-// kernel's definitions, with ranks by counting over the at most L*W nodes.
+//       64-bit keys; the slot-0 parent's wave sorts its high words and takes
+//       the W-th as the bound T (its W best children alone reach T); the
+//       previous level's path ranks; the rest of A S^T.
+//   P3a keys with high word >= T compacted into LDS.
+//   P3b survivors ranked by counting; the W smallest ranks are the level, in
+//       order; this depth's staged E and h rows written into LDS.
+//   P4  one wave per kept node: its state tanh(A s_parent + E[u] + h_d) split
+//       into the two fp16 planes the next depth reads.
+// The next depth's U fragments and E / h rows are loaded into registers one
+// share per phase. After the loop: the levels to global memory, the deferred
+// top-B by counting ranks over the at most L*W nodes, emission and mask.
 #include "common.h"
 #include "kernels.h"
 
@@ -38,7 +44,7 @@ namespace {
 constexpr int kT = 1024;
 constexpr int kWaves = kT / kWave;
 constexpr int RT = 256;            // state width
-constexpr int SSTR = RT + 8;       // split-state row stride (bf16 halves)
+constexpr int SSTR = RT + 8;       // state-plane row stride (fp16 elements)
 constexpr int ASTR = RT + 4;       // A*S row stride (floats)
 constexpr int kWMax = 16;
 constexpr int kLMax = 31;
@@ -181,8 +187,9 @@ __device__ __forceinline__ FLay make_flay(const VOff& o) {
 
 // Two fp16 parts of 4 consecutive fp32 state values (8 bytes per plane):
 // hi = the value truncated to fp16, lo = the remainder (exact in fp32)
-// truncated to fp16; hi + lo carries 22 significant bits (relative error at
-// most 2^-22 for |s| >= 2^-14, absolute at most 2^-25 below).
+// truncated to fp16. |hi - s| < 2^-10 |s| and truncating the remainder loses
+// less than 2^-10 of it, so |s - (hi + lo)| < max(2^-20 |s|, 2^-24) (the
+// second term where the remainder falls below the fp16 normal range).
 __device__ __forceinline__ void split_store4(const FLay& s, int row, int j0, const float (&v)[4]) {
   const h16x2_t h01 = pkrtz(v[0], v[1]);
   const h16x2_t h23 = pkrtz(v[2], v[3]);
