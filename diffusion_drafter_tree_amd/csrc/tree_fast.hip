@@ -277,32 +277,16 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   auto kstep = [&](int i) { return hk * 4 + ((i + zrot) & 3); };
 
   // ---- prologue ------------------------------------------------------------
-  // Global loads are issued first, in the order the work needs them: this
-  // wave's slice lists, its A fragments, the root state row.
+  // This wave's slice lists and the root state row are loaded first; the A
+  // fragments only after the merge (their 128 KB would hold the list loads
+  // and the merge behind them in the memory pipeline).
   uint64_t ks[kMaxMergeS];
+  u16x8_t araw[2][4];
   const bool merge_here = expand && a.lists != nullptr;
   if (merge_here && w < L) {
     const uint64_t* lst = a.lists + (size_t)(q * L + w) * a.S * KC;
 #pragma unroll
     for (int sl = 0; sl < kMaxMergeS; ++sl) ks[sl] = (sl < a.S && lane < KC) ? lst[sl * KC + lane] : 0ull;
-  }
-  // A fragments: 1 KB contiguous runs of the fp16 copy the scan launch
-  // staged, or (without it) 16 rows x 16 bytes of A per load, converted below
-  u16x8_t araw[2][4];
-  if (expand && a.a_frag) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        araw[t][i] = *reinterpret_cast<const u16x8_t*>(
-            a.a_frag + ((size_t)((w * 2 + t) * 4 + ((i + zrot) & 3)) * kWave + lane) * 8);
-  } else if (expand) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint16_t* arow = A + (size_t)(aw * 32 + t * 16 + (lane & 15)) * RT + sub;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) araw[t][i] = *reinterpret_cast<const u16x8_t*>(arow + kstep(i) * 32);
-    }
   }
   f32x4_t h0 = {0.f, 0.f, 0.f, 0.f};
   if (expand && a.d0 == 1 && tid < RT / 4) h0 = *reinterpret_cast<const f32x4_t*>(hq + tid * 4);
@@ -332,7 +316,7 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
     // the elementwise maximum of one descending list and the other reversed
     // holds the K best of both as a bitonic sequence, which six half-cleaner
     // stages sort descending. Keys are (value key << 32) | ~id, so the order
-    // is value descending, id ascending.
+    // is value descending, id ascending. kMaxMergeS <= 8 slices.
     for (int row = w; row < L; row += kWaves) {
       if (row != w) {
         const uint64_t* lst = a.lists + (size_t)(q * L + row) * a.S * KC;
@@ -370,6 +354,23 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       const int c = cid_g[i];
       s.cid[i] = (c < 0 || c >= a.V) ? 0 : c;
       s.clog[i] = clog_g[i];
+    }
+  }
+  // A fragments: 1 KB contiguous runs of the fp16 copy the scan launch
+  // staged, or (without it) 16 rows x 16 bytes of A per load, converted below
+  if (expand && a.a_frag) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        araw[t][i] = *reinterpret_cast<const u16x8_t*>(
+            a.a_frag + ((size_t)((w * 2 + t) * 4 + ((i + zrot) & 3)) * kWave + lane) * 8);
+  } else if (expand) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t* arow = A + (size_t)(aw * 32 + t * 16 + (lane & 15)) * RT + sub;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) araw[t][i] = *reinterpret_cast<const u16x8_t*>(arow + kstep(i) * 32);
     }
   }
   if (expand) {

@@ -197,3 +197,6 @@ def test_gpu_parity_cases_cover_the_block_decoding_kernel(lib):
         assert info["tree_kernel"] == (1 if name in mod.FAST else 0), (name, info)
     slices = {ops.round_plan(ops.make_dims(mod.SMALL[n]))["scan_slices"] for n in mod.FAST}
     assert 1 in slices and max(slices) > 1
+    # both key widths of the slice-list merge: bf16 and fp32 logits over several slices
+    multi = [mod.SMALL[n] for n in mod.FAST if ops.round_plan(ops.make_dims(mod.SMALL[n]))["scan_slices"] > 1]
+    assert {c.logits_dtype for c in multi} == {"bf16", "f32"}

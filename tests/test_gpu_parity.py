@@ -82,6 +82,8 @@ SMALL = {
     "fast_L1": I.small_variant("qwen3_4b", n_req=3, V=3000, L=1, K=64, W=8, B=5, r=256, D=32),
     "fast_multislice_K64": I.small_variant("qwen3_4b", n_req=1, V=100000, L=4, K=64, W=10, B=30, r=256, D=64,
                                            beta=-5.0),
+    "fast_f32_logits_multislice": I.small_variant("qwen3_4b", n_req=2, V=60000, L=5, K=64, W=8, B=24, r=256, D=64,
+                                                  logits_dtype="f32"),
 }
 FAST = sorted(k for k in SMALL if k.startswith("fast_"))
 
