@@ -201,13 +201,6 @@ __device__ __forceinline__ void wave_sort_desc(uint32_t& hi, uint32_t& lo) {
 }
 
 // Wave reductions; the result is wave-uniform.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp<kDppXor1>(v));
-  v = max(v, dpp<kDppXor2>(v));
-  v = max(v, dpp<kDppHalfMirror>(v));
-  v = max(v, dpp<kDppMirror>(v));
-  return max(max(readlane(v, 0), readlane(v, 16)), max(readlane(v, 32), readlane(v, 48)));
-}
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   v = min(v, dpp<kDppXor1>(v));
   v = min(v, dpp<kDppXor2>(v));
@@ -270,11 +263,47 @@ __device__ __forceinline__ int wave_sum_i32(int x) {
   return (int)(readlane(v, 0) + readlane(v, 16) + readlane(v, 32) + readlane(v, 48));
 }
 
+// Largest of the 64 lanes' unsigned values, as a scalar (the DPP pattern of
+// wave_max_f32).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  uint32_t r;
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %1, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %1, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %1, %1, %1 row_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %1, %1, %1 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_u32_dpp %1, %1, %1 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_readlane_b32 %0, %1, 63"
+      : "=s"(r), "+v"(x));
+  return r;
+}
+
 // m-th largest of the lanes' values among lanes with valid set (wave-uniform;
-// 0 when fewer than m lanes are valid). Bit-by-bit search on ballots.
+// 0 when fewer than m lanes are valid). For m <= 8 the largest remaining
+// value is taken out m times at most (all lanes holding it at once, their
+// count added up); otherwise a bit-by-bit search on ballots.
 __device__ __forceinline__ uint32_t wave_mth_largest(uint32_t v, bool valid, int m, int nbits) {
   const uint64_t vm = __builtin_amdgcn_ballot_w64(valid);
   uint32_t t = 0;
+  if (m <= 8) {
+    v = valid ? v : 0u;
+    int have = 0;
+    for (int it = 0; it < m; ++it) {
+      t = wave_max_u32(v);
+      have += __popcll(__builtin_amdgcn_ballot_w64(v == t) & vm);
+      if (have >= m || t == 0u) break;
+      v = v == t ? 0u : v;
+    }
+    return have >= m ? t : 0u;
+  }
   for (int b = nbits - 1; b >= 0; --b) {
     const uint32_t c = t | (1u << b);
     const int n = __popcll(__builtin_amdgcn_ballot_w64(v >= c) & vm);

@@ -202,23 +202,29 @@ __device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
   const bool bound_ok = sm.misc[4] == 0;
   const uint32_t T = ~(uint32_t)sm.misc[2];
   if (bound_ok) {
-    // hit vectors (largest key >= T) go to LDS, one wave-level append per
-    // vector round; then one thread per element of a hit vector
+    // hit vectors (largest key >= T) go to LDS, one LDS atomic per wave for
+    // all its rounds; then one thread per element of a hit vector
+    uint64_t bal[NV];
+    int nhit = 0;
 #pragma unroll
     for (int it = 0; it < NV; ++it) {
-      const bool hit = vk[it] >= T;
-      const uint64_t bal = __builtin_amdgcn_ballot_w64(hit);
-      if (bal) {
-        int base = 0;
-        if (lane == 0) base = atomicAdd(&sm.misc[5], __popcll(bal));
-        base = __builtin_amdgcn_readfirstlane(base);
-        if (hit) {
-          const int hv = base + (int)mbcnt64(bal);
+      bal[it] = __builtin_amdgcn_ballot_w64(vk[it] >= T);
+      nhit += __popcll(bal[it]);
+    }
+    if (nhit) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&sm.misc[5], nhit);
+      base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+      for (int it = 0; it < NV; ++it) {
+        if (vk[it] >= T) {
+          const int hv = base + (int)mbcnt64(bal[it]);
           if (hv < kHitCap) {
             sm.hitq[hv] = q[it];
             sm.hitid[hv] = id0(it);
           }
         }
+        base += __popcll(bal[it]);
       }
     }
   }
