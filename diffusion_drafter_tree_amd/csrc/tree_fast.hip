@@ -48,6 +48,7 @@ constexpr int SSTR = RT + 8;       // state-plane row stride (fp16 elements)
 constexpr int ASTR = RT + 4;       // A*S row stride (floats)
 constexpr int kWMax = 16;
 constexpr int kLMax = 31;
+static_assert(kLMax * kWMax <= kT, "the tail takes one supertree node per thread");
 constexpr int kSkCap = 1024;       // survivor keys (>= 16 parents x 64 candidates)
 constexpr size_t kMaxSmem = 160 * 1024;
 constexpr int kMaxMergeS = 8;     // slice lists merged in the prologue
@@ -78,7 +79,7 @@ struct FX {
 
 // Variable LDS region (depends on L, W, B).
 struct VOff {
-  size_t cid, clog, tok, ps, lex, cum, sb, cnt, nkey, sf, eix, nd, base, epar, mb, ab, total;
+  size_t cid, clog, tok, ps, lex, cum, sb, cnt, nkey, eix, nd, epar, total;
 };
 
 __host__ __device__ inline size_t fal16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -100,14 +101,10 @@ __host__ __device__ inline VOff voff(int L, int KC, int W, int B, size_t fixed) 
   o.cum = take(4 * LW);
   o.sb = take(4 * LW);
   o.cnt = take(4 * 32);
-  o.nkey = take(8 * (LW + 8));
-  o.sf = take(4 * LW);
+  o.nkey = take(8 * (LW + 16));
   o.eix = take(4 * LW);
   o.nd = take(4 * 32);
-  o.base = take(4 * 33);
   o.epar = take(4ul * B);
-  o.mb = take(8 * 128);
-  o.ab = take(4 * 128);
   o.total = off;
   return o;
 }
@@ -139,14 +136,10 @@ struct FLay {
   LDS float* lv_cum;
   LDS float* lv_sb;
   LDS int* lv_cnt;     // [32]
-  LDS uint64_t* nkey;  // [L*W]
-  LDS int* sf;         // [L*W] selected flag
-  LDS int* eix;        // [L*W] emitted index
-  LDS int* nd;         // [32]
-  LDS int* base;       // [33]
-  LDS int* epar;       // [B]
-  LDS uint64_t* mb;    // [2][64]
-  LDS int* ab;         // [2][64]
+  LDS uint64_t* nkey;  // [L*W + 16] node keys, zero-padded
+  LDS int* eix;        // [L*W] rank counters
+  LDS int* nd;         // [32] selected path ranks per level
+  LDS int* epar;       // [B] emitted parent index
 };
 
 template <int KC>
@@ -174,13 +167,9 @@ __device__ __forceinline__ FLay make_flay(const VOff& o) {
   s.lv_sb = (LDS float*)(b + o.sb);
   s.lv_cnt = (LDS int*)(b + o.cnt);
   s.nkey = (LDS uint64_t*)(b + o.nkey);
-  s.sf = (LDS int*)(b + o.sf);
   s.eix = (LDS int*)(b + o.eix);
   s.nd = (LDS int*)(b + o.nd);
-  s.base = (LDS int*)(b + o.base);
   s.epar = (LDS int*)(b + o.epar);
-  s.mb = (LDS uint64_t*)(b + o.mb);
-  s.ab = (LDS int*)(b + o.ab);
   return s;
 }
 
@@ -711,18 +700,18 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       }
     }
   }
-  // Node keys (0 for empty slots), zero-padded to a multiple of 8; the rank
-  // counters (held in eix until the emitted index replaces them) start at 0.
-  const int N = L * W, N8 = (N + 7) & ~7;
-  for (int i = tid; i < N8; i += kT) {
+  // Node keys (0 for empty slots), zero-padded to a multiple of 16; the rank
+  // counters start at 0. The level arrays are read whole, in one round trip.
+  const int N = L * W, N16 = (N + 15) & ~15;
+  for (int i = tid; i < N16; i += kT) {
     uint64_t key = 0ull;
     if (i < N) {
       const int d = i / W + 1, sl = i - (d - 1) * W;
-      if (sl < s.lv_cnt[d - 1]) {
-        const uint32_t tok = (uint32_t)s.lv_tok[i] & 0x3FFFFu;
-        const uint32_t ps = d == 1 ? 0u : ((uint32_t)s.lv_ps[i] & 0x1FFu);
-        key = ((uint64_t)f32_key(s.lv_sb[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (((uint32_t)d << 27) | (tok << 9) | ps));
-      }
+      const int cnt = s.lv_cnt[d - 1];
+      const uint32_t tok = (uint32_t)s.lv_tok[i] & 0x3FFFFu;
+      const uint32_t ps = d == 1 ? 0u : ((uint32_t)s.lv_ps[i] & 0x1FFu);
+      const uint32_t kv = f32_key(s.lv_sb[i]);
+      if (sl < cnt) key = ((uint64_t)kv << 32) | (uint64_t)(0xFFFFFFFFu - (((uint32_t)d << 27) | (tok << 9) | ps));
       s.eix[i] = 0;
     }
     s.nkey[i] = key;
@@ -734,20 +723,20 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
     // over NW waves, the keys over G = 16 / NW segments, one per group of NW
     // waves: all lanes of a wave compare against the same keys, read by
     // broadcast, and the partial counts are added in LDS.
-    const int NW = (N8 + kWave - 1) / kWave;
+    const int NW = (N16 + kWave - 1) / kWave;
     const int G = kWaves / NW;
     const int seg = w / NW, x = (w - seg * NW) * kWave + lane;
     if (seg < G) {
-      const uint64_t kx = x < N8 ? s.nkey[x] : ~0ull;
-      const int KS = (((N8 + G - 1) / G) + 7) & ~7;   // keys per segment, a multiple of 8
-      const int y0 = seg * KS, y1 = min(N8, y0 + KS);
+      const uint64_t kx = x < N16 ? s.nkey[x] : ~0ull;
+      const int KS = (((N16 + G - 1) / G) + 15) & ~15;   // keys per segment, a multiple of 16
+      const int y0 = seg * KS, y1 = min(N16, y0 + KS);
       uint32_t c = 0u;
-      for (int y = y0; y < y1; y += 8) {   // four 16-byte reads in flight per step
-        u64x2_t k2[4];
+      for (int y = y0; y < y1; y += 16) {   // eight 16-byte reads in flight per step
+        u64x2_t k2[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) k2[e] = *reinterpret_cast<const LDS u64x2_t*>(s.nkey + y + 2 * e);
+        for (int e = 0; e < 8; ++e) k2[e] = *reinterpret_cast<const LDS u64x2_t*>(s.nkey + y + 2 * e);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) c += (k2[e].x > kx ? 1u : 0u) + (k2[e].y > kx ? 1u : 0u);
+        for (int e = 0; e < 8; ++e) c += (k2[e].x > kx ? 1u : 0u) + (k2[e].y > kx ? 1u : 0u);
       }
       if (x < N && c) lds_add(&s.eix[x], (int)c);
     }
@@ -757,44 +746,49 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   for (int i = tid; i < N; i += kT)
     if (s.nkey[i] != 0ull && s.eix[i] < B) lds_or(&s.nd[i / W], 1 << s.lv_lex[i]);
   lds_sync();
-  // emitted index: selected nodes of earlier levels, then selected nodes of
+  // Emitted index: selected nodes of earlier levels, then selected nodes of
   // the level with a smaller path rank (breadth-first order = path order).
-  // Wave 0 also totals the selection for everyone.
-  for (int i = tid; i < ((N + kWave - 1) & ~(kWave - 1)); i += kT) {
-    const int d = min(i / W + 1, L);
-    int base = 0, tot = 0;
+  // Every thread totals the selection. A node's parent index comes from the
+  // same per-level bits: the parent of a selected node is selected (prefix
+  // closure), at the parent level's base plus its rank among that level's
+  // selected path ranks. One node per thread (L * W <= 1024).
+  int n = 0, base = 0, basep = 0;
+  const int d_i = min(tid / W + 1, L);
 #pragma unroll
-    for (int j = 0; j < 32; j += 4) {
-      const u32x4_t v4 = *reinterpret_cast<const LDS u32x4_t*>(s.nd + j);
-      const int p0 = __popc(v4.x), p1 = __popc(v4.y), p2 = __popc(v4.z), p3 = __popc(v4.w);
-      base += (j < d - 1 ? p0 : 0) + (j + 1 < d - 1 ? p1 : 0) + (j + 2 < d - 1 ? p2 : 0) + (j + 3 < d - 1 ? p3 : 0);
-      tot += p0 + p1 + p2 + p3;
-    }
-    if (i == 0) s.base[32] = tot;
-    if (i < N) {
-      const uint32_t m = s.nd[d - 1];
-      const int lx = s.lv_lex[i];
-      int e = -1;
-      if (s.nkey[i] != 0ull && ((m >> lx) & 1u)) e = base + __popc(m & ((1u << lx) - 1u));
-      s.eix[i] = e;
+  for (int j = 0; j < 32; j += 4) {
+    const u32x4_t v4 = *reinterpret_cast<const LDS u32x4_t*>(s.nd + j);
+    const int p[4] = {(int)__popc(v4.x), (int)__popc(v4.y), (int)__popc(v4.z), (int)__popc(v4.w)};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      n += p[t];
+      base += j + t < d_i - 1 ? p[t] : 0;
+      basep += j + t < d_i - 2 ? p[t] : 0;
     }
   }
-  lds_sync();
-  const int n = s.base[32];
   int32_t* o_tok = a.tok + (size_t)q * B;
   int32_t* o_dep = a.depth + (size_t)q * B;
   int32_t* o_par = a.parent + (size_t)q * B;
   float* o_sc = a.score + (size_t)q * B;
   int32_t* o_slot = a.slot + (size_t)q * B;
-  for (int i = tid; i < N; i += kT) {
-    const int e = s.eix[i];
-    if (e >= 0) {
-      const int d = i / W + 1, sl = i - (d - 1) * W;
-      const int pe = d == 1 ? -1 : s.eix[(d - 2) * W + min(max(s.lv_ps[i], 0), W - 1)];
-      o_tok[e] = s.lv_tok[i];
+  if (tid < N) {
+    const int i = tid, d = d_i, sl = i - (d - 1) * W;
+    const uint32_t m = (uint32_t)s.nd[d - 1], mp = d > 1 ? (uint32_t)s.nd[d - 2] : 0u;
+    const int lx = s.lv_lex[i];
+    const int psl = min(max(s.lv_ps[i], 0), W - 1);
+    const bool sel = s.nkey[i] != 0ull && ((m >> lx) & 1u);
+    const int tk = s.lv_tok[i];
+    const float sb = s.lv_sb[i];
+    if (sel) {
+      const int e = base + __popc(m & ((1u << lx) - 1u));
+      int pe = -1;
+      if (d > 1) {
+        const int plx = s.lv_lex[(d - 2) * W + psl];
+        pe = ((mp >> plx) & 1u) ? basep + __popc(mp & ((1u << plx) - 1u)) : -1;
+      }
+      o_tok[e] = tk;
       o_dep[e] = d;
       o_par[e] = pe;
-      o_sc[e] = s.lv_sb[i];
+      o_sc[e] = sb;
       o_slot[e] = sl;
       s.epar[e] = pe;
     }
