@@ -37,6 +37,7 @@ constexpr int kMaxNV = 5;        // 16-byte vectors per thread
 constexpr int kHitCap = 512;     // vectors holding a key >= T
 struct ScanSmem {
   uint64_t key[kScanCap + 8];
+  uint32_t key32[kScanCap + 16];   // bf16 slices: 32-bit survivor keys, zero-padded
   uint64_t out[1024];
   u32x4_t hitq[kHitCap];
   int hitid[kHitCap];
@@ -130,6 +131,45 @@ __device__ void rank_select(ScanSmem& sm, int ns, int K) {
     if (G >= 8) cnt += lane_xor<4>(cnt);
     if (G >= 16) cnt += lane_xor<8>(cnt);
     if (x < ns && seg == 0 && (int)cnt < K) sm.out[cnt] = kx;
+  }
+  for (int i = ns + tid; i < K; i += kT) sm.out[i] = 0ull;
+  __syncthreads();
+}
+
+// The same for bf16 slices on 32-bit keys (bf16 key << 16 | 0xFFFF - offset
+// in the slice: slices are shorter than 65,536 elements, so the keys are
+// distinct and in the same order as the 64-bit ones, and a compare is one
+// 32-bit instruction). Keys past ns are zero, so segments are read in whole
+// 16-key steps. The output is the 64-bit form.
+__device__ void rank_select32(ScanSmem& sm, int ns, int K, int s0) {
+  const int tid = threadIdx.x;
+  int G = 16;
+  while (G > 1 && ns * G > kT) G >>= 1;
+  const int per = (((ns + G - 1) / G) + 15) & ~15;   // multiple of 16
+  for (int x0 = 0; x0 < ns; x0 += kT / G) {
+    const int x = x0 + tid / G, seg = tid % G;
+    uint32_t kx = 0u, cnt = 0u;
+    if (x < ns) {
+      kx = sm.key32[x];
+      const int y1 = min(ns, (seg + 1) * per);
+      for (int y = seg * per; y < y1; y += 16) {
+        u32x4_t k4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) k4[e] = *reinterpret_cast<const u32x4_t*>(&sm.key32[y + 4 * e]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          cnt += (k4[e].x > kx ? 1u : 0u) + (k4[e].y > kx ? 1u : 0u) + (k4[e].z > kx ? 1u : 0u) +
+                 (k4[e].w > kx ? 1u : 0u);
+      }
+    }
+    if (G >= 2) cnt += dpp<kDppXor1>(cnt);
+    if (G >= 4) cnt += dpp<kDppXor2>(cnt);
+    if (G >= 8) cnt += lane_xor<4>(cnt);
+    if (G >= 16) cnt += lane_xor<8>(cnt);
+    if (x < ns && seg == 0 && (int)cnt < K) {
+      const uint32_t idx = (uint32_t)s0 + 0xFFFFu - (kx & 0xFFFFu);
+      sm.out[cnt] = ((uint64_t)(kx >> 16) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+    }
   }
   for (int i = ns + tid; i < K; i += kT) sm.out[i] = 0ull;
   __syncthreads();
@@ -242,7 +282,12 @@ __device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
       base = __builtin_amdgcn_readfirstlane(base);
       if (sv) {
         const int p = base + (int)mbcnt64(bal);
-        if (p < kScanCap) sm.key[p] = ((uint64_t)kk << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
+        if (p < kScanCap) {
+          if constexpr (BF16)
+            sm.key32[p] = (kk << 16) | (0xFFFFu - (uint32_t)(idx - s0));
+          else
+            sm.key[p] = ((uint64_t)kk << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
+        }
       }
     }
   }
@@ -310,14 +355,28 @@ __device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
         for (int e = 0; e < EPV; ++e) {
           const uint32_t kk = Tr::key(Tr::raw(q[it], e));
           const uint32_t ci = 0xFFFFFFFFu - (uint32_t)(e0 + e);
-          if (e0 + e < s1 && (kk > Th || (kk == Th && ci >= Ui))) sm.key[p++] = ((uint64_t)kk << 32) | ci;
+          if (e0 + e < s1 && (kk > Th || (kk == Th && ci >= Ui))) {
+            if constexpr (BF16)
+              sm.key32[p++] = (kk << 16) | (0xFFFFu - (uint32_t)(e0 + e - s0));
+            else
+              sm.key[p++] = ((uint64_t)kk << 32) | ci;
+          }
         }
       }
     }
     __syncthreads();
     ns = sm.misc[3];
+    if constexpr (BF16) {
+      // keys of the overflowed pass may remain past ns: the ranking reads up
+      // to 16 keys beyond ns and needs zeros there
+      if (tid < 16) sm.key32[ns + tid] = 0u;
+      __syncthreads();
+    }
   }
-  rank_select(sm, ns, K);
+  if constexpr (BF16)
+    rank_select32(sm, ns, K, s0);
+  else
+    rank_select(sm, ns, K);
   if (a.S == 1) {
     int32_t* ids = a.cand_ids + (size_t)row * K;
     float* vals = a.cand_logit + (size_t)row * K;
@@ -395,6 +454,8 @@ __global__ __launch_bounds__(kT) void scan_kernel(ScanArgs a) {
   const int b = blockIdx.x;
   if (b < a.n_scan) {
     if (threadIdx.x < 8) smem.scan.misc[threadIdx.x] = 0;
+    if (BF16)
+      for (int i = threadIdx.x; i < kScanCap + 16; i += kT) smem.scan.key32[i] = 0u;
     __syncthreads();
     scan_block<BF16, NV>(a, smem.scan, b);
   } else if (b < a.n_scan + a.n_head) {
