@@ -12,11 +12,13 @@
 // its raw bits (the signed view orders non-negative values and reverses
 // negative ones). Each wave takes the m-th largest of its lanes' largest keys,
 // m = ceil(K / active waves); the smallest of those, T, is reached by at least
-// K elements. Elements with key >= T are compacted (one LDS atomic per
-// thread that holds any) and ranked by counting, G threads per survivor. A
-// slice whose bound fails (a wave with fewer than m lanes) or whose survivors
-// overflow takes an exact path: bitwise searches for the K-th largest key and,
-// among keys equal to it, for the largest complemented ids.
+// K elements. Vectors holding a key >= T are queued in LDS (one LDS atomic
+// per wave), their elements checked one a thread and the survivors compacted
+// (one LDS atomic per wave and pass), then ranked by counting, G threads per
+// survivor (bf16: on 32-bit keys, two survivors a group). A slice whose bound
+// fails (a wave with fewer than m lanes) or whose survivors overflow takes an
+// exact path: bitwise searches for the K-th largest key and, among keys equal
+// to it, for the largest complemented ids.
 //
 // Head workgroups: one per 16x16 tile of h[M][r] = H[M][D] * P[D][r] (Pt
 // stored [r][D]); the 16 waves split D, each issuing all its loads before its
@@ -37,7 +39,7 @@ constexpr int kMaxNV = 5;        // 16-byte vectors per thread
 constexpr int kHitCap = 512;     // vectors holding a key >= T
 struct ScanSmem {
   uint64_t key[kScanCap + 8];
-  uint32_t key32[kScanCap + 16];   // bf16 slices: 32-bit survivor keys, zero-padded
+  uint32_t key32[kScanCap + 32];   // bf16 slices: 32-bit survivor keys, zero-padded
   uint64_t out[1024];
   u32x4_t hitq[kHitCap];
   int hitid[kHitCap];
@@ -138,37 +140,46 @@ __device__ void rank_select(ScanSmem& sm, int ns, int K) {
 
 // The same for bf16 slices on 32-bit keys (bf16 key << 16 | 0xFFFF - offset
 // in the slice: slices are shorter than 65,536 elements, so the keys are
-// distinct and in the same order as the 64-bit ones, and a compare is one
-// 32-bit instruction). Keys past ns are zero, so segments are read in whole
-// 16-key steps. The output is the 64-bit form.
+// distinct and in the same order as the 64-bit ones). A group of G threads
+// ranks two survivors (x and x + ceil(ns / 2)) against one segment of the
+// keys, read 32 at a time and all in flight at once; keys past ns are zero,
+// so segments are read in whole steps. The output is the 64-bit form.
 __device__ void rank_select32(ScanSmem& sm, int ns, int K, int s0) {
   const int tid = threadIdx.x;
+  const int ng = (ns + 1) >> 1;
   int G = 16;
-  while (G > 1 && ns * G > kT) G >>= 1;
-  const int per = (((ns + G - 1) / G) + 15) & ~15;   // multiple of 16
-  for (int x0 = 0; x0 < ns; x0 += kT / G) {
-    const int x = x0 + tid / G, seg = tid % G;
-    uint32_t kx = 0u, cnt = 0u;
-    if (x < ns) {
-      kx = sm.key32[x];
+  while (G > 1 && ng * G > kT) G >>= 1;
+  const int per = (((ns + G - 1) / G) + 31) & ~31;   // multiple of 32
+  auto out64 = [&](uint32_t k) {
+    const uint32_t idx = (uint32_t)s0 + 0xFFFFu - (k & 0xFFFFu);
+    return ((uint64_t)(k >> 16) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+  };
+  for (int g0 = 0; g0 < ng; g0 += kT / G) {
+    const int g = g0 + tid / G, seg = tid % G;
+    const int xb = g + ng;
+    uint32_t ka = 0u, kb = 0u, ca = 0u, cb = 0u;
+    if (g < ng) {
+      ka = sm.key32[g];
+      kb = sm.key32[xb];   // xb <= ns: the zero pad when ns is odd (unused)
       const int y1 = min(ns, (seg + 1) * per);
-      for (int y = seg * per; y < y1; y += 16) {
-        u32x4_t k4[4];
+      for (int y = seg * per; y < y1; y += 32) {
+        u32x4_t k4[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) k4[e] = *reinterpret_cast<const u32x4_t*>(&sm.key32[y + 4 * e]);
+        for (int e = 0; e < 8; ++e) k4[e] = *reinterpret_cast<const u32x4_t*>(&sm.key32[y + 4 * e]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          cnt += (k4[e].x > kx ? 1u : 0u) + (k4[e].y > kx ? 1u : 0u) + (k4[e].z > kx ? 1u : 0u) +
-                 (k4[e].w > kx ? 1u : 0u);
+        for (int e = 0; e < 8; ++e) {
+          ca += (k4[e].x > ka ? 1u : 0u) + (k4[e].y > ka ? 1u : 0u) + (k4[e].z > ka ? 1u : 0u) + (k4[e].w > ka ? 1u : 0u);
+          cb += (k4[e].x > kb ? 1u : 0u) + (k4[e].y > kb ? 1u : 0u) + (k4[e].z > kb ? 1u : 0u) + (k4[e].w > kb ? 1u : 0u);
+        }
       }
     }
-    if (G >= 2) cnt += dpp<kDppXor1>(cnt);
-    if (G >= 4) cnt += dpp<kDppXor2>(cnt);
-    if (G >= 8) cnt += lane_xor<4>(cnt);
-    if (G >= 16) cnt += lane_xor<8>(cnt);
-    if (x < ns && seg == 0 && (int)cnt < K) {
-      const uint32_t idx = (uint32_t)s0 + 0xFFFFu - (kx & 0xFFFFu);
-      sm.out[cnt] = ((uint64_t)(kx >> 16) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+    if (G >= 2) { ca += dpp<kDppXor1>(ca); cb += dpp<kDppXor1>(cb); }
+    if (G >= 4) { ca += dpp<kDppXor2>(ca); cb += dpp<kDppXor2>(cb); }
+    if (G >= 8) { ca += lane_xor<4>(ca); cb += lane_xor<4>(cb); }
+    if (G >= 16) { ca += lane_xor<8>(ca); cb += lane_xor<8>(cb); }
+    if (g < ng && seg == 0) {
+      if ((int)ca < K) sm.out[ca] = out64(ka);
+      if (xb < ns && (int)cb < K) sm.out[cb] = out64(kb);
     }
   }
   for (int i = ns + tid; i < K; i += kT) sm.out[i] = 0ull;
@@ -271,22 +282,35 @@ __device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
   __syncthreads();
   if (bound_ok) {
     const int nh = min(sm.misc[5], kHitCap);
-    for (int t = tid; t < nh * EPV; t += kT) {
-      const int hv = t / EPV, e = t - hv * EPV;
-      const int idx = sm.hitid[hv] + e;
-      const uint32_t kk = Tr::key(Tr::raw(sm.hitq[hv], e));
-      const bool sv = idx < s1 && kk >= T;
-      const uint64_t bal = __builtin_amdgcn_ballot_w64(sv);
+    // two elements a thread per pass, both read before either is used: one
+    // pass covers up to 256 hit vectors
+    for (int t0 = tid; t0 < nh * EPV; t0 += 2 * kT) {
+      bool sv[2];
+      uint32_t kk[2];
+      int idx[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t = t0 + u * kT;
+        const int hv = min(t, nh * EPV - 1) / EPV, e = t - hv * EPV;
+        idx[u] = sm.hitid[hv] + e;
+        kk[u] = Tr::key(Tr::raw(sm.hitq[hv], e & (EPV - 1)));
+        sv[u] = t < nh * EPV && idx[u] < s1 && kk[u] >= T;
+      }
+      const uint64_t b0 = __builtin_amdgcn_ballot_w64(sv[0]), b1 = __builtin_amdgcn_ballot_w64(sv[1]);
+      const int n0 = __popcll(b0), n01 = n0 + __popcll(b1);
       int base = 0;
-      if (lane == 0 && bal) base = atomicAdd(&sm.misc[3], __popcll(bal));
+      if (lane == 0 && n01) base = atomicAdd(&sm.misc[3], n01);
       base = __builtin_amdgcn_readfirstlane(base);
-      if (sv) {
-        const int p = base + (int)mbcnt64(bal);
-        if (p < kScanCap) {
-          if constexpr (BF16)
-            sm.key32[p] = (kk << 16) | (0xFFFFu - (uint32_t)(idx - s0));
-          else
-            sm.key[p] = ((uint64_t)kk << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (sv[u]) {
+          const int p = base + (u ? n0 : 0) + (int)mbcnt64(u ? b1 : b0);
+          if (p < kScanCap) {
+            if constexpr (BF16)
+              sm.key32[p] = (kk[u] << 16) | (0xFFFFu - (uint32_t)(idx[u] - s0));
+            else
+              sm.key[p] = ((uint64_t)kk[u] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx[u]);
+          }
         }
       }
     }
@@ -368,8 +392,8 @@ __device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
     ns = sm.misc[3];
     if constexpr (BF16) {
       // keys of the overflowed pass may remain past ns: the ranking reads up
-      // to 16 keys beyond ns and needs zeros there
-      if (tid < 16) sm.key32[ns + tid] = 0u;
+      // to 32 keys beyond ns and needs zeros there
+      if (tid < 32) sm.key32[ns + tid] = 0u;
       __syncthreads();
     }
   }
@@ -455,7 +479,7 @@ __global__ __launch_bounds__(kT) void scan_kernel(ScanArgs a) {
   if (b < a.n_scan) {
     if (threadIdx.x < 8) smem.scan.misc[threadIdx.x] = 0;
     if (BF16)
-      for (int i = threadIdx.x; i < kScanCap + 16; i += kT) smem.scan.key32[i] = 0u;
+      for (int i = threadIdx.x; i < kScanCap + 32; i += kT) smem.scan.key32[i] = 0u;
     __syncthreads();
     scan_block<BF16, NV>(a, smem.scan, b);
   } else if (b < a.n_scan + a.n_head) {
