@@ -541,4 +541,102 @@ __device__ __forceinline__ int block_select(const uint64_t (&k)[EPT], const int 
   return select_rank(ns, K, sm);
 }
 
+// ---------------------------------------------------------------------------
+// Sorted top-K by a value histogram, for K in the hundreds.
+//
+// Keys are unique and nonzero, 64-bit, with the value key in the high word.
+// Only keys whose value key is >= lo_v take part; hi_v is >= every such value
+// key. Each key falls in bin (value key - lo_v) >> shift, shift chosen so
+// that hi_v lands in bin 255 or lower. The binning is monotone in the key, so
+// counting down from the top bin finds the boundary bin b*: fewer than K keys
+// lie above it and at least K at or above it (all keys when fewer than K take
+// part). The keys of bin b* and above are scattered into buckets (one per
+// bin, at its offset among the keys above), and each key is placed at its
+// bucket's offset plus its rank within the bucket, counted against the
+// bucket's other keys. Buckets hold one value each when the values span fewer
+// than 256 keys, so the counting is short; the positions below K are the K
+// largest keys in descending order. Out of the K slots, those past the number
+// of keys taking part are zero.
+//
+// hist and cursor must be zero on entry. Returns false, with only hist,
+// cursor, base and misc written, when the keys of bin b* and above exceed cap
+// (massive ties); the caller then selects by another route.
+// ---------------------------------------------------------------------------
+struct HistSmem {
+  LDS int* hist;         // [256]
+  LDS int* cursor;       // [256]
+  LDS int* base;         // [256]
+  LDS int* misc;         // [2]
+  LDS uint64_t* bucket;  // [cap]
+  LDS uint64_t* out;     // [>= K]
+  int cap;
+};
+
+template <int EPT>
+__device__ __forceinline__ bool hist_topk(const uint64_t (&k)[EPT], uint32_t lo_v, uint32_t hi_v, int K,
+                                          const HistSmem& sm) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const uint32_t span = hi_v > lo_v ? hi_v - lo_v : 0u;
+  const int nb = span ? 32 - __builtin_clz(span) : 0;
+  const int shift = nb > 8 ? nb - 8 : 0;
+  int bin[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const uint32_t hv = (uint32_t)(k[e] >> 32);
+    bin[e] = (k[e] != 0ull && hv >= lo_v) ? (int)min(255u, (hv - lo_v) >> shift) : -1;
+    if (bin[e] >= 0) lds_add(&sm.hist[bin[e]], 1);
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    // lane l holds bins 255 - 4l .. 252 - 4l, so lanes run from the top bin down
+    const int b0 = 255 - 4 * tid;
+    const int h0 = sm.hist[b0], h1 = sm.hist[b0 - 1], h2 = sm.hist[b0 - 2], h3 = sm.hist[b0 - 3];
+    const int s = h0 + h1 + h2 + h3;
+    int inc = s;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int t = __shfl_up(inc, d);
+      if (tid >= d) inc += t;
+    }
+    const int a0 = inc - s, a1 = a0 + h0, a2 = a1 + h1, a3 = a2 + h2;
+    const int total = __shfl(inc, kWave - 1);
+    const int kk = min(K, total);
+    sm.base[b0] = a0;
+    sm.base[b0 - 1] = a1;
+    sm.base[b0 - 2] = a2;
+    sm.base[b0 - 3] = a3;
+    if (kk == 0) {
+      if (tid == 0) { sm.misc[0] = 256; sm.misc[1] = 0; }
+    } else {
+      // exactly one bin has above < kk <= above + count
+      if (a0 < kk && kk <= a1) { sm.misc[0] = b0; sm.misc[1] = a1; }
+      if (a1 < kk && kk <= a2) { sm.misc[0] = b0 - 1; sm.misc[1] = a2; }
+      if (a2 < kk && kk <= a3) { sm.misc[0] = b0 - 2; sm.misc[1] = a3; }
+      if (a3 < kk && kk <= a3 + h3) { sm.misc[0] = b0 - 3; sm.misc[1] = a3 + h3; }
+    }
+  }
+  __syncthreads();
+  const int bstar = sm.misc[0], narea = sm.misc[1];
+  if (narea > sm.cap) return false;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    if (bin[e] >= bstar) {
+      const int slot = lds_add(&sm.cursor[bin[e]], 1);
+      sm.bucket[sm.base[bin[e]] + slot] = k[e];
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < narea; p += nthr) {
+    const uint64_t x = sm.bucket[p];
+    const int b = (int)min(255u, ((uint32_t)(x >> 32) - lo_v) >> shift);
+    const int lo = sm.base[b], hi = lo + sm.hist[b];
+    int r = 0;
+    for (int q = lo; q < hi; ++q) r += sm.bucket[q] > x ? 1 : 0;
+    if (lo + r < K) sm.out[lo + r] = x;
+  }
+  for (int i = narea + tid; i < K; i += nthr) sm.out[i] = 0ull;
+  __syncthreads();
+  return true;
+}
+
 }  // namespace dartree

@@ -31,6 +31,7 @@ constexpr size_t kAFragBytes = (size_t)256 * 256 * 2;  // one fp16 copy of A
 struct ScanPlan {
   int S, slice, nv, n_scan, merge_ept;
   size_t list_bytes;
+  bool wide;   // K > 64: the wide selection (histogram-ordered survivors)
   bool ok;
 };
 ScanPlan scan_plan(int rows, int V, int K, bool bf16);

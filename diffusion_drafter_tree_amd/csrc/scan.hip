@@ -54,6 +54,37 @@ union KernelSmem {
   HeadSmem head;
 };
 
+// Wide variant (K > 64): larger hit queue and survivor list; the hit queue's
+// space is reused for the histogram selection's buckets and output once the
+// queued vectors have been checked.
+constexpr int kHitCapW = 2048;
+constexpr int kSurvW = 4096;   // 32-bit survivor keys (bf16); half as many 64-bit keys (fp32)
+struct WideSmem {
+  union {
+    struct {
+      u32x4_t hitq[kHitCapW];
+      int hitid[kHitCapW];
+    };
+    struct {
+      uint64_t bucket[kSurvW];
+      uint64_t out[1024];
+    };
+  };
+  union {
+    uint32_t key32[kSurvW + 32];
+    uint64_t key[kSurvW / 2 + 8];
+  };
+  int hist[256];
+  int cursor[256];
+  int base[256];
+  int misc[8];
+  int wsum[kWaves];
+};
+union WideKernelSmem {
+  WideSmem scan;
+  HeadSmem head;
+};
+
 template <bool BF16>
 struct Traits;
 template <>
@@ -94,7 +125,8 @@ struct Traits<false> {
 };
 
 // Block-wide sum of an int (every thread gets the total). Two barriers.
-__device__ int block_sum(ScanSmem& sm, int v) {
+template <class Smem>
+__device__ int block_sum(Smem& sm, int v) {
   const int w = threadIdx.x / kWave;
   const int s = wave_sum_i32(v);
   if (lane_id() == 0) sm.wsum[w] = s;
@@ -186,9 +218,11 @@ __device__ void rank_select32(ScanSmem& sm, int ns, int K, int s0) {
   __syncthreads();
 }
 
-template <bool BF16, int NV>
-__device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
+template <bool BF16, int NV, bool WIDE, class Smem>
+__device__ void scan_block(const ScanArgs& a, Smem& sm, int blk) {
   using Tr = Traits<BF16>;
+  constexpr int HCAP = WIDE ? kHitCapW : kHitCap;
+  constexpr int SCAP = WIDE ? (BF16 ? kSurvW : kSurvW / 2) : kScanCap;
   constexpr int EPV = Tr::EPV;
   constexpr int ESZ = 16 / EPV;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
@@ -239,6 +273,11 @@ __device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
   const int nact = (nthr_valid + kWave - 1) / kWave;
   const int m = nact > 0 ? (K + nact - 1) / nact : K;
   if (nact == 0 && tid == 0) sm.misc[4] = 1;   // empty slice: the exact path yields nothing
+  if (WIDE) {
+    // the slice's largest key bounds the histogram bins of the selection
+    const uint32_t wm = wave_max_u32(lk);
+    if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(&sm.misc[6]), wm);
+  }
   if (w < nact) {
     const bool lv = tid < nthr_valid;
     const int nl = __popcll(__ballot(lv));
@@ -270,7 +309,7 @@ __device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
       for (int it = 0; it < NV; ++it) {
         if (vk[it] >= T) {
           const int hv = base + (int)mbcnt64(bal[it]);
-          if (hv < kHitCap) {
+          if (hv < HCAP) {
             sm.hitq[hv] = q[it];
             sm.hitid[hv] = id0(it);
           }
@@ -281,7 +320,7 @@ __device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
   }
   __syncthreads();
   if (bound_ok) {
-    const int nh = min(sm.misc[5], kHitCap);
+    const int nh = min(sm.misc[5], HCAP);
     // two elements a thread per pass, both read before either is used: one
     // pass covers up to 256 hit vectors
     for (int t0 = tid; t0 < nh * EPV; t0 += 2 * kT) {
@@ -305,7 +344,7 @@ __device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
       for (int u = 0; u < 2; ++u) {
         if (sv[u]) {
           const int p = base + (u ? n0 : 0) + (int)mbcnt64(u ? b1 : b0);
-          if (p < kScanCap) {
+          if (p < SCAP) {
             if constexpr (BF16)
               sm.key32[p] = (kk[u] << 16) | (0xFFFFu - (uint32_t)(idx[u] - s0));
             else
@@ -317,7 +356,8 @@ __device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
   }
   __syncthreads();
   int ns = sm.misc[3];
-  if (!bound_ok || sm.misc[5] > kHitCap || ns > kScanCap) {
+  uint32_t lo_v = T;   // every survivor's value key is >= lo_v
+  if (!bound_ok || sm.misc[5] > HCAP || ns > SCAP) {
     // -- exact path: Th = K-th largest key (bitwise search on block counts),
     //    then among keys == Th the largest complemented ids (lowest ids)
     int nvalid = 0;
@@ -344,6 +384,7 @@ __device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
       for (int e = 0; e < EPV; ++e) ngt += (e0 + e < s1 && Tr::key(Tr::raw(q[it], e)) > Th) ? 1 : 0;
     }
     const int take = need - block_sum(sm, ngt);   // ties at Th to take, lowest ids first
+    lo_v = Th;
     uint32_t Ui = 0;
     for (int b = 31; b >= 0; --b) {
       const uint32_t cand = Ui | (1u << b);
@@ -397,10 +438,34 @@ __device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
       __syncthreads();
     }
   }
-  if constexpr (BF16)
+  if constexpr (WIDE) {
+    // survivors, as 64-bit keys, ordered by the value histogram (ns <= the
+    // bucket space, so the selection cannot run out of room)
+    uint64_t kr[kSurvW / kT];
+#pragma unroll
+    for (int e = 0; e < kSurvW / kT; ++e) {
+      const int i = tid + e * kT;
+      uint64_t x = 0ull;
+      if (i < ns) {
+        if constexpr (BF16) {
+          const uint32_t k32 = sm.key32[i];
+          const uint32_t idx = (uint32_t)s0 + 0xFFFFu - (k32 & 0xFFFFu);
+          x = ((uint64_t)(k32 >> 16) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+        } else {
+          x = sm.key[i];
+        }
+      }
+      kr[e] = x;
+    }
+    HistSmem hs{(LDS int*)sm.hist, (LDS int*)sm.cursor, (LDS int*)sm.base, (LDS int*)&sm.misc[0],
+                (LDS uint64_t*)sm.bucket, (LDS uint64_t*)sm.out, kSurvW};
+    __syncthreads();   // misc[0..1] and the hit queue's space are reused
+    hist_topk<kSurvW / kT>(kr, lo_v, (uint32_t)sm.misc[6], K, hs);
+  } else if constexpr (BF16) {
     rank_select32(sm, ns, K, s0);
-  else
+  } else {
     rank_select(sm, ns, K);
+  }
   if (a.S == 1) {
     int32_t* ids = a.cand_ids + (size_t)row * K;
     float* vals = a.cand_logit + (size_t)row * K;
@@ -415,6 +480,7 @@ __device__ void scan_block(const ScanArgs& a, ScanSmem& sm, int blk) {
   }
 }
 
+template <int G>
 __device__ void head_block(const ScanArgs& a, HeadSmem& sm, int tile) {
   const int lane = lane_id(), w = threadIdx.x / kWave;
   const int ntn = a.r / 16;
@@ -427,7 +493,6 @@ __device__ void head_block(const ScanArgs& a, HeadSmem& sm, int tile) {
   const uint16_t* hrow = a.H + (size_t)(m < a.M ? m : 0) * a.D + sub;
   const uint16_t* prow = a.Pt + (size_t)n * a.D + sub;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int G = 8;
   for (int kb = k0; kb < k1; kb += G) {
     u16x8_t av[G], bv[G];
 #pragma unroll
@@ -481,15 +546,41 @@ __global__ __launch_bounds__(kT) void scan_kernel(ScanArgs a) {
     if (BF16)
       for (int i = threadIdx.x; i < kScanCap + 32; i += kT) smem.scan.key32[i] = 0u;
     __syncthreads();
-    scan_block<BF16, NV>(a, smem.scan, b);
+    scan_block<BF16, NV, false>(a, smem.scan, b);
   } else if (b < a.n_scan + a.n_head) {
-    head_block(a, smem.head, b - a.n_scan);
+    head_block<8>(a, smem.head, b - a.n_scan);
+  } else {
+    afrag_block(a, b - a.n_scan - a.n_head);
+  }
+}
+
+// The same launch for K > 64, with the wide selection; two workgroups fit a
+// CU (<= 64 VGPRs, ~60 KB of LDS), so one's selection overlaps the other's
+// loads when rows outnumber the CUs.
+template <bool BF16, int NV>
+__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8))) void scan_wide_kernel(ScanArgs a) {
+  __shared__ WideKernelSmem smem;
+  const int b = blockIdx.x;
+  if (b < a.n_scan) {
+    if (threadIdx.x < 8) smem.scan.misc[threadIdx.x] = 0;
+    for (int i = threadIdx.x; i < 256; i += kT) {
+      smem.scan.hist[i] = 0;
+      smem.scan.cursor[i] = 0;
+    }
+    __syncthreads();
+    scan_block<BF16, NV, true>(a, smem.scan, b);
+  } else if (b < a.n_scan + a.n_head) {
+    head_block<4>(a, smem.head, b - a.n_scan);
   } else {
     afrag_block(a, b - a.n_scan - a.n_head);
   }
 }
 
 // Per-row merge of S sorted slice lists (used when a row spans several slices).
+// Every slice holds K keys at or above its K-th, so the row's K-th largest
+// value is at least the largest of the slices' K-th values: that value and the
+// largest head bound the histogram selection. Massive ties fall back to the
+// bound-and-rank selection.
 template <int EPT>
 __global__ __launch_bounds__(kT) void merge_kernel(const uint64_t* __restrict__ lists, int S, int K, bool bf16,
                                                    int32_t* __restrict__ cand_ids, float* __restrict__ cand_logit) {
@@ -499,11 +590,21 @@ __global__ __launch_bounds__(kT) void merge_kernel(const uint64_t* __restrict__ 
   __shared__ uint64_t s_out[1024];
   __shared__ int s_outp[1024];
   __shared__ int s_misc[8];
+  __shared__ int s_hist[256], s_cursor[256], s_base[256], s_hmisc[2];
   const int row = blockIdx.x, tid = threadIdx.x;
   if (tid < 8) s_misc[tid] = 0;
   for (int i = tid; i < kScanCap; i += kT) s_rank[i] = 0;
+  for (int i = tid; i < 256; i += kT) {
+    s_hist[i] = 0;
+    s_cursor[i] = 0;
+  }
   __syncthreads();
   const uint64_t* L = lists + (size_t)row * S * K;
+  uint32_t lo_v = 0u, hi_v = 0u;
+  for (int sl = 0; sl < S; ++sl) {
+    hi_v = max(hi_v, (uint32_t)(L[(size_t)sl * K] >> 32));
+    lo_v = max(lo_v, (uint32_t)(L[(size_t)sl * K + K - 1] >> 32));
+  }
   uint64_t k[EPT];
   int p[EPT];
 #pragma unroll
@@ -512,9 +613,13 @@ __global__ __launch_bounds__(kT) void merge_kernel(const uint64_t* __restrict__ 
     k[e] = i < S * K ? L[i] : 0ull;
     p[e] = 0;
   }
-  SelSmem sm{(LDS uint64_t*)s_key, (LDS int*)s_pay, (LDS int*)s_rank, (LDS uint64_t*)s_out, (LDS int*)s_outp,
-             (LDS int*)s_misc, kScanCap};
-  block_select<EPT>(k, p, K, bf16 ? 16 : 32, sm);
+  HistSmem hs{(LDS int*)s_hist, (LDS int*)s_cursor, (LDS int*)s_base, (LDS int*)s_hmisc, (LDS uint64_t*)s_key,
+              (LDS uint64_t*)s_out, kScanCap};
+  if (!hist_topk<EPT>(k, lo_v, hi_v, K, hs)) {
+    SelSmem sm{(LDS uint64_t*)s_key, (LDS int*)s_pay, (LDS int*)s_rank, (LDS uint64_t*)s_out, (LDS int*)s_outp,
+               (LDS int*)s_misc, kScanCap};
+    block_select<EPT>(k, p, K, bf16 ? 16 : 32, sm);
+  }
   for (int i = tid; i < K; i += kT) {
     const uint64_t x = s_out[i];
     cand_ids[(size_t)row * K + i] = x ? (int32_t)(0xFFFFFFFFu - (uint32_t)x) : -1;
@@ -558,6 +663,7 @@ ScanPlan scan_plan(int rows, int V, int K, bool bf16) {
   p.n_scan = rows * p.S;
   p.merge_ept = (p.S * K + kT - 1) / kT <= 8 ? 8 : 16;
   p.list_bytes = p.S > 1 ? (size_t)rows * p.S * K * sizeof(uint64_t) : 0;
+  p.wide = K > 64;
   p.ok = p.nv >= 1 && p.nv <= kMaxNV && (long long)p.S * K <= 16LL * kT;
   return p;
 }
@@ -573,7 +679,13 @@ hipError_t launch_scan(const ScanPlan& p, bool bf16, const ScanArgs& args_in, hi
   a.n_scan = p.n_scan;
   const int grid = a.n_scan + a.n_head + a.n_afrag;
   if (grid == 0) return hipSuccess;
-#define DT_SCAN(B, NVV) hipLaunchKernelGGL((scan_kernel<B, NVV>), dim3(grid), dim3(kT), 0, s, a)
+#define DT_SCAN(B, NVV)                                                                  \
+  do {                                                                                    \
+    if (p.wide)                                                                           \
+      hipLaunchKernelGGL((scan_wide_kernel<B, NVV>), dim3(grid), dim3(kT), 0, s, a);      \
+    else                                                                                  \
+      hipLaunchKernelGGL((scan_kernel<B, NVV>), dim3(grid), dim3(kT), 0, s, a);           \
+  } while (0)
   switch (p.nv) {
     case 1: if (bf16) DT_SCAN(true, 1); else DT_SCAN(false, 1); break;
     case 2: if (bf16) DT_SCAN(true, 2); else DT_SCAN(false, 2); break;
