@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--graph-rounds", type=int, default=16, help="rounds captured per HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-scan-stress", action="store_true",
+                    help="skip the logits scan measured at the 64-request shape (311 MB of logits a round)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="if > 0: run only this many eager rounds (for rocprofv3) and exit")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -225,6 +227,11 @@ def main():
                    "ideal_us_at_hbm_peak": round(ideal_us, 3), "alg_bytes": round_bytes,
                    "round_roofline_frac": round(ideal_us / us_round, 5)}
 
+    # ---- the logits scan where bandwidth decides: 64 requests, K = 512 ----------
+    scan_stress = None
+    if not args.no_scan_stress:
+        scan_stress = scan_at_stress_shape(HBM_PEAK)
+
     # ---- CPU oracle baseline on a bounded sample -------------------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -250,6 +257,7 @@ def main():
                    "global_batch": n, "parallelism": "single GPU"},
         "roofline": roofline,
         "roofline_scan": roofline_scan,
+        "roofline_scan_stress": scan_stress,
         "kernels": kernels,
         "stage_timing": event_kind,
         "plan": info,
@@ -292,6 +300,63 @@ def measured_traffic(cfg_name):
         if h.hexdigest()[:16] == rec[k]["src_sha256"]:
             out[k] = rec[k]["bytes"]
     return out
+
+
+def scan_at_stress_shape(hbm_peak, n_timed=16):
+    """a1 alone (dartree_topk_candidates: the scan launch, then the slice-list
+    merge) at the stress_64req shape: 1024 rows of V = 151936 bf16 logits,
+    K = 512. Two distinct device-resident rounds (622 MB, over twice the
+    Infinity Cache) alternate. Each call's scan and merge launches are timed by
+    the library's stage events. A device-to-device copy of one round's logits
+    is timed beside it as the achievable-bandwidth reference."""
+    import numpy as np
+    import torch
+
+    from diffusion_drafter_tree_amd import inputs as I
+    from diffusion_drafter_tree_amd import ops
+
+    cfg = I.CONFIGS["stress_64req"]
+    lg = [ops.to_device(I.make_round(cfg, 0, t).logits) for t in range(2)]
+    rb = ops.RoundBuffers(cfg)
+    dims = rb.dims
+    info = ops.round_plan(dims)
+    for t in range(4):
+        ops.topk_candidates(dims, lg[t % 2], rb.cand_ids, rb.cand_logit, rb.ws)
+    torch.cuda.synchronize()
+    hev = StageEvents(n_timed * 4)
+    for t in range(n_timed):
+        hev.set(t)
+        ops.topk_candidates(dims, lg[t % 2], rb.cand_ids, rb.cand_logit, rb.ws)
+    ops.set_stage_events(None)
+    torch.cuda.synchronize()
+    scan_us = float(np.mean([hev.elapsed_us(t, 0, 1) for t in range(n_timed)]))
+    merge_us = float(np.mean([hev.elapsed_us(t, 1, 2) for t in range(n_timed)]))
+    hev.close()
+    # reference: copy of one round's logits (bytes read + bytes written)
+    dst = torch.empty_like(lg[0])
+    for _ in range(3):
+        dst.copy_(lg[1])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for t in range(8):
+        dst.copy_(lg[t % 2])
+    e1.record()
+    torch.cuda.synchronize()
+    nbytes = lg[0].numel() * lg[0].element_size()
+    copy_us = e0.elapsed_time(e1) * 1000.0 / 8
+    rows = cfg.n_req * cfg.L
+    S = info["scan_slices"]
+    lists = rows * S * cfg.K * 8 if S > 1 else rows * cfg.K * 8
+    alg = nbytes + lists   # logits read once, the slice lists written
+    gbs = alg / (scan_us * 1e-6) / 1e9
+    return {"kernel": "scan_wide_kernel (logits scan, histogram-ordered selection)", "bound": "hbm",
+            "workload": f"stress_64req logits: {rows} rows x V={cfg.V} bf16, K={cfg.K}, {S} slices a row",
+            "achieved": round(gbs, 1), "peak": hbm_peak, "unit": "GB/s", "frac": round(gbs / hbm_peak, 4),
+            "us": round(scan_us, 2), "alg_bytes": alg, "merge_us": round(merge_us, 2),
+            "topk_us": round(scan_us + merge_us, 2),
+            "copy_ref_GB_s": round(2 * nbytes / (copy_us * 1e-6) / 1e9, 1),
+            "copy_ref_frac": round(2 * nbytes / (copy_us * 1e-6) / 1e9 / hbm_peak, 4)}
 
 
 class StageEvents:

@@ -317,10 +317,13 @@ dartree_status dartree_topk_candidates(const dartree_dims* dims, const void* log
   sa.cand_ids = cand_ids;
   sa.cand_logit = cand_logit;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  stage_mark(0, s);
   hipError_t e = dartree::launch_scan(w.plan, bf, sa, s);
   if (e != hipSuccess) return hip_fail(e, "scan launch");
+  stage_mark(1, s);
   e = dartree::launch_merge(w.plan, rows, dims->K, bf, sa.lists, cand_ids, cand_logit, s);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
+  stage_mark(2, s);
   return DARTREE_OK;
 }
 

@@ -312,6 +312,28 @@ __device__ __forceinline__ uint32_t wave_mth_largest(uint32_t v, bool valid, int
   return t;
 }
 
+// The same through the 64-lane sort network (21 DPP / permlane stages, no
+// SALU round trips), for m above 8. All 64 lanes must be active.
+__device__ __forceinline__ uint32_t wave_mth_largest_sorted(uint32_t v, bool valid, int m) {
+  uint32_t k = valid ? v : 0u;
+  wave_sort_desc32(k);
+  return readlane(k, m - 1);
+}
+
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4 and 8 inside each
+// 16-lane row (lanes without a source add zero), then row 0's total into row
+// 1 and row 1's into rows 2 and 3 (row_bcast:15), then row 1's running total
+// into rows 2 and 3 (row_bcast:31). All 64 lanes must be active.
+__device__ __forceinline__ int wave_incl_scan_i32(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
 // two fp32 values to fp16, rounding toward zero (v_cvt_pkrtz_f16_f32)
 __device__ __forceinline__ h16x2_t pkrtz(float a, float b) {
   typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
@@ -558,7 +580,9 @@ __device__ __forceinline__ int block_select(const uint64_t (&k)[EPT], const int 
 // largest keys in descending order. Out of the K slots, those past the number
 // of keys taking part are zero.
 //
-// hist and cursor must be zero on entry. Returns false, with only hist,
+// Its barriers wait for LDS traffic only (outstanding global loads, e.g. a
+// prefetch into registers, stay in flight). hist and cursor must be zero on
+// entry. Returns false, with only hist,
 // cursor, base and misc written, when the keys of bin b* and above exceed cap
 // (massive ties); the caller then selects by another route.
 // ---------------------------------------------------------------------------
@@ -586,20 +610,15 @@ __device__ __forceinline__ bool hist_topk(const uint64_t (&k)[EPT], uint32_t lo_
     bin[e] = (k[e] != 0ull && hv >= lo_v) ? (int)min(255u, (hv - lo_v) >> shift) : -1;
     if (bin[e] >= 0) lds_add(&sm.hist[bin[e]], 1);
   }
-  __syncthreads();
+  lds_sync();
   if (tid < kWave) {
     // lane l holds bins 255 - 4l .. 252 - 4l, so lanes run from the top bin down
     const int b0 = 255 - 4 * tid;
     const int h0 = sm.hist[b0], h1 = sm.hist[b0 - 1], h2 = sm.hist[b0 - 2], h3 = sm.hist[b0 - 3];
     const int s = h0 + h1 + h2 + h3;
-    int inc = s;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int t = __shfl_up(inc, d);
-      if (tid >= d) inc += t;
-    }
+    const int inc = wave_incl_scan_i32(s);
     const int a0 = inc - s, a1 = a0 + h0, a2 = a1 + h1, a3 = a2 + h2;
-    const int total = __shfl(inc, kWave - 1);
+    const int total = (int)readlane((uint32_t)inc, kWave - 1);
     const int kk = min(K, total);
     sm.base[b0] = a0;
     sm.base[b0 - 1] = a1;
@@ -615,7 +634,7 @@ __device__ __forceinline__ bool hist_topk(const uint64_t (&k)[EPT], uint32_t lo_
       if (a3 < kk && kk <= a3 + h3) { sm.misc[0] = b0 - 3; sm.misc[1] = a3 + h3; }
     }
   }
-  __syncthreads();
+  lds_sync();
   const int bstar = sm.misc[0], narea = sm.misc[1];
   if (narea > sm.cap) return false;
 #pragma unroll
@@ -625,17 +644,21 @@ __device__ __forceinline__ bool hist_topk(const uint64_t (&k)[EPT], uint32_t lo_
       sm.bucket[sm.base[bin[e]] + slot] = k[e];
     }
   }
-  __syncthreads();
+  lds_sync();
   for (int p = tid; p < narea; p += nthr) {
     const uint64_t x = sm.bucket[p];
     const int b = (int)min(255u, ((uint32_t)(x >> 32) - lo_v) >> shift);
     const int lo = sm.base[b], hi = lo + sm.hist[b];
-    int r = 0;
-    for (int q = lo; q < hi; ++q) r += sm.bucket[q] > x ? 1 : 0;
+    int r = 0, q = lo;
+    for (; q + 4 <= hi; q += 4) {
+      const uint64_t y0 = sm.bucket[q], y1 = sm.bucket[q + 1], y2 = sm.bucket[q + 2], y3 = sm.bucket[q + 3];
+      r += (y0 > x ? 1 : 0) + (y1 > x ? 1 : 0) + (y2 > x ? 1 : 0) + (y3 > x ? 1 : 0);
+    }
+    for (; q < hi; ++q) r += sm.bucket[q] > x ? 1 : 0;
     if (lo + r < K) sm.out[lo + r] = x;
   }
   for (int i = narea + tid; i < K; i += nthr) sm.out[i] = 0ull;
-  __syncthreads();
+  lds_sync();
   return true;
 }
 

@@ -54,34 +54,40 @@ union KernelSmem {
   HeadSmem head;
 };
 
-// Wide variant (K > 64): larger hit queue and survivor list; the hit queue's
-// space is reused for the histogram selection's buckets and output once the
-// queued vectors have been checked.
-constexpr int kHitCapW = 2048;
-constexpr int kSurvW = 4096;   // 32-bit survivor keys (bf16); half as many 64-bit keys (fp32)
+// Wide variant (K > 64), NT threads a workgroup: the hit queue holds 2 NT
+// vectors and the survivor list 4 NT 32-bit keys (bf16; half as many 64-bit
+// keys for fp32); the hit queue's space is reused for the histogram
+// selection's buckets and output once the queued vectors have been checked.
+#ifndef DARTREE_WIDE_NT
+#define DARTREE_WIDE_NT 1024
+#endif
+constexpr int kWideT = DARTREE_WIDE_NT;
+template <int NT>
 struct WideSmem {
+  static constexpr int kHit = 2 * NT, kSurv = 4 * NT;
   union {
     struct {
-      u32x4_t hitq[kHitCapW];
-      int hitid[kHitCapW];
+      u32x4_t hitq[kHit];
+      int hitid[kHit];
     };
     struct {
-      uint64_t bucket[kSurvW];
+      uint64_t bucket[kSurv];
       uint64_t out[1024];
     };
   };
   union {
-    uint32_t key32[kSurvW + 32];
-    uint64_t key[kSurvW / 2 + 8];
+    uint32_t key32[kSurv + 32];
+    uint64_t key[kSurv / 2 + 8];
   };
   int hist[256];
   int cursor[256];
   int base[256];
   int misc[8];
-  int wsum[kWaves];
+  int wsum[NT / kWave];
 };
+template <int NT>
 union WideKernelSmem {
-  WideSmem scan;
+  WideSmem<NT> scan;
   HeadSmem head;
 };
 
@@ -127,6 +133,7 @@ struct Traits<false> {
 // Block-wide sum of an int (every thread gets the total). Two barriers.
 template <class Smem>
 __device__ int block_sum(Smem& sm, int v) {
+  constexpr int kWaves = sizeof(sm.wsum) / sizeof(sm.wsum[0]);
   const int w = threadIdx.x / kWave;
   const int s = wave_sum_i32(v);
   if (lane_id() == 0) sm.wsum[w] = s;
@@ -218,24 +225,20 @@ __device__ void rank_select32(ScanSmem& sm, int ns, int K, int s0) {
   __syncthreads();
 }
 
-template <bool BF16, int NV, bool WIDE, class Smem>
-__device__ void scan_block(const ScanArgs& a, Smem& sm, int blk) {
+// The slice blk of the logits into q: at most kMaxNV 16-byte vectors per
+// thread; absent elements get the lowest key.
+template <bool BF16, int NV, int kT>
+__device__ __forceinline__ void load_slice(const ScanArgs& a, int blk, u32x4_t (&q)[NV]) {
   using Tr = Traits<BF16>;
-  constexpr int HCAP = WIDE ? kHitCapW : kHitCap;
-  constexpr int SCAP = WIDE ? (BF16 ? kSurvW : kSurvW / 2) : kScanCap;
   constexpr int EPV = Tr::EPV;
   constexpr int ESZ = 16 / EPV;
-  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int tid = threadIdx.x;
   const int row = blk / a.S, sl = blk - row * a.S;
   const int s0 = sl * a.slice;
   const int s1 = min(a.V, s0 + a.slice);
   const char* rowp = static_cast<const char*>(a.logits) + (size_t)row * (size_t)a.V * ESZ;
   const bool vec_ok = (((uintptr_t)rowp) & 15u) == 0;
-  const int K = a.K;
   auto id0 = [&](int it) { return s0 + (it * kT + tid) * EPV; };
-
-  // -- the slice, at most kMaxNV vectors per thread; absent elements get the lowest key
-  u32x4_t q[NV];
 #pragma unroll
   for (int it = 0; it < NV; ++it) {
     const int e0 = id0(it);
@@ -260,6 +263,22 @@ __device__ void scan_block(const ScanArgs& a, Smem& sm, int blk) {
       q[it] = u32x4_t{wv[0], wv[1], wv[2], wv[3]};
     }
   }
+}
+
+// Top-K of slice blk, whose vectors are in q.
+template <bool BF16, int NV, bool WIDE, int kT, class Smem>
+__device__ void scan_block(const ScanArgs& a, Smem& sm, int blk, const u32x4_t (&q)[NV]) {
+  using Tr = Traits<BF16>;
+  constexpr int kSurvW = 4 * kT;
+  constexpr int HCAP = WIDE ? 2 * kT : kHitCap;
+  constexpr int SCAP = WIDE ? (BF16 ? kSurvW : kSurvW / 2) : kScanCap;
+  constexpr int EPV = Tr::EPV;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int row = blk / a.S, sl = blk - row * a.S;
+  const int s0 = sl * a.slice;
+  const int s1 = min(a.V, s0 + a.slice);
+  const int K = a.K;
+  auto id0 = [&](int it) { return s0 + (it * kT + tid) * EPV; };
   // -- largest key per vector and per lane
   uint32_t vk[NV];
   uint32_t lk = 0u;
@@ -282,7 +301,7 @@ __device__ void scan_block(const ScanArgs& a, Smem& sm, int blk) {
     const bool lv = tid < nthr_valid;
     const int nl = __popcll(__ballot(lv));
     if (nl >= m && m <= kWave) {
-      const uint32_t t = wave_mth_largest(lk, lv, m, Tr::KBITS);
+      const uint32_t t = (WIDE && m > 8) ? wave_mth_largest_sorted(lk, lv, m) : wave_mth_largest(lk, lv, m, Tr::KBITS);
       if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(&sm.misc[2]), ~t);
     } else if (lane == 0) {
       atomicOr(&sm.misc[4], 1);
@@ -319,7 +338,50 @@ __device__ void scan_block(const ScanArgs& a, Smem& sm, int blk) {
     }
   }
   __syncthreads();
-  if (bound_ok) {
+  if (WIDE && bound_ok) {
+    // one thread per queued vector, its elements checked in registers; the
+    // survivors of a wave are placed by a prefix of the per-thread counts
+    // (0..8, four bits, one ballot each) and one LDS atomic
+    const int nh = min(sm.misc[5], HCAP);
+    for (int v0 = 0; v0 < nh; v0 += kT) {
+      const int v = v0 + tid;
+      uint32_t smask = 0u, kk[EPV];
+      int idb = 0;
+      if (v < nh) {
+        const u32x4_t qv = sm.hitq[v];
+        idb = sm.hitid[v];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          kk[e] = Tr::key(Tr::raw(qv, e));
+          smask |= (idb + e < s1 && kk[e] >= T) ? (1u << e) : 0u;
+        }
+      }
+      const uint32_t c = (uint32_t)__popc(smask);
+      uint32_t pre = 0u, tot = 0u;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint64_t bb = __builtin_amdgcn_ballot_w64((c >> b) & 1u);
+        pre += mbcnt64(bb) << b;
+        tot += (uint32_t)__popcll(bb) << b;
+      }
+      int base = 0;
+      if (lane == 0 && tot) base = atomicAdd(&sm.misc[3], (int)tot);
+      base = __builtin_amdgcn_readfirstlane(base);
+      int p = base + (int)pre;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        if ((smask >> e) & 1u) {
+          if (p < SCAP) {
+            if constexpr (BF16)
+              sm.key32[p] = (kk[e] << 16) | (0xFFFFu - (uint32_t)(idb + e - s0));
+            else
+              sm.key[p] = ((uint64_t)kk[e] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(idb + e));
+          }
+          ++p;
+        }
+      }
+    }
+  } else if (bound_ok) {
     const int nh = min(sm.misc[5], HCAP);
     // two elements a thread per pass, both read before either is used: one
     // pass covers up to 256 hit vectors
@@ -459,7 +521,7 @@ __device__ void scan_block(const ScanArgs& a, Smem& sm, int blk) {
     }
     HistSmem hs{(LDS int*)sm.hist, (LDS int*)sm.cursor, (LDS int*)sm.base, (LDS int*)&sm.misc[0],
                 (LDS uint64_t*)sm.bucket, (LDS uint64_t*)sm.out, kSurvW};
-    __syncthreads();   // misc[0..1] and the hit queue's space are reused
+    lds_sync();   // misc[0..1] and the hit queue's space are reused
     hist_topk<kSurvW / kT>(kr, lo_v, (uint32_t)sm.misc[6], K, hs);
   } else if constexpr (BF16) {
     rank_select32(sm, ns, K, s0);
@@ -480,7 +542,7 @@ __device__ void scan_block(const ScanArgs& a, Smem& sm, int blk) {
   }
 }
 
-template <int G>
+template <int G, int kWaves>
 __device__ void head_block(const ScanArgs& a, HeadSmem& sm, int tile) {
   const int lane = lane_id(), w = threadIdx.x / kWave;
   const int ntn = a.r / 16;
@@ -529,7 +591,7 @@ __device__ void head_block(const ScanArgs& a, HeadSmem& sm, int tile) {
 // (wave, tile, k-step) so the tree kernel reads 1 KB runs.
 __device__ void afrag_block(const ScanArgs& a, int tw) {
   const int hk = tw >> 3, aw = tw & 7;
-  for (int v = threadIdx.x; v < 2 * 4 * kWave; v += kT) {
+  for (int v = threadIdx.x; v < 2 * 4 * kWave; v += blockDim.x) {
     const int t = v >> 8, kl = (v >> 6) & 3, l = v & 63;
     const int row = aw * 32 + t * 16 + (l & 15), col = (hk * 4 + kl) * 32 + (l >> 4) * 8;
     const u16x8_t x = *reinterpret_cast<const u16x8_t*>(a.A + (size_t)row * 256 + col);
@@ -546,33 +608,45 @@ __global__ __launch_bounds__(kT) void scan_kernel(ScanArgs a) {
     if (BF16)
       for (int i = threadIdx.x; i < kScanCap + 32; i += kT) smem.scan.key32[i] = 0u;
     __syncthreads();
-    scan_block<BF16, NV, false>(a, smem.scan, b);
+    u32x4_t q[NV];
+    load_slice<BF16, NV, kT>(a, b, q);
+    scan_block<BF16, NV, false, kT>(a, smem.scan, b, q);
   } else if (b < a.n_scan + a.n_head) {
-    head_block<8>(a, smem.head, b - a.n_scan);
+    head_block<8, kWaves>(a, smem.head, b - a.n_scan);
   } else {
     afrag_block(a, b - a.n_scan - a.n_head);
   }
 }
 
-// The same launch for K > 64, with the wide selection; two workgroups fit a
+// The same launch for K > 64, with the wide selection: two workgroups fit a
 // CU (<= 64 VGPRs, ~60 KB of LDS), so one's selection overlaps the other's
-// loads when rows outnumber the CUs.
+// loads when rows outnumber the CUs. The head tiles are spread evenly over
+// the grid (block b is a head tile when floor((b + 1) n_head / total) steps
+// up), so their MFMA and cache traffic overlaps the scan's HBM reads
+// instead of trailing it.
 template <bool BF16, int NV>
-__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8))) void scan_wide_kernel(ScanArgs a) {
-  __shared__ WideKernelSmem smem;
+__global__ __launch_bounds__(kWideT) __attribute__((amdgpu_waves_per_eu(8))) void scan_wide_kernel(ScanArgs a) {
+  __shared__ WideKernelSmem<kWideT> smem;
   const int b = blockIdx.x;
-  if (b < a.n_scan) {
-    if (threadIdx.x < 8) smem.scan.misc[threadIdx.x] = 0;
-    for (int i = threadIdx.x; i < 256; i += kT) {
-      smem.scan.hist[i] = 0;
-      smem.scan.cursor[i] = 0;
+  const int mixed = a.n_scan + a.n_head;
+  if (b < mixed) {
+    const int f1 = (int)(((long long)(b + 1) * a.n_head) / mixed);
+    const int f0 = (int)(((long long)b * a.n_head) / mixed);
+    if (f1 == f0) {
+      if (threadIdx.x < 8) smem.scan.misc[threadIdx.x] = 0;
+      for (int i = threadIdx.x; i < 256; i += kWideT) {
+        smem.scan.hist[i] = 0;
+        smem.scan.cursor[i] = 0;
+      }
+      u32x4_t q[NV];
+      load_slice<BF16, NV, kWideT>(a, b - f1, q);
+      __syncthreads();
+      scan_block<BF16, NV, true, kWideT>(a, smem.scan, b - f1, q);
+    } else {
+      head_block<4, kWideT / kWave>(a, smem.head, f0);
     }
-    __syncthreads();
-    scan_block<BF16, NV, true>(a, smem.scan, b);
-  } else if (b < a.n_scan + a.n_head) {
-    head_block<4>(a, smem.head, b - a.n_scan);
   } else {
-    afrag_block(a, b - a.n_scan - a.n_head);
+    afrag_block(a, b - mixed);
   }
 }
 
@@ -653,17 +727,18 @@ ScanPlan scan_plan(int rows, int V, int K, bool bf16) {
   ScanPlan p{};
   const int epv = bf16 ? 8 : 4;
   // slices per row: as few as keep every thread at <= kMaxNV vectors
-  const long long per_wg = (long long)kT * epv * kMaxNV;
+  p.wide = K > 64;
+  const int nt = p.wide ? kWideT : kT;
+  const long long per_wg = (long long)nt * epv * kMaxNV;
   p.S = (int)((V + per_wg - 1) / per_wg);
   long long sl = ((long long)V + p.S - 1) / p.S;
   sl = (sl + epv - 1) / epv * epv;   // slice length: multiple of the vector width
   p.slice = (int)sl;
   const int nvec = (int)((sl + epv - 1) / epv);
-  p.nv = (nvec + kT - 1) / kT;
+  p.nv = (nvec + nt - 1) / nt;
   p.n_scan = rows * p.S;
   p.merge_ept = (p.S * K + kT - 1) / kT <= 8 ? 8 : 16;
   p.list_bytes = p.S > 1 ? (size_t)rows * p.S * K * sizeof(uint64_t) : 0;
-  p.wide = K > 64;
   p.ok = p.nv >= 1 && p.nv <= kMaxNV && (long long)p.S * K <= 16LL * kT;
   return p;
 }
@@ -682,7 +757,7 @@ hipError_t launch_scan(const ScanPlan& p, bool bf16, const ScanArgs& args_in, hi
 #define DT_SCAN(B, NVV)                                                                  \
   do {                                                                                    \
     if (p.wide)                                                                           \
-      hipLaunchKernelGGL((scan_wide_kernel<B, NVV>), dim3(grid), dim3(kT), 0, s, a);      \
+      hipLaunchKernelGGL((scan_wide_kernel<B, NVV>), dim3(grid), dim3(kWideT), 0, s, a);  \
     else                                                                                  \
       hipLaunchKernelGGL((scan_kernel<B, NVV>), dim3(grid), dim3(kT), 0, s, a);           \
   } while (0)

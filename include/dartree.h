@@ -219,7 +219,9 @@ dartree_status dartree_round_plan(const dartree_dims* dims, dartree_round_info* 
  * first launch, events[1] after the logits scan (with the head tiles),
  * events[2] after the candidate merge (recorded also when no merge runs) and
  * events[3] after the tree kernel, each on the call's stream, so that
- * hipEventElapsedTime gives the time of each stage. `events` holds n = 4
+ * hipEventElapsedTime gives the time of each stage; every following
+ * dartree_topk_candidates records events[0], events[1] (after the scan) and
+ * events[2] (after the merge) the same way. `events` holds n = 4
  * hipEvent_t handles (passed as void*) created by the caller and kept alive
  * while set; n = 0 (events may be NULL) clears the hook. Returns
  * INVALID_ARGUMENT for any other n or NULL handles. */
