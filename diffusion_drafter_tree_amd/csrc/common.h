@@ -596,21 +596,21 @@ struct HistSmem {
   int cap;
 };
 
-template <int EPT>
-__device__ __forceinline__ bool hist_topk(const uint64_t (&k)[EPT], uint32_t lo_v, uint32_t hi_v, int K,
-                                          const HistSmem& sm) {
-  const int tid = threadIdx.x, nthr = blockDim.x;
+// Bin shift for value keys in [lo_v, hi_v]: the span lands in bin 255 or lower.
+__device__ __forceinline__ int hist_shift(uint32_t lo_v, uint32_t hi_v) {
   const uint32_t span = hi_v > lo_v ? hi_v - lo_v : 0u;
   const int nb = span ? 32 - __builtin_clz(span) : 0;
-  const int shift = nb > 8 ? nb - 8 : 0;
-  int bin[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const uint32_t hv = (uint32_t)(k[e] >> 32);
-    bin[e] = (k[e] != 0ull && hv >= lo_v) ? (int)min(255u, (hv - lo_v) >> shift) : -1;
-    if (bin[e] >= 0) lds_add(&sm.hist[bin[e]], 1);
-  }
-  lds_sync();
+  return nb > 8 ? nb - 8 : 0;
+}
+__device__ __forceinline__ int hist_bin(uint32_t hv, uint32_t lo_v, int shift) {
+  return (int)min(255u, (hv - lo_v) >> shift);
+}
+
+// With hist complete: wave 0 writes each bin's offset among the keys above
+// it (base) and the boundary bin b* and the count of keys in b* and above
+// (misc[0..1]). The caller syncs afterwards.
+__device__ __forceinline__ void hist_boundary(int K, const HistSmem& sm) {
+  const int tid = threadIdx.x;
   if (tid < kWave) {
     // lane l holds bins 255 - 4l .. 252 - 4l, so lanes run from the top bin down
     const int b0 = 255 - 4 * tid;
@@ -634,20 +634,24 @@ __device__ __forceinline__ bool hist_topk(const uint64_t (&k)[EPT], uint32_t lo_
       if (a3 < kk && kk <= a3 + h3) { sm.misc[0] = b0 - 3; sm.misc[1] = a3 + h3; }
     }
   }
-  lds_sync();
-  const int bstar = sm.misc[0], narea = sm.misc[1];
-  if (narea > sm.cap) return false;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    if (bin[e] >= bstar) {
-      const int slot = lds_add(&sm.cursor[bin[e]], 1);
-      sm.bucket[sm.base[bin[e]] + slot] = k[e];
-    }
+}
+
+// One key into its bucket when its bin is b* or above.
+__device__ __forceinline__ void hist_scatter(uint64_t x, int bin, int bstar, const HistSmem& sm) {
+  if (bin >= bstar) {
+    const int slot = lds_add(&sm.cursor[bin], 1);
+    sm.bucket[sm.base[bin] + slot] = x;
   }
-  lds_sync();
+}
+
+// With the buckets filled: each key at its bucket's offset plus its rank in
+// the bucket; the positions below K are the K largest, descending; zeros
+// past narea. Ends with a sync.
+__device__ __forceinline__ void hist_rank_out(int K, uint32_t lo_v, int shift, int narea, const HistSmem& sm) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
   for (int p = tid; p < narea; p += nthr) {
     const uint64_t x = sm.bucket[p];
-    const int b = (int)min(255u, ((uint32_t)(x >> 32) - lo_v) >> shift);
+    const int b = hist_bin((uint32_t)(x >> 32), lo_v, shift);
     const int lo = sm.base[b], hi = lo + sm.hist[b];
     int r = 0, q = lo;
     for (; q + 4 <= hi; q += 4) {
@@ -659,6 +663,28 @@ __device__ __forceinline__ bool hist_topk(const uint64_t (&k)[EPT], uint32_t lo_
   }
   for (int i = narea + tid; i < K; i += nthr) sm.out[i] = 0ull;
   lds_sync();
+}
+
+template <int EPT>
+__device__ __forceinline__ bool hist_topk(const uint64_t (&k)[EPT], uint32_t lo_v, uint32_t hi_v, int K,
+                                          const HistSmem& sm) {
+  const int shift = hist_shift(lo_v, hi_v);
+  int bin[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const uint32_t hv = (uint32_t)(k[e] >> 32);
+    bin[e] = (k[e] != 0ull && hv >= lo_v) ? hist_bin(hv, lo_v, shift) : -1;
+    if (bin[e] >= 0) lds_add(&sm.hist[bin[e]], 1);
+  }
+  lds_sync();
+  hist_boundary(K, sm);
+  lds_sync();
+  const int bstar = sm.misc[0], narea = sm.misc[1];
+  if (narea > sm.cap) return false;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) hist_scatter(k[e], bin[e], bstar, sm);
+  lds_sync();
+  hist_rank_out(K, lo_v, shift, narea, sm);
   return true;
 }
 

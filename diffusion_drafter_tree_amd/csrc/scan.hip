@@ -82,6 +82,7 @@ struct WideSmem {
   int hist[256];
   int cursor[256];
   int base[256];
+  int bhist[256];   // lane maxima by distance below the slice's largest key
   int misc[8];
   int wsum[NT / kWave];
 };
@@ -292,24 +293,64 @@ __device__ void scan_block(const ScanArgs& a, Smem& sm, int blk, const u32x4_t (
   const int nact = (nthr_valid + kWave - 1) / kWave;
   const int m = nact > 0 ? (K + nact - 1) / nact : K;
   if (nact == 0 && tid == 0) sm.misc[4] = 1;   // empty slice: the exact path yields nothing
-  if (WIDE) {
-    // the slice's largest key bounds the histogram bins of the selection
+  bool block_bound = false;
+  if constexpr (WIDE) {
+    // Bound from the whole block: the K-th largest lane maximum, to bin
+    // precision. Lane maxima are binned by their key distance below the
+    // slice's largest key (bin = one bf16 value, or 2^16 fp32 keys; 255
+    // collects the rest); counting down from the top bin, the first bin b*
+    // that brings the count to K gives T, the lowest key bin b* can hold.
+    // At least K lanes, hence K elements, reach T (a histogram of the five
+    // vector maxima a lane holds gives a tighter T, but its LDS atomics cost
+    // more than the smaller survivor set saves). The slice's largest key
+    // also bounds the selection's histogram later.
+    constexpr int SH = BF16 ? 0 : 16;
     const uint32_t wm = wave_max_u32(lk);
     if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(&sm.misc[6]), wm);
-  }
-  if (w < nact) {
-    const bool lv = tid < nthr_valid;
-    const int nl = __popcll(__ballot(lv));
-    if (nl >= m && m <= kWave) {
-      const uint32_t t = (WIDE && m > 8) ? wave_mth_largest_sorted(lk, lv, m) : wave_mth_largest(lk, lv, m, Tr::KBITS);
-      if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(&sm.misc[2]), ~t);
-    } else if (lane == 0) {
-      atomicOr(&sm.misc[4], 1);
+    __syncthreads();
+    const uint32_t hi = (uint32_t)sm.misc[6];
+    if (tid < nthr_valid) {
+      const uint32_t d = (hi - lk) >> SH;
+      atomicAdd(&sm.bhist[d < 255u ? d : 255u], 1);
     }
+    __syncthreads();
+    if (w == 0) {
+      const int b0 = 4 * lane;
+      const int h0 = sm.bhist[b0], h1 = sm.bhist[b0 + 1], h2 = sm.bhist[b0 + 2], h3 = sm.bhist[b0 + 3];
+      const int sum = h0 + h1 + h2 + h3;
+      const int a0 = wave_incl_scan_i32(sum) - sum, a1 = a0 + h0, a2 = a1 + h1, a3 = a2 + h2;
+      // misc[7] = b* + 1, left 0 when b* would be the catch-all bin
+      if (a0 < K && K <= a1 && b0 < 255) sm.misc[7] = b0 + 1;
+      if (a1 < K && K <= a2 && b0 + 1 < 255) sm.misc[7] = b0 + 2;
+      if (a2 < K && K <= a3 && b0 + 2 < 255) sm.misc[7] = b0 + 3;
+      if (a3 < K && K <= a3 + h3 && b0 + 3 < 255) sm.misc[7] = b0 + 4;
+    }
+    __syncthreads();
+    block_bound = sm.misc[7] > 0 && sm.misc[4] == 0;
   }
-  __syncthreads();
-  const bool bound_ok = sm.misc[4] == 0;
-  const uint32_t T = ~(uint32_t)sm.misc[2];
+  uint32_t T;
+  bool bound_ok;
+  if (block_bound) {
+    const uint32_t hi = (uint32_t)sm.misc[6];
+    const uint32_t span = (uint32_t)sm.misc[7] << (BF16 ? 0 : 16);
+    T = hi + 1u > span ? hi + 1u - span : 0u;
+    bound_ok = true;
+  } else {
+    // every active wave vouches for m lanes whose largest key >= its t
+    if (w < nact) {
+      const bool lv = tid < nthr_valid;
+      const int nl = __popcll(__ballot(lv));
+      if (nl >= m && m <= kWave) {
+        const uint32_t t = (WIDE && m > 8) ? wave_mth_largest_sorted(lk, lv, m) : wave_mth_largest(lk, lv, m, Tr::KBITS);
+        if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(&sm.misc[2]), ~t);
+      } else if (lane == 0) {
+        atomicOr(&sm.misc[4], 1);
+      }
+    }
+    __syncthreads();
+    bound_ok = sm.misc[4] == 0;
+    T = ~(uint32_t)sm.misc[2];
+  }
   if (bound_ok) {
     // hit vectors (largest key >= T) go to LDS, one LDS atomic per wave for
     // all its rounds; then one thread per element of a hit vector
@@ -338,7 +379,11 @@ __device__ void scan_block(const ScanArgs& a, Smem& sm, int blk, const u32x4_t (
     }
   }
   __syncthreads();
-  if (WIDE && bound_ok) {
+  // wide variant: survivors are counted into the selection's value histogram
+  // as they are appended (bins over [T, the slice's largest key])
+  const int wshift = hist_shift(T, (uint32_t)sm.misc[6]);
+  if constexpr (WIDE) {
+   if (bound_ok) {
     // one thread per queued vector, its elements checked in registers; the
     // survivors of a wave are placed by a prefix of the per-thread counts
     // (0..8, four bits, one ballot each) and one LDS atomic
@@ -376,11 +421,13 @@ __device__ void scan_block(const ScanArgs& a, Smem& sm, int blk, const u32x4_t (
               sm.key32[p] = (kk[e] << 16) | (0xFFFFu - (uint32_t)(idb + e - s0));
             else
               sm.key[p] = ((uint64_t)kk[e] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(idb + e));
+            atomicAdd(&sm.hist[hist_bin(kk[e], T, wshift)], 1);
           }
           ++p;
         }
       }
     }
+   }
   } else if (bound_ok) {
     const int nh = min(sm.misc[5], HCAP);
     // two elements a thread per pass, both read before either is used: one
@@ -419,7 +466,11 @@ __device__ void scan_block(const ScanArgs& a, Smem& sm, int blk, const u32x4_t (
   __syncthreads();
   int ns = sm.misc[3];
   uint32_t lo_v = T;   // every survivor's value key is >= lo_v
-  if (!bound_ok || sm.misc[5] > HCAP || ns > SCAP) {
+  const bool exact = !bound_ok || sm.misc[5] > HCAP || ns > SCAP;
+  if (exact) {
+    if constexpr (WIDE) {
+      for (int i = tid; i < 256; i += kT) sm.hist[i] = 0;
+    }
     // -- exact path: Th = K-th largest key (bitwise search on block counts),
     //    then among keys == Th the largest complemented ids (lowest ids)
     int nvalid = 0;
@@ -501,6 +552,30 @@ __device__ void scan_block(const ScanArgs& a, Smem& sm, int blk, const u32x4_t (
     }
   }
   if constexpr (WIDE) {
+    HistSmem hs{(LDS int*)sm.hist, (LDS int*)sm.cursor, (LDS int*)sm.base, (LDS int*)&sm.misc[0],
+                (LDS uint64_t*)sm.bucket, (LDS uint64_t*)sm.out, kSurvW};
+    if (!exact) {
+      // the histogram is complete: boundary, buckets, ranks
+      hist_boundary(K, hs);
+      lds_sync();
+      const int bstar = sm.misc[0], narea = sm.misc[1];
+      for (int i = tid; i < ns; i += kT) {
+        uint64_t x;
+        uint32_t hv;
+        if constexpr (BF16) {
+          const uint32_t k32 = sm.key32[i];
+          const uint32_t idx = (uint32_t)s0 + 0xFFFFu - (k32 & 0xFFFFu);
+          hv = k32 >> 16;
+          x = ((uint64_t)hv << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+        } else {
+          x = sm.key[i];
+          hv = (uint32_t)(x >> 32);
+        }
+        hist_scatter(x, hist_bin(hv, T, wshift), bstar, hs);
+      }
+      lds_sync();
+      hist_rank_out(K, T, wshift, narea, hs);
+    } else {
     // survivors, as 64-bit keys, ordered by the value histogram (ns <= the
     // bucket space, so the selection cannot run out of room)
     uint64_t kr[kSurvW / kT];
@@ -519,10 +594,9 @@ __device__ void scan_block(const ScanArgs& a, Smem& sm, int blk, const u32x4_t (
       }
       kr[e] = x;
     }
-    HistSmem hs{(LDS int*)sm.hist, (LDS int*)sm.cursor, (LDS int*)sm.base, (LDS int*)&sm.misc[0],
-                (LDS uint64_t*)sm.bucket, (LDS uint64_t*)sm.out, kSurvW};
     lds_sync();   // misc[0..1] and the hit queue's space are reused
     hist_topk<kSurvW / kT>(kr, lo_v, (uint32_t)sm.misc[6], K, hs);
+    }
   } else if constexpr (BF16) {
     rank_select32(sm, ns, K, s0);
   } else {
@@ -637,6 +711,7 @@ __global__ __launch_bounds__(kWideT) __attribute__((amdgpu_waves_per_eu(8))) voi
       for (int i = threadIdx.x; i < 256; i += kWideT) {
         smem.scan.hist[i] = 0;
         smem.scan.cursor[i] = 0;
+        smem.scan.bhist[i] = 0;
       }
       u32x4_t q[NV];
       load_slice<BF16, NV, kWideT>(a, b - f1, q);
