@@ -173,6 +173,44 @@ def test_topk_tie_heavy_rows_bit_exact(K):
     CK.check_candidates(ids, vals, x.astype(np.float64), K, where=f"topk f32 K={K}")
 
 
+def test_topk_stress_shape_all_rows():
+    """Every row of a 64-request round at K = 512 (1024 rows of V = 151936
+    bf16: four slices a row through the wide selection, then the slice-list
+    merge) against the oracle's top-K, bit for bit."""
+    cfg = I.CONFIGS["stress_64req"]
+    rnd = I.make_round(cfg, 0, 0)
+    rows = cfg.n_req * cfg.L
+    say(f"case topk stress shape rows={rows} V={cfg.V} K={cfg.K}")
+    dims = ops.make_dims(cfg)
+    lg = ops.to_device(rnd.logits)
+    ids = torch.zeros((cfg.n_req, cfg.L, cfg.K), dtype=torch.int32, device="cuda")
+    vals = torch.zeros((cfg.n_req, cfg.L, cfg.K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(ops.workspace_size(dims), dtype=torch.uint8, device="cuda")
+    ops.workspace_init(dims, ws)
+    ops.topk_candidates(dims, lg, ids, vals, ws)
+    torch.cuda.synchronize()
+    ref = I.bf16_bits_to_f32(rnd.logits.reshape(rows, cfg.V)).astype(np.float64)
+    CK.check_candidates(ids.cpu().numpy().reshape(rows, cfg.K), vals.cpu().numpy().reshape(rows, cfg.K), ref, cfg.K,
+                        where="stress topk")
+
+
+@pytest.mark.parametrize("K", [65, 128, 256])
+def test_topk_wide_selection_boosted_rows(K):
+    """K above 64 takes the wide selection; rows drawn like the workloads'
+    (noise plus boosted ids), bf16 and fp32."""
+    cfg = I.CONFIGS["stress_64req"].with_(n_req=1, L=16)
+    rnd = I.make_round(cfg, 3, K)
+    bits = rnd.logits.reshape(cfg.L, cfg.V)
+    say(f"case topk wide bf16 rows={cfg.L} V={cfg.V} K={K}")
+    ids, vals = _topk_rows(bits, K)
+    ref = I.bf16_bits_to_f32(bits).astype(np.float64)
+    CK.check_candidates(ids, vals, ref, K, where=f"wide bf16 K={K}")
+    x = ref.astype(np.float32) + np.float32(1e-3) * np.random.default_rng(K).standard_normal(ref.shape).astype(np.float32)
+    say(f"case topk wide f32 rows={cfg.L} V={cfg.V} K={K}")
+    ids, vals = _topk_rows(x, K, dtype="f32")
+    CK.check_candidates(ids, vals, x.astype(np.float64), K, where=f"wide f32 K={K}")
+
+
 def test_topk_small_and_ragged_rows():
     rng = np.random.default_rng(7)
     for V, K in [(1, 1), (7, 7), (9, 3), (4099, 64), (8192, 64), (8193, 100), (16385, 1024), (24577, 17)]:
