@@ -229,8 +229,10 @@ def main():
 
     # ---- the logits scan where bandwidth decides: 64 requests, K = 512 ----------
     scan_stress = None
+    head_stress = None
     if not args.no_scan_stress:
         scan_stress = scan_at_stress_shape(HBM_PEAK)
+        head_stress = head_at_stress_shape()
 
     # ---- CPU oracle baseline on a bounded sample -------------------------------
     cpu = None
@@ -258,6 +260,7 @@ def main():
         "roofline": roofline,
         "roofline_scan": roofline_scan,
         "roofline_scan_stress": scan_stress,
+        "roofline_head_stress": head_stress,
         "kernels": kernels,
         "stage_timing": event_kind,
         "plan": info,
@@ -300,6 +303,41 @@ def measured_traffic(cfg_name):
         if h.hexdigest()[:16] == rec[k]["src_sha256"]:
             out[k] = rec[k]["bytes"]
     return out
+
+
+def head_at_stress_shape(n_timed=16):
+    """a0 alone (dartree_head_states) at the stress_64req shape: h = P^T H for
+    1024 rows, D = 4096, r = 512, bf16 inputs (H ~ N(0, 1), P ~ N(0, 1/D)),
+    fp32 output, against the dense bf16 MFMA peak."""
+    import numpy as np
+    import torch
+
+    from diffusion_drafter_tree_amd import inputs as I
+    from diffusion_drafter_tree_amd import ops
+
+    cfg = I.CONFIGS["stress_64req"]
+    M, D, r = cfg.n_req * cfg.L, cfg.D, cfg.r
+    rng = np.random.default_rng(11)
+    H = ops.to_device(I.f32_to_bf16_bits(rng.standard_normal((M, D)).astype(np.float32)))
+    Pt = ops.to_device(I.f32_to_bf16_bits((rng.standard_normal((r, D)) / np.sqrt(D)).astype(np.float32)))
+    h = torch.empty((M, r), dtype=torch.float32, device="cuda")
+    dims = ops.make_dims(cfg)
+    for _ in range(4):
+        ops.head_states(dims, H, Pt, h)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n_timed):
+        ops.head_states(dims, H, Pt, h)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / n_timed
+    flops = 2 * M * D * r
+    peak = 2500.0   # TFLOP/s, dense bf16 MFMA
+    tf = flops / (us * 1e-6) / 1e12
+    return {"kernel": "head tiles of h = P^T H (64 x 64, LDS-staged, v_mfma_f32_16x16x32_bf16)", "bound": "mfma",
+            "workload": f"stress_64req head inputs: M={M} D={D} r={r} bf16, fp32 out", "achieved": round(tf, 1),
+            "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4), "us": round(us, 2), "alg_flops": flops}
 
 
 def scan_at_stress_shape(hbm_peak, n_timed=16):

@@ -244,7 +244,8 @@ dartree_status dartree_round_plan(const dartree_dims* dims, dartree_round_info* 
   const bool head_fused = dims->D > 0 && dartree::head_mfma_ok(dims->weight_dtype == DARTREE_BF16,
                                                                dummy_lists, dummy_lists, dims->D, dims->r);
   info->n_launches = 2 + (merge_sep ? 1 : 0) + ((dims->D > 0 && !head_fused) ? 1 : 0);
-  info->scan_workgroups = w.plan.n_scan + (head_fused ? (dims->r / 16) * ((rows + 15) / 16) : 0) +
+  const bool head_big = w.plan.wide && dartree::head_big_ok(rows, dims->D, dims->r);
+  info->scan_workgroups = w.plan.n_scan + (head_fused ? dartree::head_tiles(head_big, rows, dims->r) : 0) +
                           ((tp.mode == 3 && w.afrag_off) ? dartree::kAFragWaves : 0);
   info->tree_kernel = tp.mode == 3 ? 1 : 0;
   info->tree_lds_bytes = (int32_t)tp.smem;
@@ -439,7 +440,8 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
     sa.M = rows;
     sa.D = dims->D;
     sa.r = dims->r;
-    sa.n_head = (dims->r / 16) * ((rows + 15) / 16);
+    sa.head_big = (w.plan.wide && dartree::head_big_ok(rows, dims->D, dims->r)) ? 1 : 0;
+    sa.n_head = dartree::head_tiles(sa.head_big, rows, dims->r);
   }
   hipError_t e;
   stage_mark(0, s);

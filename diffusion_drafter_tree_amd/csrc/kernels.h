@@ -19,6 +19,7 @@ struct ScanArgs {
   const uint16_t* Pt;   // [r][D]
   float* h;             // [M][r]
   int M, D, r, n_head;
+  int head_big;         // wide launch only: 64 x 64 head tiles (head_big_ok)
   // staging of A (bf16 [256][256]) as fp16 MFMA fragments for the
   // block-decoding tree kernel: n_afrag = 16 workgroups (one per tree wave)
   // write a_frag[wave][tile][k-step][lane][8], 0 for none
@@ -36,6 +37,9 @@ struct ScanPlan {
 };
 ScanPlan scan_plan(int rows, int V, int K, bool bf16);
 bool head_mfma_ok(bool bf16, const void* H, const void* Pt, int D, int r);
+// 64 x 64 head tiles staged through LDS: many rows, r % 64 == 0, D % 128 == 0
+bool head_big_ok(int M, int D, int r);
+int head_tiles(bool big, int M, int r);
 hipError_t launch_scan(const ScanPlan& p, bool bf16, const ScanArgs& a, hipStream_t s);
 hipError_t launch_merge(const ScanPlan& p, int rows, int K, bool bf16, const uint64_t* lists, int32_t* cand_ids,
                         float* cand_logit, hipStream_t s);

@@ -86,10 +86,18 @@ struct WideSmem {
   int misc[8];
   int wsum[NT / kWave];
 };
+// Head tiles for many rows: 64 x 64 outputs per workgroup, D staged through
+// LDS in double-buffered stages of 128 columns (rows padded by 8 elements).
+constexpr int kHB = 64, kHS = 128, kHP = kHS + 8;
+struct HeadBigSmem {
+  uint16_t a[2][kHB][kHP];
+  uint16_t b[2][kHB][kHP];
+};
 template <int NT>
 union WideKernelSmem {
   WideSmem<NT> scan;
   HeadSmem head;
+  HeadBigSmem headbig;
 };
 
 template <bool BF16>
@@ -673,6 +681,58 @@ __device__ void afrag_block(const ScanArgs& a, int tw) {
   }
 }
 
+// One 64 x 64 tile of h[M][r] = H[M][D] * P[D][r] (Pt stored [r][D]) by a
+// 1024-thread workgroup: wave w computes the 16 x 16 sub-tile (w / 4, w % 4)
+// on v_mfma_f32_16x16x32_bf16, reading its fragments from LDS. Each stage of
+// 128 columns of D is one 16-byte vector of H and one of P a thread; the next
+// stage's vectors are loaded before the current stage's MFMAs and written to
+// the other LDS buffer after them (loading four stages ahead through a ring
+// of registers measured slower). Rows of H past M read as zero.
+__device__ void head_block_big(const ScanArgs& a, HeadBigSmem& sm, int tile) {
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int ntn = a.r / kHB;
+  const int nt = tile % ntn, mt = tile / ntn;
+  const int m0 = mt * kHB, n0 = nt * kHB;
+  const int sr = tid >> 4, sc = (tid & 15) * 8;   // staging: row 0..63, column 0..120
+  const bool av = m0 + sr < a.M;
+  const uint16_t* ag = a.H + (size_t)(av ? m0 + sr : 0) * a.D + sc;
+  const uint16_t* bg = a.Pt + (size_t)(n0 + sr) * a.D + sc;
+  const u16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int NS = a.D / kHS;
+  u16x8_t ra = av ? *reinterpret_cast<const u16x8_t*>(ag) : zero;
+  u16x8_t rb = *reinterpret_cast<const u16x8_t*>(bg);
+  *reinterpret_cast<u16x8_t*>(&sm.a[0][sr][sc]) = ra;
+  *reinterpret_cast<u16x8_t*>(&sm.b[0][sr][sc]) = rb;
+  __syncthreads();
+  const int wm = w >> 2, wn = w & 3;
+  const int fr = lane & 15, fc = (lane >> 4) * 8;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int st = 0; st < NS; ++st) {
+    const int cur = st & 1;
+    const bool more = st + 1 < NS;
+    if (more) {
+      ra = av ? *reinterpret_cast<const u16x8_t*>(ag + (size_t)(st + 1) * kHS) : zero;
+      rb = *reinterpret_cast<const u16x8_t*>(bg + (size_t)(st + 1) * kHS);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kHS / 32; ++ks) {
+      const u16x8_t fa = *reinterpret_cast<const u16x8_t*>(&sm.a[cur][wm * 16 + fr][ks * 32 + fc]);
+      const u16x8_t fb = *reinterpret_cast<const u16x8_t*>(&sm.b[cur][wn * 16 + fr][ks * 32 + fc]);
+      acc = mfma_bf16(fa, fb, acc);
+    }
+    if (more) {
+      *reinterpret_cast<u16x8_t*>(&sm.a[cur ^ 1][sr][sc]) = ra;
+      *reinterpret_cast<u16x8_t*>(&sm.b[cur ^ 1][sr][sc]) = rb;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 16 + (lane >> 4) * 4 + i;
+    if (m < a.M) a.h[(size_t)m * a.r + n0 + wn * 16 + (lane & 15)] = acc[i];
+  }
+}
+
 template <bool BF16, int NV>
 __global__ __launch_bounds__(kT) void scan_kernel(ScanArgs a) {
   __shared__ KernelSmem smem;
@@ -717,6 +777,8 @@ __global__ __launch_bounds__(kWideT) __attribute__((amdgpu_waves_per_eu(8))) voi
       load_slice<BF16, NV, kWideT>(a, b - f1, q);
       __syncthreads();
       scan_block<BF16, NV, true, kWideT>(a, smem.scan, b - f1, q);
+    } else if (a.head_big) {
+      head_block_big(a, smem.headbig, f0);
     } else {
       head_block<4, kWideT / kWave>(a, smem.head, f0);
     }
@@ -822,6 +884,12 @@ bool head_mfma_ok(bool bf16, const void* H, const void* Pt, int D, int r) {
   return bf16 && D % 32 == 0 && r % 16 == 0 && ((((uintptr_t)H) | ((uintptr_t)Pt)) & 15u) == 0;
 }
 
+bool head_big_ok(int M, int D, int r) { return M >= kHB && r % kHB == 0 && D % kHS == 0; }
+
+int head_tiles(bool big, int M, int r) {
+  return big ? (r / kHB) * ((M + kHB - 1) / kHB) : (r / 16) * ((M + 15) / 16);
+}
+
 hipError_t launch_scan(const ScanPlan& p, bool bf16, const ScanArgs& args_in, hipStream_t s) {
   ScanArgs a = args_in;
   a.S = p.S;
@@ -866,9 +934,13 @@ hipError_t launch_head(bool bf16, const void* H, const void* Pt, float* h, int M
   a.M = M;
   a.D = D;
   a.r = r;
-  a.n_head = (r / 16) * ((M + 15) / 16);
   a.n_scan = 0;
-  hipLaunchKernelGGL((scan_kernel<true, 1>), dim3(a.n_head), dim3(kT), 0, s, a);
+  a.head_big = head_big_ok(M, D, r) ? 1 : 0;
+  a.n_head = head_tiles(a.head_big, M, r);
+  if (a.head_big)
+    hipLaunchKernelGGL((scan_wide_kernel<true, 1>), dim3(a.n_head), dim3(kWideT), 0, s, a);
+  else
+    hipLaunchKernelGGL((scan_kernel<true, 1>), dim3(a.n_head), dim3(kT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -211,6 +211,27 @@ def test_topk_wide_selection_boosted_rows(K):
     CK.check_candidates(ids, vals, x.astype(np.float64), K, where=f"wide f32 K={K}")
 
 
+@pytest.mark.parametrize("n_req,L,D,r", [(64, 16, 4096, 512), (5, 20, 2560, 256), (4, 16, 2560, 256)])
+def test_head_states_many_rows(n_req, L, D, r):
+    """h = P^T H through dartree_head_states at many rows (64 x 64 tiles
+    staged through LDS; M = 100 leaves a partial tile) against the oracle's
+    projection, within the score tolerance."""
+    cfg = I.CONFIGS["stress_64req"].with_(n_req=n_req, L=L, D=D, r=r)
+    rng = np.random.default_rng(n_req * 1000 + D)
+    M = n_req * L
+    Hb = I.f32_to_bf16_bits(rng.standard_normal((M, D)).astype(np.float32))
+    Pb = I.f32_to_bf16_bits((rng.standard_normal((r, D)) / np.sqrt(D)).astype(np.float32))
+    say(f"case head_states M={M} D={D} r={r}")
+    dims = ops.make_dims(cfg)
+    h = torch.zeros((M, r), dtype=torch.float32, device="cuda")
+    ops.head_states(dims, ops.to_device(Hb), ops.to_device(Pb), h)
+    torch.cuda.synchronize()
+    ref = O.head_states(O.widen(Hb, "bf16"), O.widen(Pb, "bf16"))
+    err = float(np.max(np.abs(h.cpu().numpy().astype(np.float64) - ref)))
+    say(f"  max|dh| = {err:.2e}")
+    assert err <= TOL, err
+
+
 def test_topk_small_and_ragged_rows():
     rng = np.random.default_rng(7)
     for V, K in [(1, 1), (7, 7), (9, 3), (4099, 64), (8192, 64), (8193, 100), (16385, 1024), (24577, 17)]:
