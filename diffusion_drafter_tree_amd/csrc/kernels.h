@@ -37,7 +37,7 @@ struct ScanPlan {
 };
 ScanPlan scan_plan(int rows, int V, int K, bool bf16);
 bool head_mfma_ok(bool bf16, const void* H, const void* Pt, int D, int r);
-// 64 x 64 head tiles staged through LDS: many rows, r % 64 == 0, D % 128 == 0
+// 64 x 64 head tiles staged through LDS: many rows, r % 64 == 0, D % 512 == 0
 bool head_big_ok(int M, int D, int r);
 int head_tiles(bool big, int M, int r);
 hipError_t launch_scan(const ScanPlan& p, bool bf16, const ScanArgs& a, hipStream_t s);

@@ -93,6 +93,7 @@ struct HeadBigSmem {
   uint16_t a[2][kHB][kHP];
   uint16_t b[2][kHB][kHP];
 };
+static_assert(sizeof(HeadBigSmem) >= 4 * kHB * (kHB + 1) * sizeof(float), "partial quadrants fit the staging buffers");
 template <int NT>
 union WideKernelSmem {
   WideSmem<NT> scan;
@@ -682,54 +683,88 @@ __device__ void afrag_block(const ScanArgs& a, int tw) {
 }
 
 // One 64 x 64 tile of h[M][r] = H[M][D] * P[D][r] (Pt stored [r][D]) by a
-// 1024-thread workgroup: wave w computes the 16 x 16 sub-tile (w / 4, w % 4)
-// on v_mfma_f32_16x16x32_bf16, reading its fragments from LDS. Each stage of
-// 128 columns of D is one 16-byte vector of H and one of P a thread; the next
-// stage's vectors are loaded before the current stage's MFMAs and written to
-// the other LDS buffer after them (loading four stages ahead through a ring
-// of registers measured slower). Rows of H past M read as zero.
+// 1024-thread workgroup on v_mfma_f32_16x16x32_bf16, fragments read from
+// LDS. Wave w takes the 32 x 32 quadrant w % 4 (2 x 2 sub-tiles, so each
+// fragment it reads feeds two MFMAs) and, of every stage's four k-steps, the
+// k-step w / 4; the four partial quadrants are added in LDS in a fixed order
+// at the end. Each stage of 128 columns of D is one 16-byte vector of H and
+// one of P a thread. Stages are loaded four ahead into a ring of registers
+// (slot = stage % 4, the stage loop unrolled by four so that slots and LDS
+// buffers are named statically; D is a multiple of 512), and each stage is
+// written to the other LDS buffer while the current one feeds the MFMAs.
+// Every load is unconditional: past the last stage the last one is read
+// again, and rows of H past M read row 0 (an output row depends only on the
+// same row of H, and rows past M are not stored). The compiler's wait before a
+// stage's LDS write then counts exactly the three younger stages' loads, and
+// the per-stage barriers wait for LDS traffic only, so about three stages of
+// loads stay in flight.
 __device__ void head_block_big(const ScanArgs& a, HeadBigSmem& sm, int tile) {
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int ntn = a.r / kHB;
   const int nt = tile % ntn, mt = tile / ntn;
   const int m0 = mt * kHB, n0 = nt * kHB;
   const int sr = tid >> 4, sc = (tid & 15) * 8;   // staging: row 0..63, column 0..120
-  const bool av = m0 + sr < a.M;
-  const uint16_t* ag = a.H + (size_t)(av ? m0 + sr : 0) * a.D + sc;
+  const uint16_t* ag = a.H + (size_t)(m0 + sr < a.M ? m0 + sr : 0) * a.D + sc;
   const uint16_t* bg = a.Pt + (size_t)(n0 + sr) * a.D + sc;
-  const u16x8_t zero = {0, 0, 0, 0, 0, 0, 0, 0};
   const int NS = a.D / kHS;
-  u16x8_t ra = av ? *reinterpret_cast<const u16x8_t*>(ag) : zero;
-  u16x8_t rb = *reinterpret_cast<const u16x8_t*>(bg);
-  *reinterpret_cast<u16x8_t*>(&sm.a[0][sr][sc]) = ra;
-  *reinterpret_cast<u16x8_t*>(&sm.b[0][sr][sc]) = rb;
-  __syncthreads();
-  const int wm = w >> 2, wn = w & 3;
-  const int fr = lane & 15, fc = (lane >> 4) * 8;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int st = 0; st < NS; ++st) {
-    const int cur = st & 1;
-    const bool more = st + 1 < NS;
-    if (more) {
-      ra = av ? *reinterpret_cast<const u16x8_t*>(ag + (size_t)(st + 1) * kHS) : zero;
-      rb = *reinterpret_cast<const u16x8_t*>(bg + (size_t)(st + 1) * kHS);
-    }
+  u16x8_t pa[4], pb[4];
+  auto load = [&](int u, int st) {
+    const size_t off = (size_t)(st < NS ? st : NS - 1) * kHS;
+    pa[u] = *reinterpret_cast<const u16x8_t*>(ag + off);
+    pb[u] = *reinterpret_cast<const u16x8_t*>(bg + off);
+  };
+  auto stage_to_lds = [&](int u, int buf) {
+    *reinterpret_cast<u16x8_t*>(&sm.a[buf][sr][sc]) = pa[u];
+    *reinterpret_cast<u16x8_t*>(&sm.b[buf][sr][sc]) = pb[u];
+  };
 #pragma unroll
-    for (int ks = 0; ks < kHS / 32; ++ks) {
-      const u16x8_t fa = *reinterpret_cast<const u16x8_t*>(&sm.a[cur][wm * 16 + fr][ks * 32 + fc]);
-      const u16x8_t fb = *reinterpret_cast<const u16x8_t*>(&sm.b[cur][wn * 16 + fr][ks * 32 + fc]);
-      acc = mfma_bf16(fa, fb, acc);
+  for (int u = 0; u < 4; ++u) load(u, u);
+  stage_to_lds(0, 0);
+  lds_sync();
+  const int qm = (w & 3) >> 1, qn = w & 1, ksl = w >> 2;
+  const int fr = lane & 15, kc = ksl * 32 + (lane >> 4) * 8;
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int st0 = 0; st0 < NS; st0 += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int cur = u & 1;   // stage st0 + u, st0 a multiple of 4
+      load(u, st0 + u + 4);    // slot u held stage st0 + u, already in LDS
+      const u16x8_t fa0 = *reinterpret_cast<const u16x8_t*>(&sm.a[cur][qm * 32 + fr][kc]);
+      const u16x8_t fa1 = *reinterpret_cast<const u16x8_t*>(&sm.a[cur][qm * 32 + 16 + fr][kc]);
+      const u16x8_t fb0 = *reinterpret_cast<const u16x8_t*>(&sm.b[cur][qn * 32 + fr][kc]);
+      const u16x8_t fb1 = *reinterpret_cast<const u16x8_t*>(&sm.b[cur][qn * 32 + 16 + fr][kc]);
+      acc[0][0] = mfma_bf16(fa0, fb0, acc[0][0]);
+      acc[0][1] = mfma_bf16(fa0, fb1, acc[0][1]);
+      acc[1][0] = mfma_bf16(fa1, fb0, acc[1][0]);
+      acc[1][1] = mfma_bf16(fa1, fb1, acc[1][1]);
+      stage_to_lds((u + 1) & 3, cur ^ 1);   // past the last stage: never read
+      lds_sync();
     }
-    if (more) {
-      *reinterpret_cast<u16x8_t*>(&sm.a[cur ^ 1][sr][sc]) = ra;
-      *reinterpret_cast<u16x8_t*>(&sm.b[cur ^ 1][sr][sc]) = rb;
-    }
-    __syncthreads();
   }
+  // partial quadrants [k-step][64][64 + 1] over the staging buffers, then
+  // each thread adds the four partials of four outputs in k-step order
+  LDS float* part = (LDS float*)&sm.a[0][0][0];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 16 + (lane >> 4) * 4 + i;
-    if (m < a.M) a.h[(size_t)m * a.r + n0 + wn * 16 + (lane & 15)] = acc[i];
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = qm * 32 + i * 16 + (lane >> 4) * 4 + e, col = qn * 32 + j * 16 + (lane & 15);
+        part[(ksl * kHB + row) * (kHB + 1) + col] = acc[i][j][e];
+      }
+  lds_sync();
+#pragma unroll
+  for (int q = 0; q < kHB * kHB / 1024; ++q) {
+    const int idx = tid + q * 1024, row = idx / kHB, col = idx % kHB;
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v += part[(k * kHB + row) * (kHB + 1) + col];
+    if (m0 + row < a.M) a.h[(size_t)(m0 + row) * a.r + n0 + col] = v;
   }
 }
 
@@ -884,7 +919,7 @@ bool head_mfma_ok(bool bf16, const void* H, const void* Pt, int D, int r) {
   return bf16 && D % 32 == 0 && r % 16 == 0 && ((((uintptr_t)H) | ((uintptr_t)Pt)) & 15u) == 0;
 }
 
-bool head_big_ok(int M, int D, int r) { return M >= kHB && r % kHB == 0 && D % kHS == 0; }
+bool head_big_ok(int M, int D, int r) { return M >= kHB && r % kHB == 0 && D % (4 * kHS) == 0; }
 
 int head_tiles(bool big, int M, int r) {
   return big ? (r / kHB) * ((M + kHB - 1) / kHB) : (r / 16) * ((M + 15) / 16);
