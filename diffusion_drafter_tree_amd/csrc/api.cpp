@@ -465,4 +465,62 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
   return DARTREE_OK;
 }
 
+dartree_status dartree_serial_workspace_size(const dartree_dims* dims, size_t* bytes) {
+  g_err[0] = 0;
+  TRY(check_dims(dims));
+  if (!bytes) return fail(DARTREE_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = (size_t)dims->n_req * (size_t)(dims->B + 1) * (size_t)dims->r * sizeof(float);
+  return DARTREE_OK;
+}
+
+dartree_status dartree_build_serial(const dartree_dims* dims, const dartree_head* head, const int32_t* cand_ids,
+                                    const float* cand_logit, const float* h, int32_t* n_sel, int32_t* tok,
+                                    int32_t* depth, int32_t* parent, float* score, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  g_err[0] = 0;
+  TRY(check_dims(dims));
+  if (dims->B > dartree::kSerialMaxB)
+    return fail(DARTREE_ERR_UNSUPPORTED, "heap-serial construction: B=%d exceeds %d", dims->B, dartree::kSerialMaxB);
+  if (!head) return fail(DARTREE_ERR_INVALID_ARGUMENT, "head is NULL");
+  const int wa = dims->weight_dtype == DARTREE_BF16 ? 2 : 4;
+  REQ_PTR(head->A, wa);
+  REQ_PTR(head->E, wa);
+  REQ_PTR(head->U, wa);
+  REQ_PTR(cand_ids, 4);
+  REQ_PTR(cand_logit, 4);
+  REQ_PTR(h, 4);
+  REQ_PTR(n_sel, 4);
+  REQ_PTR(tok, 4);
+  REQ_PTR(depth, 4);
+  REQ_PTR(parent, 4);
+  REQ_PTR(score, 4);
+  REQ_PTR(ws, 4);
+  const size_t need = (size_t)dims->n_req * (size_t)(dims->B + 1) * (size_t)dims->r * sizeof(float);
+  if (ws_bytes < need)
+    return fail(DARTREE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+  dartree::SerialArgs a{};
+  a.n_req = dims->n_req;
+  a.L = dims->L;
+  a.V = dims->V;
+  a.K = dims->K;
+  a.B = dims->B;
+  a.r = dims->r;
+  a.beta = dims->beta;
+  a.A = head->A;
+  a.E = head->E;
+  a.U = head->U;
+  a.cand_ids = cand_ids;
+  a.cand_logit = cand_logit;
+  a.h = h;
+  a.states = static_cast<float*>(ws);
+  a.n_sel = n_sel;
+  a.tok = tok;
+  a.depth = depth;
+  a.parent = parent;
+  a.score = score;
+  hipError_t e = dartree::launch_serial(a, dims->weight_dtype == DARTREE_BF16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "serial launch");
+  return DARTREE_OK;
+}
+
 }  // extern "C"

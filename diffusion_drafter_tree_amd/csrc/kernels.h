@@ -98,6 +98,26 @@ TreePlan tree_fast_plan(const TreeArgs& a);
 hipError_t launch_tree_fast(const TreePlan& p, const TreeArgs& a, hipStream_t s);
 
 hipError_t launch_mask(int n_req, int B, const int32_t* n_sel, const int32_t* parent, uint64_t* mask, hipStream_t s);
+
+// ---- heap-serial construction (the "pop then correct" baseline) -------------
+constexpr int kSerialMaxB = 511;   // pop indices pack into 9 bits of the node key
+struct SerialArgs {
+  int n_req, L, V, K, B, r;
+  float beta;
+  const void* A;
+  const void* E;
+  const void* U;
+  const int32_t* cand_ids;    // [n][L][K]
+  const float* cand_logit;    // [n][L][K]
+  const float* h;             // [n][L][r]
+  float* states;              // [n][B + 1][r] workspace
+  int32_t* n_sel;             // [n]
+  int32_t* tok;               // [n][B], pop order
+  int32_t* depth;             // [n][B]
+  int32_t* parent;            // [n][B]: pop index of the parent, -1 for the root
+  float* score;               // [n][B]: s_beta
+};
+hipError_t launch_serial(const SerialArgs& a, bool bf16w, hipStream_t s);
 hipError_t launch_fill_u32(void* p, size_t n_words, uint32_t value, hipStream_t s);
 
 }  // namespace dartree

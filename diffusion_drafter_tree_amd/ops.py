@@ -184,6 +184,41 @@ def run_steps(dims: C.Dims, head: DeviceHead, logits: torch.Tensor, H_or_h: torc
     tree_mask(dims, rb.n_sel, rb.parent, rb.mask, stream)
 
 
+def serial_workspace_size(dims: C.Dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(C.load().dartree_serial_workspace_size(ctypes.byref(dims), ctypes.byref(n)), "serial_workspace_size")
+    return n.value
+
+
+class SerialOutputs:
+    """Outputs of the heap-serial construction for one config, in pop order."""
+
+    def __init__(self, cfg: I.Config, device="cuda"):
+        n, B = cfg.n_req, cfg.B
+        self.dims = make_dims(cfg)
+        self.n_sel = torch.zeros((n,), dtype=torch.int32, device=device)
+        self.tok = torch.zeros((n, B), dtype=torch.int32, device=device)
+        self.depth = torch.zeros((n, B), dtype=torch.int32, device=device)
+        self.parent = torch.zeros((n, B), dtype=torch.int32, device=device)
+        self.score = torch.zeros((n, B), dtype=torch.float32, device=device)
+        self.ws_bytes = serial_workspace_size(self.dims)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+
+    def numpy(self) -> Dict[str, np.ndarray]:
+        g = lambda t: t.detach().cpu().numpy()
+        return {"n_sel": g(self.n_sel), "tok": g(self.tok), "depth": g(self.depth), "parent": g(self.parent),
+                "score": g(self.score)}
+
+
+def build_serial(dims: C.Dims, head: DeviceHead, cand_ids: torch.Tensor, cand_logit: torch.Tensor,
+                 h: torch.Tensor, out: SerialOutputs, stream=None):
+    """The heap-serial construction through dartree_build_serial."""
+    _check(C.load().dartree_build_serial(ctypes.byref(dims), ctypes.byref(head.c), _p(cand_ids), _p(cand_logit),
+                                         _p(h), _p(out.n_sel), _p(out.tok), _p(out.depth), _p(out.parent),
+                                         _p(out.score), _p(out.ws), out.ws_bytes, _stream(stream)),
+           "build_serial")
+
+
 def set_stage_events(events: Optional[list]):
     """Profiling hook: record the given four torch.cuda.Event objects around the
     stages of every following build_round on this thread (scan, merge, tree

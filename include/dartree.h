@@ -214,6 +214,34 @@ typedef struct {
 } dartree_round_info;
 dartree_status dartree_round_plan(const dartree_dims* dims, dartree_round_info* info);
 
+/* Heap-serial construction, the "pop then correct" baseline of the deferred
+ * round (marsggbo blog, section 2 and section 4.3, Table 2: a best-first
+ * builder that runs the correction head once per popped node). Per request,
+ * from the round's candidates and head inputs: the root (state h_0) has the K
+ * candidates of depth 1 as pending children; B times, the best pending node
+ * by the round's comparator (s_beta descending, depth ascending, token
+ * ascending, then the parent's own order) is popped; when its depth d < L its
+ * state tanh(A s_parent + E[u] + h_d) is computed and all K candidates of
+ * depth d + 1 become its pending children with
+ * cum = cum_parent + min(log q, 0), s_beta = cum + beta (d + 1). No per-depth
+ * width applies (W is ignored). With W >= B the deferred round selects the
+ * same nodes (a consequence of the definitions, pinned on the oracle).
+ * Inputs: cand_ids / cand_logit [n][L][K] (dartree_topk_candidates), h
+ * [n][L][r] fp32 (dartree_head_states or supplied), the head (A, E, U in
+ * weight_dtype). Outputs in pop order, device arrays [n][B]: tok, depth,
+ * parent (pop index of the parent, -1 for the root; always below the node's
+ * own index), score (s_beta); n_sel[n] = min(B, reachable nodes); pads as in
+ * dartree_select_topB (tok -1, depth 0, parent -2, score -inf).
+ * dartree_tree_mask builds the ancestor mask from n_sel and parent. ws is a
+ * device workspace of dartree_serial_workspace_size bytes (the nodes' states,
+ * [n][B + 1][r] fp32), overwritten. UNSUPPORTED for B > 511; other errors as
+ * for the round. */
+dartree_status dartree_serial_workspace_size(const dartree_dims* dims, size_t* bytes);
+dartree_status dartree_build_serial(const dartree_dims* dims, const dartree_head* head, const int32_t* cand_ids,
+                                    const float* cand_logit, const float* h, int32_t* n_sel, int32_t* tok,
+                                    int32_t* depth, int32_t* parent, float* score, void* ws, size_t ws_bytes,
+                                    void* stream);
+
 /* Profiling hook (not part of a round's computation). When set, every
  * following dartree_build_round on this thread records events[0] before its
  * first launch, events[1] after the logits scan (with the head tiles),

@@ -200,3 +200,30 @@ def test_gpu_parity_cases_cover_the_block_decoding_kernel(lib):
     # both key widths of the slice-list merge: bf16 and fp32 logits over several slices
     multi = [mod.SMALL[n] for n in mod.FAST if ops.round_plan(ops.make_dims(mod.SMALL[n]))["scan_slices"] > 1]
     assert {c.logits_dtype for c in multi} == {"bf16", "f32"}
+
+
+def test_serial_builder_validates_on_host(lib):
+    """dartree_build_serial: workspace size n (B + 1) r fp32; B above 511,
+    NULL or misaligned pointers and a short workspace are rejected before any
+    launch."""
+    d = dims()
+    n = ctypes.c_size_t(0)
+    assert lib.dartree_serial_workspace_size(ctypes.byref(d), ctypes.byref(n)) == C.OK
+    assert n.value == d.n_req * (d.B + 1) * d.r * 4
+    fake = ctypes.c_void_p(0x10000)
+    s = ctypes.c_void_p(None)
+    head = C.Head(A=0x10000, E=0x10000, U=0x10000, Pt=0x10000)
+    args = lambda dd, ws_bytes, **kw: [ctypes.byref(dd), ctypes.byref(head)] + [kw.get(k, fake) for k in (
+        "cand_ids", "cand_logit", "h", "n_sel", "tok", "depth", "parent", "score", "ws")] + [ws_bytes, s]
+    big = dims(B=600, W=16)
+    nb = ctypes.c_size_t(0)
+    assert lib.dartree_serial_workspace_size(ctypes.byref(big), ctypes.byref(nb)) == C.OK
+    assert lib.dartree_build_serial(*args(big, nb.value)) == C.ERR_UNSUPPORTED
+    assert "511" in C.last_error()
+    assert lib.dartree_build_serial(*args(d, n.value, h=None)) == C.ERR_INVALID_ARGUMENT
+    assert "h" in C.last_error()
+    assert lib.dartree_build_serial(*args(d, n.value, score=ctypes.c_void_p(0x10002))) == C.ERR_INVALID_ARGUMENT
+    assert lib.dartree_build_serial(*args(d, n.value - 1)) == C.ERR_WORKSPACE_TOO_SMALL
+    assert lib.dartree_build_serial(ctypes.byref(d), None, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                    n.value, s) == C.ERR_INVALID_ARGUMENT
+
