@@ -38,6 +38,15 @@ notes of the repository):
       index, then token id.
   R8  mask row i has bit j set iff j == i or node j is an ancestor of i.
   R9  values compare numerically (so -0.0 == +0.0); ties go to the lower id.
+  R10 verification (section 3.2) with a synthetic target: the target's greedy
+      continuation is one token per depth, independent of the draft; a node is
+      accepted when its whole root path matches it.
+  R11 the acceptance length tau counts the accepted draft tokens plus the
+      target's own next token (at least 1).
+  R12 the tree-attention step is one head over the draft nodes only: node i
+      attends to the nodes whose bit is set in mask row i, softmax of the
+      scaled dot products (the prefix's keys, which every node also sees, are
+      left out of this synthetic step).
 """
 from __future__ import annotations
 
@@ -218,6 +227,48 @@ def tree_mask(parent: np.ndarray, n_sel: int, B: int) -> np.ndarray:
             m[i, j // 64] |= np.uint64(1) << np.uint64(j % 64)
             j = int(parent[j])
     return m
+
+
+# ----------------------------------------------------------------------------
+# verification consumer (blog section 3.2: the drafted tree is verified in
+# one target pass under the tree-attention mask), with a synthetic target
+# ----------------------------------------------------------------------------
+def accept_longest(tok: np.ndarray, depth: np.ndarray, parent: np.ndarray, n_sel: int,
+                   target: np.ndarray):
+    """Greedy verification against a target continuation target[0..L-1]
+    (target[d-1] is the target's token at depth d): a node is accepted iff its
+    token equals the target's at its depth and its parent is the anchor or
+    accepted (R10). Every root path is enumerated and compared token by token.
+    Returns (tau, nodes): tau = 1 + the depth of the deepest accepted node
+    (the accepted draft tokens plus the target's own next token, R11); nodes =
+    the emitted indices along the accepted path, depth 1 first."""
+    best = []
+    for i in range(n_sel):
+        path = []
+        j = i
+        while j >= 0:
+            path.append(j)
+            j = int(parent[j])
+        path.reverse()
+        if all(int(tok[v]) == int(target[k]) for k, v in enumerate(path)) and len(path) > len(best):
+            best = path
+    return 1 + len(best), best
+
+
+def tree_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, mask: np.ndarray, n_sel: int) -> np.ndarray:
+    """One attention step over the draft nodes under the tree mask (R12):
+    out[i] = sum_j softmax_j(<Q[i], K[j]> / sqrt(dh)) V[j] over the j whose
+    bit is set in mask row i (the node and its ancestors); rows >= n_sel are 0.
+    Q, K, V: [B][dh]; mask: uint64[B][ceil(B/64)]."""
+    B, dh = Q.shape
+    out = np.zeros((B, dh))
+    for i in range(n_sel):
+        js = [j for j in range(B) if (int(mask[i, j // 64]) >> (j % 64)) & 1]
+        s = np.array([np.dot(Q[i], K[j]) for j in js]) / np.sqrt(dh)
+        w = np.exp(s - s.max())
+        w /= w.sum()
+        out[i] = sum(wk * V[j] for wk, j in zip(w, js))
+    return out
 
 
 # ----------------------------------------------------------------------------

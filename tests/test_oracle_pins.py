@@ -438,3 +438,72 @@ def test_planted_mistakes_are_caught(name):
 
 def test_unmutated_oracle_passes_pin_set():
     _run_pins()
+
+
+# ---- verification consumer (blog section 3.2; readings R10-R12) -------------
+def _hand_tree():
+    # emitted breadth-first: 0:(5,d1) 1:(7,d1) 2:(3,d2,p0) 3:(9,d2,p0) 4:(3,d2,p1) 5:(4,d3,p4)
+    tok = np.array([5, 7, 3, 9, 3, 4, -1, -1])
+    dep = np.array([1, 1, 2, 2, 2, 3, 0, 0])
+    par = np.array([-1, -1, 0, 0, 1, 4, -2, -2])
+    return tok, dep, par, 6
+
+
+@pytest.mark.parametrize("target,tau,nodes", [
+    ([7, 3, 4, 8], 4, [1, 4, 5]),   # the whole deepest path, then the bonus token
+    ([5, 3, 1, 1], 3, [0, 2]),
+    ([2, 3, 4, 8], 1, []),          # nothing accepted: the target's own token only
+    ([7, 9, 4, 8], 2, [1]),         # 9 sits under node 0, not under the accepted node 1
+])
+def test_accept_longest_hand_tree(target, tau, nodes):
+    tok, dep, par, n = _hand_tree()
+    t, path = O.accept_longest(tok, dep, par, n, np.array(target))
+    assert t == tau and path == nodes
+
+
+def _random_tree(rng, n, B):
+    par = np.full(B, -2)
+    for i in range(n):
+        par[i] = -1 if i < 3 else int(rng.integers(-1, i))
+    return par
+
+
+def test_tree_attention_uniform_scores_give_the_masked_mean():
+    """K = 0: every allowed score is 0, so each row is the plain mean of the V
+    rows its mask allows (computed here as a 0/1 matrix product)."""
+    rng = np.random.default_rng(5)
+    B, n, dh = 24, 20, 16
+    par = _random_tree(rng, n, B)
+    mask = O.tree_mask(par, n, B)
+    M = np.array([[(int(mask[i, j // 64]) >> (j % 64)) & 1 for j in range(B)] for i in range(B)], float)
+    Q, V = rng.standard_normal((B, dh)), rng.standard_normal((B, dh))
+    out = O.tree_attention(Q, np.zeros((B, dh)), V, mask, n)
+    exp = (M @ V)[:n] / M.sum(axis=1)[:n, None]
+    assert np.allclose(out[:n], exp, atol=1e-12)
+    assert np.all(out[n:] == 0)
+
+
+def test_tree_attention_depth_one_nodes_see_only_themselves():
+    rng = np.random.default_rng(6)
+    B, n, dh = 16, 12, 8
+    par = _random_tree(rng, n, B)
+    mask = O.tree_mask(par, n, B)
+    Q, K, V = (rng.standard_normal((B, dh)) for _ in range(3))
+    out = O.tree_attention(Q, K, V, mask, n)
+    for i in range(n):
+        if par[i] == -1:
+            assert np.array_equal(out[i], V[i])
+
+
+def test_tree_attention_scale_is_one_over_sqrt_dh():
+    """Duplicating every column of Q and K doubles the dot products while dh
+    doubles, so the logits grow by sqrt(2): the same as scaling Q and K by
+    2^(1/4) at the original width."""
+    rng = np.random.default_rng(7)
+    B, n, dh = 16, 14, 8
+    par = _random_tree(rng, n, B)
+    mask = O.tree_mask(par, n, B)
+    Q, K, V = (rng.standard_normal((B, dh)) for _ in range(3))
+    wide = O.tree_attention(np.hstack([Q, Q]), np.hstack([K, K]), np.hstack([V, V]), mask, n)[:, :dh]
+    scaled = O.tree_attention(Q * 2 ** 0.25, K * 2 ** 0.25, V, mask, n)
+    assert np.allclose(wide, scaled, atol=1e-12)
