@@ -240,6 +240,9 @@ def main():
     serial = None
     if not args.no_serial and cfg.B <= 511:
         serial = serial_vs_deferred(cfg, dims, dhead, logits[0], hin[0], rb, kern_us["tree_kernel"], us_round)
+    verify = None
+    if not args.no_serial:
+        verify = verify_step(cfg, dims, rb)
 
     # ---- CPU oracle baseline on a bounded sample -------------------------------
     cpu = None
@@ -269,6 +272,7 @@ def main():
         "roofline_scan_stress": scan_stress,
         "roofline_head_stress": head_stress,
         "serial_heap": serial,
+        "verify_step": verify,
         "kernels": kernels,
         "stage_timing": event_kind,
         "plan": info,
@@ -339,6 +343,37 @@ def serial_vs_deferred(cfg, dims, dhead, logits, hin, rb, tree_us, round_us, n_t
             "serial_over_deferred_tree": round(us / tree_us, 2),
             "pages_context": "whole draft rounds with real models on an RTX 6000 Ada: 62.7 ms serial vs 28.5 ms "
                              "deferred (2.2x)"}
+
+
+def verify_step(cfg, dims, rb, dh=128, n_timed=32):
+    """dartree_verify_tree on the round last built into rb: acceptance against
+    a random synthetic target and one tree-attention head (dh = 128) over the
+    B draft nodes."""
+    import numpy as np
+    import torch
+
+    from diffusion_drafter_tree_amd import ops
+
+    n, L, B = cfg.n_req, cfg.L, cfg.B
+    rng = np.random.default_rng(3)
+    target = ops.to_device(rng.integers(0, cfg.V, (n, L)).astype(np.int32))
+    Q, K, V = (ops.to_device(rng.standard_normal((n, B, dh)).astype(np.float32)) for _ in range(3))
+    acc_len = torch.zeros((n,), dtype=torch.int32, device="cuda")
+    acc_nodes = torch.zeros((n, L), dtype=torch.int32, device="cuda")
+    out = torch.zeros((n, B, dh), dtype=torch.float32, device="cuda")
+    call = lambda: ops.verify_tree(dims, rb.n_sel, rb.tok, rb.depth, rb.parent, rb.mask, target, Q, K, V, acc_len,
+                                   acc_nodes, out)
+    for _ in range(3):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n_timed):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return {"kernel": "verify_kernel (acceptance + one tree-attention head)", "dh": dh,
+            "us": round(e0.elapsed_time(e1) * 1000.0 / n_timed, 2)}
 
 
 def head_at_stress_shape(n_timed=16):

@@ -523,4 +523,45 @@ dartree_status dartree_build_serial(const dartree_dims* dims, const dartree_head
   return DARTREE_OK;
 }
 
+dartree_status dartree_verify_tree(const dartree_dims* dims, const int32_t* n_sel, const int32_t* tok,
+                                   const int32_t* depth, const int32_t* parent, const uint64_t* mask,
+                                   const int32_t* target, const float* Q, const float* K, const float* V, int32_t dh,
+                                   int32_t* accepted_len, int32_t* accepted_nodes, float* attn_out, void* stream) {
+  g_err[0] = 0;
+  TRY(check_dims(dims));
+  if (dh < 1 || dh > 256) return fail(DARTREE_ERR_UNSUPPORTED, "dh=%d outside 1..256", dh);
+  REQ_PTR(n_sel, 4);
+  REQ_PTR(tok, 4);
+  REQ_PTR(depth, 4);
+  REQ_PTR(parent, 4);
+  REQ_PTR(mask, 8);
+  REQ_PTR(target, 4);
+  REQ_PTR(Q, 4);
+  REQ_PTR(K, 4);
+  REQ_PTR(V, 4);
+  REQ_PTR(accepted_len, 4);
+  REQ_PTR(accepted_nodes, 4);
+  REQ_PTR(attn_out, 4);
+  dartree::VerifyArgs a{};
+  a.n_req = dims->n_req;
+  a.L = dims->L;
+  a.B = dims->B;
+  a.dh = dh;
+  a.n_sel = n_sel;
+  a.tok = tok;
+  a.depth = depth;
+  a.parent = parent;
+  a.mask = mask;
+  a.target = target;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.acc_len = accepted_len;
+  a.acc_nodes = accepted_nodes;
+  a.out = attn_out;
+  hipError_t e = dartree::launch_verify(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "verify launch");
+  return DARTREE_OK;
+}
+
 }  // extern "C"

@@ -118,6 +118,24 @@ struct SerialArgs {
   float* score;               // [n][B]: s_beta
 };
 hipError_t launch_serial(const SerialArgs& a, bool bf16w, hipStream_t s);
+
+// ---- verification consumer with a synthetic target -----------------------------
+struct VerifyArgs {
+  int n_req, L, B, dh;
+  const int32_t* n_sel;       // [n]
+  const int32_t* tok;         // [n][B] emitted tree
+  const int32_t* depth;       // [n][B]
+  const int32_t* parent;      // [n][B]
+  const uint64_t* mask;       // [n][B][ceil(B/64)]
+  const int32_t* target;      // [n][L]
+  const float* Q;             // [n][B][dh]
+  const float* K;
+  const float* V;
+  int32_t* acc_len;           // [n]
+  int32_t* acc_nodes;         // [n][L]
+  float* out;                 // [n][B][dh]
+};
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_fill_u32(void* p, size_t n_words, uint32_t value, hipStream_t s);
 
 }  // namespace dartree

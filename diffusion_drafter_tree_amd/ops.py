@@ -219,6 +219,16 @@ def build_serial(dims: C.Dims, head: DeviceHead, cand_ids: torch.Tensor, cand_lo
            "build_serial")
 
 
+def verify_tree(dims: C.Dims, n_sel: torch.Tensor, tok: torch.Tensor, depth: torch.Tensor, parent: torch.Tensor,
+                mask: torch.Tensor, target: torch.Tensor, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                accepted_len: torch.Tensor, accepted_nodes: torch.Tensor, attn_out: torch.Tensor, stream=None):
+    """The verification consumer through dartree_verify_tree."""
+    _check(C.load().dartree_verify_tree(ctypes.byref(dims), _p(n_sel), _p(tok), _p(depth), _p(parent), _p(mask),
+                                        _p(target), _p(Q), _p(K), _p(V), int(Q.shape[-1]), _p(accepted_len),
+                                        _p(accepted_nodes), _p(attn_out), _stream(stream)),
+           "verify_tree")
+
+
 def set_stage_events(events: Optional[list]):
     """Profiling hook: record the given four torch.cuda.Event objects around the
     stages of every following build_round on this thread (scan, merge, tree

@@ -242,6 +242,30 @@ dartree_status dartree_build_serial(const dartree_dims* dims, const dartree_head
                                     int32_t* depth, int32_t* parent, float* score, void* ws, size_t ws_bytes,
                                     void* stream);
 
+/* Verification consumer of an emitted tree with a synthetic target
+ * (marsggbo blog, section 3.2: the target verifies the drafted tree in one
+ * pass under the tree-attention mask and keeps the longest root path it
+ * agrees with). Per request:
+ *   acceptance  target[n][L] int32 is the target's continuation (its token at
+ *               depth d is target[d-1]); a node is accepted iff its token equals
+ *               the target's at its depth and its parent is the anchor (-1) or
+ *               accepted. accepted_len[n] = 1 + the depth of the deepest
+ *               accepted node (the target's own next token counts);
+ *               accepted_nodes[n][L] = the emitted indices along that path,
+ *               depth 1 first, -1 past its end.
+ *   attention   one head over the draft nodes: attn_out[i] = sum_j
+ *               softmax_j(<Q[i], K[j]> / sqrt(dh)) V[j] over the j whose bit
+ *               is set in mask row i (dartree_tree_mask layout: the node and its
+ *               ancestors); rows >= n_sel are zero. Q, K, V, attn_out are
+ *               [n][B][dh] fp32, 1 <= dh <= 256 (UNSUPPORTED otherwise).
+ * The tree (n_sel, tok, depth, parent, mask) is an emitted round
+ * (dartree_build_round, or dartree_select_topB + dartree_tree_mask); parent
+ * indices below their node's, as emitted. Device pointers, caller-owned. */
+dartree_status dartree_verify_tree(const dartree_dims* dims, const int32_t* n_sel, const int32_t* tok,
+                                   const int32_t* depth, const int32_t* parent, const uint64_t* mask,
+                                   const int32_t* target, const float* Q, const float* K, const float* V, int32_t dh,
+                                   int32_t* accepted_len, int32_t* accepted_nodes, float* attn_out, void* stream);
+
 /* Profiling hook (not part of a round's computation). When set, every
  * following dartree_build_round on this thread records events[0] before its
  * first launch, events[1] after the logits scan (with the head tiles),

@@ -227,3 +227,19 @@ def test_serial_builder_validates_on_host(lib):
     assert lib.dartree_build_serial(ctypes.byref(d), None, fake, fake, fake, fake, fake, fake, fake, fake, fake,
                                     n.value, s) == C.ERR_INVALID_ARGUMENT
 
+
+def test_verify_tree_validates_on_host(lib):
+    """dartree_verify_tree: dh outside 1..256, NULL or misaligned pointers
+    are rejected before any launch."""
+    d = dims()
+    f = ctypes.c_void_p(0x10000)
+    s = ctypes.c_void_p(None)
+    call = lambda dh, mask=f, q=f: lib.dartree_verify_tree(ctypes.byref(d), f, f, f, f, mask, f, q, f, f, dh, f, f,
+                                                           f, s)
+    assert call(0) == C.ERR_UNSUPPORTED
+    assert call(257) == C.ERR_UNSUPPORTED
+    assert call(128, q=None) == C.ERR_INVALID_ARGUMENT
+    assert "Q" in C.last_error()
+    assert call(128, mask=ctypes.c_void_p(0x10004)) == C.ERR_INVALID_ARGUMENT
+    assert "aligned" in C.last_error()
+

@@ -317,6 +317,53 @@ def test_serial_equals_deferred_when_width_covers_budget():
         assert pd == ps, (q, sorted(pd ^ ps)[:4])
 
 
+@pytest.mark.parametrize("name,dh", [("tiny", 64), ("verify_bf16", 100), ("qwen3_4b", 128)])
+def test_verify_tree_against_oracle(name, dh):
+    """dartree_verify_tree on emitted rounds: acceptance length and path exact
+    against the oracle's path enumeration, for targets taken from a random
+    emitted path (then random tokens) and for random targets; the attention
+    step within 1e-4 of the oracle's masked softmax."""
+    cfg = I.CONFIGS["tiny"] if name == "tiny" else (
+        I.small_variant("qwen3_4b", name="verify_bf16", n_req=3, V=60000, L=6, K=64, W=12, B=32, r=256, D=256)
+        if name == "verify_bf16" else I.CONFIGS["qwen3_4b"])
+    say(f"case verify {cfg.name} n={cfg.n_req} B={cfg.B} dh={dh}")
+    hd, dhd = device_head(cfg)
+    rnd = I.make_round(cfg, 0, 0)
+    rb = ops.RoundBuffers(cfg)
+    ops.build_round(rb.dims, dhd, ops.to_device(rnd.logits), ops.to_device(rnd.H if cfg.D > 0 else rnd.h), rb)
+    torch.cuda.synchronize()
+    e = rb.numpy()
+    rng = np.random.default_rng(dh)
+    n, L, B = cfg.n_req, cfg.L, cfg.B
+    Q, K, V = (rng.standard_normal((n, B, dh)).astype(np.float32) for _ in range(3))
+    for mode in ("path", "random"):
+        target = rng.integers(0, cfg.V, (n, L)).astype(np.int32)
+        if mode == "path":
+            for q in range(n):
+                ns = int(e["n_sel"][q])
+                v = int(rng.integers(0, ns))
+                while v >= 0:
+                    target[q, int(e["depth"][q, v]) - 1] = int(e["tok"][q, v])
+                    v = int(e["parent"][q, v])
+        acc_len = torch.zeros((n,), dtype=torch.int32, device="cuda")
+        acc_nodes = torch.zeros((n, L), dtype=torch.int32, device="cuda")
+        out = torch.zeros((n, B, dh), dtype=torch.float32, device="cuda")
+        ops.verify_tree(rb.dims, rb.n_sel, rb.tok, rb.depth, rb.parent, rb.mask, ops.to_device(target),
+                        ops.to_device(Q), ops.to_device(K), ops.to_device(V), acc_len, acc_nodes, out)
+        torch.cuda.synchronize()
+        gl, gn, go = acc_len.cpu().numpy(), acc_nodes.cpu().numpy(), out.cpu().numpy()
+        for q in range(n):
+            ns = int(e["n_sel"][q])
+            tau, path = O.accept_longest(e["tok"][q], e["depth"][q], e["parent"][q], ns, target[q])
+            assert int(gl[q]) == tau, (mode, q, int(gl[q]), tau)
+            assert gn[q].tolist() == path + [-1] * (L - len(path)), (mode, q)
+            ref = O.tree_attention(Q[q].astype(np.float64), K[q].astype(np.float64), V[q].astype(np.float64),
+                                   e["mask"][q], ns)
+            err = float(np.max(np.abs(go[q].astype(np.float64) - ref)))
+            assert err <= TOL, (mode, q, err)
+        say(f"  {mode}: tau {gl.tolist()}")
+
+
 def test_topk_small_and_ragged_rows():
     rng = np.random.default_rng(7)
     for V, K in [(1, 1), (7, 7), (9, 3), (4099, 64), (8192, 64), (8193, 100), (16385, 1024), (24577, 17)]:
