@@ -175,12 +175,13 @@ def replay_supertree(gst: GpuSupertree, cand_ids, cand_vals, h, A, E, U, W, beta
 
 
 def check_selection(levels: List[List[O.Node]], gst: GpuSupertree, sel: GpuSelection, B: int, tol: float,
-                    where="") -> Report:
-    """Global top-B over the replayed supertree, emission, and mask."""
+                    where="", budget: Optional[int] = None) -> Report:
+    """Global top-B over the replayed supertree, emission, and mask. ``B`` is
+    the output stride; ``budget`` (default B) the number of nodes to select."""
     rep = Report()
     pool = [nd for lvl in levels[1:] for nd in lvl]
     pool_sorted = sorted(pool, key=lambda nd: O.node_key(nd.sbeta, nd.depth, nd.tok, nd.parent_slot))
-    n_exp = min(B, len(pool))
+    n_exp = min(B if budget is None else budget, len(pool))
     if int(sel.n_sel) != n_exp:
         _fail(f"{where}: n_sel {sel.n_sel}, expected {n_exp}")
     n = n_exp
@@ -235,12 +236,14 @@ def check_selection(levels: List[List[O.Node]], gst: GpuSupertree, sel: GpuSelec
 
 
 def check_round(cfg, head, rnd, gpu: Dict[str, np.ndarray], tol: float = 1e-4,
-                oracle_h: Optional[np.ndarray] = None, requests=None) -> Report:
+                oracle_h: Optional[np.ndarray] = None, requests=None, widths=None, budgets=None) -> Report:
     """Full-round parity for every request. ``gpu`` holds numpy copies of the
     HIP path's outputs: cand_ids, cand_logit [n][L][K]; h [n][L][r] (when
     D > 0); st_tok, st_parent, st_cum, st_sbeta [n][L][W]; st_count [n][L];
     n_sel [n]; tok, depth, parent, score, slot [n][B]; mask [n][B][words].
-    ``requests`` restricts the check to a sample of requests."""
+    ``requests`` restricts the check to a sample of requests; ``widths`` and
+    ``budgets`` give per-request W_q and B_q (default cfg.W and cfg.B; the
+    output strides stay cfg.W and cfg.B)."""
     wd = head.dtype
     A, E, U = O.widen(head.A, wd), O.widen(head.E, wd), O.widen(head.U, wd)
     qs = list(range(cfg.n_req)) if requests is None else list(requests)
@@ -263,7 +266,9 @@ def check_round(cfg, head, rnd, gpu: Dict[str, np.ndarray], tol: float = 1e-4,
         vals = np.asarray(gpu["cand_logit"][q], np.float64)
         gst = GpuSupertree(tok=gpu["st_tok"][q], parent_slot=gpu["st_parent"][q], cum=gpu["st_cum"][q],
                            sbeta=gpu["st_sbeta"][q], count=gpu["st_count"][q])
-        levels, r1 = replay_supertree(gst, ids, vals, h_all[q], A, E, U, cfg.W, cfg.beta, tol, where=where)
+        wq = cfg.W if widths is None else int(widths[q])
+        bq = cfg.B if budgets is None else int(budgets[q])
+        levels, r1 = replay_supertree(gst, ids, vals, h_all[q], A, E, U, wq, cfg.beta, tol, where=where)
         rep.merge(r1)
         if "n_sel" in gpu:
             sel = GpuSelection(n_sel=int(gpu["n_sel"][q]), tok=gpu["tok"][q], depth=gpu["depth"][q],
@@ -272,5 +277,5 @@ def check_round(cfg, head, rnd, gpu: Dict[str, np.ndarray], tol: float = 1e-4,
             for i in range(sel.n_sel, cfg.B):
                 if not (sel.tok[i] == -1 and sel.depth[i] == 0 and sel.parent[i] == -2 and sel.slot[i] == -1):
                     _fail(f"{where}: padding wrong at {i}")
-            rep.merge(check_selection(levels, gst, sel, cfg.B, tol, where))
+            rep.merge(check_selection(levels, gst, sel, cfg.B, tol, where, budget=bq))
     return rep

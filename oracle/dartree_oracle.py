@@ -47,6 +47,11 @@ notes of the repository):
       attends to the nodes whose bit is set in mask row i, softmax of the
       scaled dot products (the prefix's keys, which every node also sees, are
       left out of this synthetic step).
+  R13 the Markov head of section 4.3 (Table 3), whose architecture the pages
+      do not state, is the synthetic head with A = 0: a node's state is
+      tanh(E[u] + h_d), so its children's distribution depends on its token
+      (and its depth) alone. The oracle takes it as A = 0; nothing else
+      changes.
 """
 from __future__ import annotations
 

@@ -308,6 +308,58 @@ def test_deferred_equals_serial_heap_when_W_ge_B(seed, beta):
     assert np.allclose([n.sbeta for n in deferred], [n.sbeta for n in serial], atol=1e-12)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_budgets_nest_and_stay_prefix_closed(seed):
+    """A per-request budget b <= B selects the first b nodes of the budget-B
+    ranking (the comparator is a total order), and every such prefix is an
+    ancestor-closed tree for beta <= 0 (Lemma 1 at each budget); the b-node
+    tree is what b best-first heap pops give."""
+    logits, h, A, E, U = rand_problem(500 + seed, V=30, L=5, K=5, ties=(seed % 2 == 0))
+    ids, vals = cands(logits, 5)
+    levels = O.build_supertree(ids, vals, h, A, E, U, W=4, beta=-0.2)
+    full = O.select_topB(levels, 18)
+    for b in range(1, 19):
+        sel = O.select_topB(levels, b)
+        assert [(n.depth, n.slot) for n in sel] == [(n.depth, n.slot) for n in full[:b]]
+        assert [(n.depth, n.slot) for n in O.heap_materialized(levels, b)] == [(n.depth, n.slot) for n in sel]
+        keys = set((n.depth, n.slot) for n in sel)
+        for n in sel:
+            assert n.depth == 1 or (n.depth - 1, n.parent_slot) in keys
+
+
+def _same_token_parent_pairs(levels):
+    """(equal, differing) counts over pairs of kept nodes of one depth whose
+    parents differ but carry the same token, comparing the child's log q."""
+    eq = diff = 0
+    for d in range(2, len(levels)):
+        seen = {}
+        for nd in levels[d]:
+            p = levels[d - 1][nd.parent_slot]
+            key, lq = (p.tok, nd.tok), nd.cum - p.cum
+            if key in seen and seen[key][0] != nd.parent_slot:
+                if abs(seen[key][1] - lq) <= 1e-12:
+                    eq += 1
+                else:
+                    diff += 1
+            seen.setdefault(key, (nd.parent_slot, lq))
+    return eq, diff
+
+
+def test_markov_head_children_depend_on_parent_token_only():
+    """The Markov-head variant (the child distribution conditioned on the
+    parent token only) is the head with A = 0: then two parents of one depth
+    with the same token give every child the same log q. With the recurrence
+    (A != 0) the parent's path matters and such pairs differ."""
+    logits, h, A, E, U = rand_problem(91, V=12, L=5, K=6, r=6)
+    ids, vals = cands(logits, 6)
+    lv0 = O.build_supertree(ids, vals, h, np.zeros_like(A), E, U, W=20, beta=-0.1)
+    eq, diff = _same_token_parent_pairs(lv0)
+    assert eq > 0 and diff == 0
+    lv1 = O.build_supertree(ids, vals, h, A, E, U, W=20, beta=-0.1)
+    eq, diff = _same_token_parent_pairs(lv1)
+    assert diff > 0
+
+
 def test_whole_supertree_selected_when_WL_le_B():
     logits, h, A, E, U = rand_problem(77, V=30, L=5, K=6)
     W, L = 3, 5
