@@ -38,6 +38,8 @@ def parse():
                     help="skip the logits scan measured at the 64-request shape (311 MB of logits a round)")
     ap.add_argument("--no-serial", action="store_true",
                     help="skip timing the heap-serial construction against the deferred tree kernel")
+    ap.add_argument("--no-sizes", action="store_true",
+                    help="skip the per-request width/budget timing (four requests of the config)")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="if > 0: run only this many eager rounds (for rocprofv3) and exit")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -243,6 +245,11 @@ def main():
     verify = None
     if not args.no_serial:
         verify = verify_step(cfg, dims, rb)
+    sizes = None
+    markov = None
+    if not args.no_sizes:
+        sizes = request_sizes(cfg)
+        markov = markov_head(cfg, head, logits[0], hin[0])
 
     # ---- CPU oracle baseline on a bounded sample -------------------------------
     cpu = None
@@ -273,6 +280,8 @@ def main():
         "roofline_head_stress": head_stress,
         "serial_heap": serial,
         "verify_step": verify,
+        "request_sizes": sizes,
+        "markov_head": markov,
         "kernels": kernels,
         "stage_timing": event_kind,
         "plan": info,
@@ -343,6 +352,71 @@ def serial_vs_deferred(cfg, dims, dhead, logits, hin, rb, tree_us, round_us, n_t
             "serial_over_deferred_tree": round(us / tree_us, 2),
             "pages_context": "whole draft rounds with real models on an RTX 6000 Ada: 62.7 ms serial vs 28.5 ms "
                              "deferred (2.2x)"}
+
+
+def request_sizes(cfg, n_timed=64):
+    """dartree_build_round on four requests of the config in one batch, every
+    request at the config's (W, B) against per-request widths and budgets
+    (W, 2W/3, W/3, W/6 and B, 3B/4, B/2, B/4): the serving knob of choosing
+    the tree size per request inside one batch."""
+    import torch
+
+    from diffusion_drafter_tree_amd import inputs as I
+    from diffusion_drafter_tree_amd import ops
+
+    c4 = cfg.with_(n_req=4, name=cfg.name + "_x4")
+    dh = ops.DeviceHead(I.make_head(c4, 0))
+    rnd = I.make_round(c4, 0, 0)
+    logits = ops.to_device(rnd.logits)
+    hin = ops.to_device(rnd.H if c4.D > 0 else rnd.h)
+    W, B = c4.W, c4.B
+    widths = [W, max(1, 2 * W // 3), max(1, W // 3), max(1, W // 6)]
+    budgets = [B, max(1, 3 * B // 4), max(1, B // 2), max(1, B // 4)]
+    res = {"requests": 4, "widths": widths, "budgets": budgets}
+    for label, wb in (("uniform_us", None), ("per_request_us", (widths, budgets))):
+        rb = ops.RoundBuffers(c4)
+        if wb is not None:
+            rb.set_request_sizes(torch.tensor(wb[0], dtype=torch.int32, device="cuda"),
+                                 torch.tensor(wb[1], dtype=torch.int32, device="cuda"))
+        for _ in range(3):
+            ops.build_round(rb.dims, dh, logits, hin, rb)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n_timed):
+            ops.build_round(rb.dims, dh, logits, hin, rb)
+        e1.record()
+        torch.cuda.synchronize()
+        res[label] = round(e0.elapsed_time(e1) * 1000.0 / n_timed, 2)
+        if wb is not None:
+            res["n_sel"] = rb.n_sel.cpu().tolist()
+    res["launch"] = "eager build_round calls, one workgroup a request"
+    return res
+
+
+def markov_head(cfg, head, logits, hin, n_timed=128):
+    """dartree_build_round with the Markov-head variant (no A: the kernels skip
+    the A s_parent contraction) against the same round with the full head."""
+    import torch
+
+    from diffusion_drafter_tree_amd import ops
+
+    res = {}
+    for label, markov in (("full_head_us", False), ("markov_head_us", True)):
+        dh = ops.DeviceHead(head, markov=markov)
+        rb = ops.RoundBuffers(cfg)
+        for _ in range(3):
+            ops.build_round(rb.dims, dh, logits, hin, rb)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n_timed):
+            ops.build_round(rb.dims, dh, logits, hin, rb)
+        e1.record()
+        torch.cuda.synchronize()
+        res[label] = round(e0.elapsed_time(e1) * 1000.0 / n_timed, 2)
+    res["launch"] = "eager build_round calls on one round"
+    return res
 
 
 def verify_step(cfg, dims, rb, dh=128, n_timed=32):

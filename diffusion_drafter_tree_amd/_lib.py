@@ -39,7 +39,8 @@ class RoundInfo(ctypes.Structure):
 
 class Supertree(ctypes.Structure):
     _fields_ = [("tok", c_void_p), ("parent_slot", c_void_p), ("cum", c_void_p), ("sbeta", c_void_p),
-                ("count", c_void_p), ("state", c_void_p), ("next_depth", c_int32)]
+                ("count", c_void_p), ("state", c_void_p), ("next_depth", c_int32),
+                ("width", c_void_p), ("budget", c_void_p)]
 
 
 PD = POINTER(Dims)

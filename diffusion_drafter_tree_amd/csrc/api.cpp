@@ -99,7 +99,7 @@ dartree_status check_ws(const dartree_dims* d, void* ws, size_t ws_bytes, WsLayo
 
 dartree_status check_head(const dartree_dims* d, const dartree_head* h) {
   if (!h) return fail(DARTREE_ERR_INVALID_ARGUMENT, "head is NULL");
-  REQ_PTR(h->A, 16);
+  if (h->A != nullptr) REQ_PTR(h->A, 16);   // NULL: the Markov head (A = 0)
   REQ_PTR(h->E, 16);
   REQ_PTR(h->U, 16);
   (void)d;
@@ -160,6 +160,8 @@ dartree::TreeArgs tree_args(const dartree_dims* dims, const dartree_head* head, 
   a.st_sbeta = st->sbeta;
   a.st_count = st->count;
   a.st_state = st->state;
+  a.w_req = st->width;
+  a.b_req = st->budget;
   a.d0 = d0;
   a.d1 = d1;
   return a;
@@ -223,7 +225,7 @@ const char* dartree_status_string(dartree_status s) {
 
 const char* dartree_last_error(void) { return g_err; }
 
-int32_t dartree_version(void) { return 1; }
+int32_t dartree_version(void) { return 2; }
 
 dartree_status dartree_round_plan(const dartree_dims* dims, dartree_round_info* info) {
   g_err[0] = 0;
@@ -415,8 +417,9 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
   uint64_t* lists = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + w.lists_off);
   dartree::TreePlan tp;
   TRY(plan_round(w, lbf, lists, cand_ids, cand_logit, ta, &tp));
-  uint16_t* a_frag = (tp.mode == 3 && w.afrag_off) ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + w.afrag_off)
-                                                   : nullptr;
+  uint16_t* a_frag = (tp.mode == 3 && w.afrag_off && head->A != nullptr)
+                         ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + w.afrag_off)
+                         : nullptr;
   ta.a_frag = a_frag;
   // launch 1: the logits scan, with the head projection tiles riding along
   dartree::ScanArgs sa{};
@@ -483,7 +486,7 @@ dartree_status dartree_build_serial(const dartree_dims* dims, const dartree_head
     return fail(DARTREE_ERR_UNSUPPORTED, "heap-serial construction: B=%d exceeds %d", dims->B, dartree::kSerialMaxB);
   if (!head) return fail(DARTREE_ERR_INVALID_ARGUMENT, "head is NULL");
   const int wa = dims->weight_dtype == DARTREE_BF16 ? 2 : 4;
-  REQ_PTR(head->A, wa);
+  if (head->A != nullptr) REQ_PTR(head->A, wa);   // NULL: the Markov head (A = 0)
   REQ_PTR(head->E, wa);
   REQ_PTR(head->U, wa);
   REQ_PTR(cand_ids, 4);

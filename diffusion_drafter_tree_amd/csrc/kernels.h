@@ -74,6 +74,8 @@ struct TreeArgs {
   float* st_cum;              // [n][L][W]
   float* st_sbeta;            // [n][L][W]
   int32_t* st_count;          // [n][L]
+  const int32_t* w_req;       // [n] per-request width, or null (W for all)
+  const int32_t* b_req;       // [n] per-request budget, or null (B for all)
   float* st_state;            // [n][W][r]
   int d0, d1;                 // depths to expand (d1 < d0: none)
   bool do_select, do_mask;

@@ -254,10 +254,10 @@ __global__ __launch_bounds__(kT) void serial_kernel(SerialArgs a) {
       __syncthreads();
       const float* hd = hq + (size_t)d * r;
       const WT* erow = E + (size_t)(tk < 0 || tk >= a.V ? 0 : tk) * r;
-      rows_dot<WT>(A, nullptr, r, r, r, sm.s_par, sm.part);
+      if (A != nullptr) rows_dot<WT>(A, nullptr, r, r, r, sm.s_par, sm.part);   // no A: the Markov head
       __syncthreads();
       for (int j = tid; j < r; j += kT) {
-        const float v = tanhf(sm.part[j] + ldw(erow, (size_t)j) + hd[j]);
+        const float v = tanhf((A != nullptr ? sm.part[j] : 0.f) + ldw(erow, (size_t)j) + hd[j]);
         sm.s_new[j] = v;
         st[(size_t)(i + 1) * r + j] = v;
       }

@@ -315,8 +315,13 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
   const Lay s = make_lay(lay_off(a.L, a.K, a.W, a.B, a.r, MODE, KQ));
   const int q = blockIdx.x, tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int L = a.L, K = a.K, W = a.W, r = a.r, B = a.B;
+  // this request's width and budget (per-request values clamped to [1, W], [1, B])
+  const int Wq = a.w_req ? min(max(a.w_req[q], 1), W) : W;
+  const int Bq = a.b_req ? min(max(a.b_req[q], 1), B) : B;
   const size_t lw = (size_t)q * L * W;
   const WT* A = static_cast<const WT*>(a.A);
+  // no A: the Markov head, whose states have no recurrence (A s_parent = 0)
+  const bool markov = A == nullptr;
   const WT* E = static_cast<const WT*>(a.E);
   const WT* U = static_cast<const WT*>(a.U);
   const float* hq = a.h + (size_t)q * L * r;
@@ -406,7 +411,8 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
     __syncthreads();   // candidates in LDS
     const uint16_t* arow = reinterpret_cast<const uint16_t*>(A) + (size_t)(w * 16 + (lane & 15)) * r + sub;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) areg[ks] = *reinterpret_cast<const u16x8_t*>(arow + ks * 32);
+    for (int ks = 0; ks < 8; ++ks)
+      areg[ks] = markov ? u16x8_t{0, 0, 0, 0, 0, 0, 0, 0} : *reinterpret_cast<const u16x8_t*>(arow + ks * 32);
     load_u(ureg, a.d0);
     if (a.d0 < L) load_e(a.d0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the LDS-direct loads have landed
@@ -447,7 +453,7 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
           if (pp < Wp) s.Zp[((size_t)z_kq * W + pp) * (K + 4) + k] = acc[i];
         }
       }
-      if (need_state) {
+      if (need_state && !markov) {
         const int p = lane & 15;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -471,10 +477,10 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
       }
     } else if (MODE == 1) {
       z_mfma_general(s, reinterpret_cast<const uint16_t*>(U), Wp, K, r);
-      if (need_state) as_mfma_general(s, reinterpret_cast<const uint16_t*>(A), Wp, r);
+      if (need_state && !markov) as_mfma_general(s, reinterpret_cast<const uint16_t*>(A), Wp, r);
     } else {
       z_valu<WT>(s, U, Wp, K, r);
-      if (need_state) as_valu<WT>(s, A, Wp, r);
+      if (need_state && !markov) as_valu<WT>(s, A, Wp, r);
     }
     __syncthreads();
 
@@ -547,8 +553,8 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
     __syncthreads();
     const uint32_t thr = s.misc[4] ? 0u : ~(uint32_t)s.misc[2];
     int ns = select_compact<EPT>(keys, pays, thr, sel);
-    if (ns > kSelCap) ns = select_exact<EPT>(keys, pays, W, sel);
-    const int nk = select_rank(ns, W, sel);
+    if (ns > kSelCap) ns = select_exact<EPT>(keys, pays, Wq, sel);
+    const int nk = select_rank(ns, Wq, sel);
 
     // ---- the new level --------------------------------------------------------
     const size_t orow = lw + (size_t)(d - 1) * W;
@@ -598,7 +604,7 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
           ev = ldw(E, (size_t)s.lv_tok[row0 + sl] * r + j);
           hv = hd[j];
         }
-        const float v = tanhf((s.AS[(size_t)ps * (r + 1) + j] + ev) + hv);
+        const float v = tanhf(((markov ? 0.f : s.AS[(size_t)ps * (r + 1) + j]) + ev) + hv);
         if (MODE == 2) split_store(s, r, sl, j, v);
         else s.Sf[sl * (r + 1) + j] = v;
         if (d == a.d1) st_out[i] = v;
@@ -642,7 +648,7 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
       }
     }
   }
-  const int n = block_select<2>(keys, pays, B, 32, sel);
+  const int n = block_select<2>(keys, pays, Bq, 32, sel);
   for (int rr = tid; rr < n; rr += kT) {
     const int i = s.opay[rr];
     s.eidx[i] = 0;

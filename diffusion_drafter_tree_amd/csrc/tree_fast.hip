@@ -234,14 +234,21 @@ __device__ __forceinline__ uint32_t group_sum(uint32_t c, int G) {
   return c;
 }
 
-template <int KC>
+template <int KC, bool MARKOV>
 __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   using C = FX<KC>;
   const FLay s = make_flay<KC>(voff(a.L, KC, a.W, a.B, C::fixed));
   const int q = blockIdx.x, tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int L = a.L, W = a.W, B = a.B;
+  // this request's width and budget (per-request values clamped to [1, W], [1, B])
+  const int Wq = a.w_req ? min(max(a.w_req[q], 1), W) : W;
+  const int Bq = a.b_req ? min(max(a.b_req[q], 1), B) : B;
   const size_t lw = (size_t)q * L * W;
   const uint16_t* A = static_cast<const uint16_t*>(a.A);
+  // MARKOV (no A): the Markov head, whose states have no recurrence
+  // (A s_parent = 0); a separate instantiation, so the full head's code is
+  // untouched by the variant
+  constexpr bool markov = MARKOV;
   const uint16_t* E = static_cast<const uint16_t*>(a.E);
   const uint16_t* U = static_cast<const uint16_t*>(a.U);
   const float* hq = a.h + (size_t)q * L * RT;
@@ -347,7 +354,12 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
   }
   // A fragments: 1 KB contiguous runs of the fp16 copy the scan launch
   // staged, or (without it) 16 rows x 16 bytes of A per load, converted below
-  if (expand && a.a_frag) {
+  if constexpr (markov) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) araw[t][i] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  } else if (expand && a.a_frag) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -498,7 +510,7 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
           s.Zp[(z_kq * 16 + (lane >> 4) * 4 + i) * C::ZSTR + z_nt * 16 + (lane & 15)] = zacc[i];
       }
       __builtin_amdgcn_sched_barrier(0);   // the Z results go out before the A*S work is issued
-      if (need_state) {
+      if (need_state && !markov) {
         as_mfma(std::integral_constant<int, 0>{}, f[0]);
         if constexpr (C::KSQ > 1) as_mfma(std::integral_constant<int, 1>{}, f[C::KSQ > 1 ? 1 : 0]);
       }
@@ -557,7 +569,7 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       }
       level_lex_wave(s, d - 1, W, Wp, tk, ps);
     }
-    if (need_state && w != 0) as_finish();
+    if (need_state && !markov && w != 0) as_finish();
     load_u1(min(d + 1, a.d1), 0);
     lds_sync();
 
@@ -573,7 +585,7 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
     }
     if (C::KSQ > 1) load_u1(min(d + 1, a.d1), 1);
     lds_sync();
-    const int nk = min(W, Wp * KC);
+    const int nk = min(Wq, Wp * KC);
     {
       // G = 2^lg threads per survivor (up to 16), as many as eight waves hold:
       // every instruction a wave executes takes its SIMD's issue cycles, so a
@@ -602,7 +614,7 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
         }
       }
       const int rk = wave_ranks ? (int)group_sum(cnt, G) : W;
-      if (x < ns && seg == 0 && rk < W) {
+      if (x < ns && seg == 0 && rk < Wq) {
         const uint32_t lo = ~(uint32_t)kx;
         const int k = lo & 63, p = (lo >> 6) & 15;
         const int row = (d - 1) * W + rk;
@@ -617,7 +629,7 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       // the other parity's bound and count are free again (read one depth ago)
       if (tid < 2) s.misc[(par ^ 1) + 2 * tid] = 0;
     }
-    if (need_state && w == 0) as_finish();
+    if (need_state && !markov && w == 0) as_finish();
     // this depth's staged E/h rows into LDS, then the next depth's first E share
     store_e();
     load_e1(min(d + 1, L), 0);
@@ -628,9 +640,12 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       const uint32_t lo = ~(uint32_t)s.win[w];
       const int k = lo & 63, p = (lo >> 6) & 15;
       const int j0 = lane * 4;
-      const f32x4_t a0 = *reinterpret_cast<const LDS f32x4_t*>(s.AS + p * ASTR + j0);
-      const f32x4_t a1 = *reinterpret_cast<const LDS f32x4_t*>(s.AS + (16 + p) * ASTR + j0);
-      const f32x4_t as4 = a0 + a1;
+      f32x4_t as4 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (!markov) {
+        const f32x4_t a0 = *reinterpret_cast<const LDS f32x4_t*>(s.AS + p * ASTR + j0);
+        const f32x4_t a1 = *reinterpret_cast<const LDS f32x4_t*>(s.AS + (16 + p) * ASTR + j0);
+        as4 = a0 + a1;
+      }
       const u32x2_t e2 = *reinterpret_cast<const LDS u32x2_t*>(s.EC + (size_t)k * RT + j0);
       const f32x4_t h4 = *reinterpret_cast<const LDS f32x4_t*>(s.hb + j0);
       const float ev[4] = {bf16_to_f32(e2.x & 0xFFFFu), bf16_to_f32(e2.x >> 16), bf16_to_f32(e2.y & 0xFFFFu),
@@ -742,9 +757,9 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
     }
   }
   lds_sync();
-  // a node is selected when its rank is below B (empty slots: key 0, never)
+  // a node is selected when its rank is below B_q (empty slots: key 0, never)
   for (int i = tid; i < N; i += kT)
-    if (s.nkey[i] != 0ull && s.eix[i] < B) lds_or(&s.nd[i / W], 1 << s.lv_lex[i]);
+    if (s.nkey[i] != 0ull && s.eix[i] < Bq) lds_or(&s.nd[i / W], 1 << s.lv_lex[i]);
   lds_sync();
   // Emitted index: selected nodes of earlier levels, then selected nodes of
   // the level with a smaller path rank (breadth-first order = path order).
@@ -865,16 +880,24 @@ TreePlan tree_fast_plan(const TreeArgs& a) {
 hipError_t launch_tree_fast(const TreePlan& p, const TreeArgs& a, hipStream_t s) {
   dim3 grid(a.n_req), block(kT);
   hipError_t e = hipSuccess;
-#define DT_FAST(KCV)                                                                                         \
-  do {                                                                                                       \
-    e = hipFuncSetAttribute((const void*)tree_fast_kernel<KCV>, hipFuncAttributeMaxDynamicSharedMemorySize, \
-                            (int)p.smem);                                                                    \
-    if (e != hipSuccess) return e;                                                                           \
-    hipLaunchKernelGGL((tree_fast_kernel<KCV>), grid, block, p.smem, s, a);                                 \
+#define DT_FAST(KCV, MK)                                                                                      \
+  do {                                                                                                        \
+    e = hipFuncSetAttribute((const void*)tree_fast_kernel<KCV, MK>, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                            (int)p.smem);                                                                     \
+    if (e != hipSuccess) return e;                                                                            \
+    hipLaunchKernelGGL((tree_fast_kernel<KCV, MK>), grid, block, p.smem, s, a);                              \
   } while (0)
-  if (a.K == 16) DT_FAST(16);
-  else if (a.K == 32) DT_FAST(32);
-  else DT_FAST(64);
+  const bool mk = a.A == nullptr;   // the Markov head
+  if (a.K == 16) {
+    if (mk) DT_FAST(16, true);
+    else DT_FAST(16, false);
+  } else if (a.K == 32) {
+    if (mk) DT_FAST(32, true);
+    else DT_FAST(32, false);
+  } else {
+    if (mk) DT_FAST(64, true);
+    else DT_FAST(64, false);
+  }
 #undef DT_FAST
   return hipGetLastError();
 }

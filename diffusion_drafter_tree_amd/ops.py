@@ -56,13 +56,15 @@ def to_device(arr: Optional[np.ndarray], device="cuda") -> Optional[torch.Tensor
 class DeviceHead:
     """Head weights resident on the GPU."""
 
-    def __init__(self, head: I.Head, device="cuda"):
-        self.A = to_device(head.A, device)
+    def __init__(self, head: I.Head, device="cuda", markov: bool = False):
+        """``markov``: pass no A (the Markov-head variant, A = 0); the kernels
+        then skip the A s_parent contraction."""
+        self.A = None if markov else to_device(head.A, device)
         self.E = to_device(head.E, device)
         self.U = to_device(head.U, device)
         self.Pt = to_device(head.Pt, device)
-        self.c = C.Head(A=self.A.data_ptr(), E=self.E.data_ptr(), U=self.U.data_ptr(),
-                        Pt=self.Pt.data_ptr() if self.Pt is not None else None)
+        self.c = C.Head(A=self.A.data_ptr() if self.A is not None else None, E=self.E.data_ptr(),
+                        U=self.U.data_ptr(), Pt=self.Pt.data_ptr() if self.Pt is not None else None)
 
 
 def workspace_size(dims: C.Dims) -> int:
@@ -110,6 +112,21 @@ class RoundBuffers:
                               cum=self.st_cum.data_ptr(), sbeta=self.st_sbeta.data_ptr(),
                               count=self.st_count.data_ptr(), state=self.st_state.data_ptr(), next_depth=1)
         workspace_init(self.dims, self.ws)
+        self.width: Optional[torch.Tensor] = None
+        self.budget: Optional[torch.Tensor] = None
+
+    def set_request_sizes(self, width: Optional[torch.Tensor] = None, budget: Optional[torch.Tensor] = None):
+        """Per-request width W_q and node budget B_q (device int32 [n_req], or
+        None for the config's W and B); the library clamps them to [1, W] and
+        [1, B]. The tensors are kept here so they outlive the calls that read
+        them."""
+        n = self.cfg.n_req
+        for name, t in (("width", width), ("budget", budget)):
+            if t is not None and (t.dtype != torch.int32 or t.numel() != n or not t.is_cuda or not t.is_contiguous()):
+                raise ValueError(f"{name}: a contiguous device int32 tensor of {n} entries is required")
+        self.width, self.budget = width, budget
+        self.st.width = _p(width)
+        self.st.budget = _p(budget)
 
     def numpy(self) -> Dict[str, np.ndarray]:
         """Host copies laid out as the parity checker expects."""

@@ -85,7 +85,13 @@ typedef struct {
  *   U  [V][r]  output rows: corrected logit z_c = Lbase[c] + <s_parent, U[c]>
  *   Pt [r][D]  input projection stored output-major, Pt[j][i] = P[i][j]
  *              (may be NULL when D == 0)
- * Child state: s = tanh(A s_parent + E[u] + h_d); the root state is h_0. */
+ * Child state: s = tanh(A s_parent + E[u] + h_d); the root state is h_0.
+ * A may be NULL: the Markov-head variant (marsggbo blog section 4.3, Table 3:
+ * DSpark's Markov head put in place of the correction head; the distribution
+ * over a node's children is conditioned on that node's token alone). It is the head with A = 0, so a
+ * state is tanh(E[u] + h_d), a function of the node's token and depth; the
+ * kernels then skip the A s_parent contraction and the scan launch stages no
+ * A fragments (dartree_round_plan counts those 16 workgroups regardless). */
 typedef struct {
   const void* A;
   const void* E;
@@ -102,7 +108,21 @@ typedef struct {
  *   state       [n][W][r] float  head states of the deepest expanded level,
  *                                read back by the next dartree_expand_depth
  *   next_depth  HOST field: the next depth dartree_expand_depth expects; set
- *               it to 1 before a round; each successful call advances it. */
+ *               it to 1 before a round; each successful call advances it.
+ *   width       [n] int32 or NULL: per-request width W_q of every depth (the
+ *               serving knob of the blog's section 3.1, "fixed width per
+ *               depth", chosen per request inside one batch); NULL means
+ *               dims->W for every request. Read on the device by
+ *               dartree_expand_depth and dartree_build_round; values are
+ *               clamped to [1, dims->W]. Slots >= W_q are padding.
+ *   budget      [n] int32 or NULL: per-request node budget B_q of the
+ *               deferred top-B (the verification-tree size); NULL means
+ *               dims->B. Read on the device by dartree_select_topB and
+ *               dartree_build_round; values are clamped to [1, dims->B].
+ *               Outputs keep their [n][B] stride; entries >= n_sel are
+ *               padding as usual.
+ * Memory for a per-request width or budget is the caller's and must hold its
+ * values until the stream has run the call. */
 typedef struct {
   int32_t* tok;
   int32_t* parent_slot;
@@ -111,6 +131,8 @@ typedef struct {
   int32_t* count;
   float* state;
   int32_t next_depth;
+  const int32_t* width;
+  const int32_t* budget;
 } dartree_supertree;
 
 /* Human-readable status name; never NULL. */

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dartree_version() == 1
+    assert lib.dartree_version() == 2
     assert C.status_string(0) == "DARTREE_OK"
     assert C.status_string(3) == "DARTREE_ERR_WORKSPACE_TOO_SMALL"
     assert C.status_string(99) == "DARTREE_UNKNOWN_STATUS"

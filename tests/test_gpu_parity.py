@@ -133,6 +133,115 @@ def test_repeat_runs_are_bit_identical():
             assert np.array_equal(o[k], outs[0][k]), k
 
 
+def _request_sizes(cfg):
+    """Per-request widths and budgets covering the full size, the minimum, a
+    middle value and out-of-range values (clamped by the library)."""
+    n = cfg.n_req
+    w_raw = [cfg.W, 1, max(1, cfg.W // 2), cfg.W + 5, 0, -3][:n]
+    b_raw = [cfg.B, 1, max(1, cfg.B // 3), cfg.B + 7, 0, 2][:n]
+    w_eff = [min(max(x, 1), cfg.W) for x in w_raw]
+    b_eff = [min(max(x, 1), cfg.B) for x in b_raw]
+    return w_raw, b_raw, w_eff, b_eff
+
+
+@pytest.mark.parametrize("name,mode", [("fast_K64_W12_L6", "build"), ("fast_K64_W12_L6", "steps"),
+                                       ("bf16_multichunk", "build"), ("wide_W32_K256", "steps"),
+                                       ("tiny_f32", "build"), ("qwen3_4b_x4", "build")])
+def test_per_request_width_and_budget(name, mode):
+    """Per-request W_q and B_q inside one batch against the oracle run with
+    each request's own sizes; supertree slots past W_q and outputs past n_sel
+    are padding."""
+    if name == "qwen3_4b_x4":
+        cfg = I.CONFIGS["qwen3_4b"].with_(n_req=4, name=name)
+    else:
+        cfg = SMALL[name].with_(name=name, n_req=4)
+    w_raw, b_raw, w_eff, b_eff = _request_sizes(cfg)
+    hd, dhd = device_head(cfg)
+    rnd = I.make_round(cfg, 0, 3)
+    say(f"case per-request sizes {name} mode={mode} widths={w_raw} budgets={b_raw}")
+    rb = ops.RoundBuffers(cfg)
+    rb.set_request_sizes(torch.tensor(w_raw, dtype=torch.int32, device="cuda"),
+                         torch.tensor(b_raw, dtype=torch.int32, device="cuda"))
+    logits = ops.to_device(rnd.logits)
+    hin = ops.to_device(rnd.H if cfg.D > 0 else rnd.h)
+    if mode == "build":
+        ops.build_round(rb.dims, dhd, logits, hin, rb)
+    else:
+        ops.run_steps(rb.dims, dhd, logits, hin, rb, depth_chunks=[(1, 2), (3, cfg.L)])
+    torch.cuda.synchronize()
+    out = rb.numpy()
+    rep = CK.check_round(cfg, hd, rnd, out, tol=TOL, widths=w_eff, budgets=b_eff)
+    for q in range(cfg.n_req):
+        cnt = out["st_count"][q]
+        assert cnt[0] == min(w_eff[q], cfg.K), q
+        for d in range(1, cfg.L):
+            assert cnt[d] == min(w_eff[q], int(cnt[d - 1]) * cfg.K), (q, d)
+        for d in range(cfg.L):
+            assert np.all(out["st_tok"][q, d, cnt[d]:] == -1), (q, d)
+            assert np.all(np.isneginf(out["st_sbeta"][q, d, cnt[d]:])), (q, d)
+        assert out["n_sel"][q] == min(b_eff[q], int(cnt.sum())), q
+    say(f"  ok: nodes={rep.nodes_checked} ties(level/topB)={rep.tie_events_level}/{rep.tie_events_topB}")
+    # the request with the full sizes equals its result in a uniform batch
+    ref = run_gpu(cfg, hd, dhd, rnd)
+    for k in ("st_tok", "st_parent", "st_count", "n_sel", "tok", "depth", "parent", "slot", "mask"):
+        assert np.array_equal(out[k][0], ref[k][0]), k
+
+
+@pytest.mark.parametrize("name", ["fast_K64_W12_L6", "bf16_multichunk", "tiny_f32", "qwen3_4b"])
+def test_markov_head_variant(name):
+    """The Markov-head variant (the child distribution conditioned on the
+    parent's token only) is the head with A = 0: a node's state is
+    tanh(E[u] + h_d), a function of its own token and depth. Parity with the
+    oracle at A = 0, and on the HIP path's own supertree: two kept nodes of
+    one depth with the same token give their children the same log q."""
+    import dataclasses
+    cfg = I.CONFIGS[name] if name in I.CONFIGS else SMALL[name].with_(name=name)
+    hd0 = I.make_head(cfg, 0)
+    hd = dataclasses.replace(hd0, A=np.zeros_like(hd0.A))
+    dhd = ops.DeviceHead(hd)
+    rnd = I.make_round(cfg, 0, 1)
+    say(f"case markov head (A = 0) {name}")
+    out = run_gpu(cfg, hd, dhd, rnd)
+    rep = CK.check_round(cfg, hd, rnd, out, tol=TOL)
+    pairs = 0
+    for q in range(cfg.n_req):
+        tok, par, cum, cnt = out["st_tok"][q], out["st_parent"][q], out["st_cum"][q], out["st_count"][q]
+        for d in range(1, cfg.L):
+            logq = {}
+            for sl in range(cnt[d]):
+                pt = int(tok[d - 1][par[d][sl]])
+                lq = float(cum[d][sl]) - float(cum[d - 1][par[d][sl]])
+                key = (pt, int(tok[d][sl]))
+                if key in logq and logq[key][0] != par[d][sl]:
+                    assert abs(logq[key][1] - lq) <= TOL, (q, d, key)
+                    pairs += 1
+                logq.setdefault(key, (par[d][sl], lq))
+    say(f"  ok: nodes={rep.nodes_checked} same-token parent pairs compared={pairs}")
+    # the boundary's Markov head (no A): the kernels skip the A*S contraction;
+    # the result equals the A = 0 run bit for bit, fused and step by step
+    dhm = ops.DeviceHead(hd0, markov=True)
+    outm = run_gpu(cfg, hd, dhm, rnd)
+    outs = run_gpu(cfg, hd, dhm, rnd, mode="steps", chunks=[(1, 1), (2, cfg.L)])
+    for k in out:
+        assert np.array_equal(outm[k], out[k]), k
+        assert np.array_equal(outs[k], out[k]), k
+    if cfg.B <= 511:
+        so0, som = _serial_gpu_head(cfg, dhd, rnd), _serial_gpu_head(cfg, dhm, rnd)
+        for k in so0:
+            assert np.array_equal(so0[k], som[k]), k
+
+
+def _serial_gpu_head(cfg, dhd, rnd):
+    rb = ops.RoundBuffers(cfg)
+    logits = ops.to_device(rnd.logits)
+    hin = ops.to_device(rnd.H if cfg.D > 0 else rnd.h)
+    ops.build_round(rb.dims, dhd, logits, hin, rb)
+    so = ops.SerialOutputs(cfg)
+    ops.build_serial(rb.dims, dhd, rb.cand_ids, rb.cand_logit, rb.h if cfg.D > 0 else hin, so)
+    torch.cuda.synchronize()
+    return so.numpy()
+
+
 def _topk_rows(logits_bits, K, dtype="bf16"):
     """Run only the candidate step over [rows][V] logits."""
     rows, V = logits_bits.shape
