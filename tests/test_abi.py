@@ -243,3 +243,31 @@ def test_verify_tree_validates_on_host(lib):
     assert call(128, mask=ctypes.c_void_p(0x10004)) == C.ERR_INVALID_ARGUMENT
     assert "aligned" in C.last_error()
 
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """Every struct of the header has, compiled by the host C compiler, the
+    size and field offsets of its ctypes mirror in the binding."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    structs = {"dartree_dims": C.Dims, "dartree_head": C.Head, "dartree_supertree": C.Supertree,
+               "dartree_round_info": C.RoundInfo}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "dartree.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
