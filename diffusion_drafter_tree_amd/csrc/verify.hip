@@ -16,7 +16,10 @@
 // One 1024-thread workgroup per request: a thread per node walks its root path
 // for the acceptance; a wave per query row iterates over the set bits of its
 // mask row with a running (online) softmax, its lanes over the head
-// dimension, each dot product added across the wave in a fixed order.
+// dimension, each dot product added across the wave in a fixed order. The
+// request's token, depth and parent arrays and its target are read into LDS
+// once (the walks are chains of dependent reads), and so are its K and V rows
+// when they fit (kVerifyKVBytes), so that a query's ancestors are LDS reads.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,16 +29,34 @@ namespace {
 
 constexpr int kVT = 1024;
 constexpr int kMaxDh = 256;
+constexpr int kMaxTreeB = 1024;                  // the library's largest B
+constexpr size_t kVerifyKVBytes = 96 * 1024;     // K and V rows staged up to this size
 
-__global__ __launch_bounds__(kVT) void verify_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kVT) void verify_kernel(VerifyArgs a, int kv_staged) {
   __shared__ int s_best;
+  __shared__ int s_tok[kMaxTreeB], s_dep[kMaxTreeB], s_par[kMaxTreeB], s_tgt[32];
+  extern __shared__ float s_kv[];   // [2][B][dh] when kv_staged
   const int q = blockIdx.x, tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int L = a.L, B = a.B, dh = a.dh;
   const int n = min(max(a.n_sel[q], 0), B);
-  const int32_t* tok = a.tok + (size_t)q * B;
-  const int32_t* dep = a.depth + (size_t)q * B;
-  const int32_t* par = a.parent + (size_t)q * B;
-  const int32_t* tgt = a.target + (size_t)q * L;
+  for (int i = tid; i < B; i += kVT) {
+    s_tok[i] = a.tok[(size_t)q * B + i];
+    s_dep[i] = a.depth[(size_t)q * B + i];
+    s_par[i] = a.parent[(size_t)q * B + i];
+  }
+  if (tid < L) s_tgt[tid] = a.target[(size_t)q * L + tid];
+  if (kv_staged) {
+    const float* kg = a.K + (size_t)q * B * dh;
+    const float* vg = a.V + (size_t)q * B * dh;
+    for (int i = tid; i < B * dh; i += kVT) {
+      s_kv[i] = kg[i];
+      s_kv[(size_t)B * dh + i] = vg[i];
+    }
+  }
+  const int32_t* tok = s_tok;
+  const int32_t* dep = s_dep;
+  const int32_t* par = s_par;
+  const int32_t* tgt = s_tgt;
   if (tid == 0) s_best = -1;
   __syncthreads();
   // ---- acceptance: deepest node whose whole root path matches the target
@@ -92,8 +113,8 @@ __global__ __launch_bounds__(kVT) void verify_kernel(VerifyArgs a) {
         const int j = wi * 64 + __builtin_ctzll(bits);
         bits &= bits - 1;
         if (j >= B) break;
-        const float* krow = a.K + ((size_t)q * B + j) * dh;
-        const float* vrow = a.V + ((size_t)q * B + j) * dh;
+        const float* krow = kv_staged ? s_kv + (size_t)j * dh : a.K + ((size_t)q * B + j) * dh;
+        const float* vrow = kv_staged ? s_kv + ((size_t)B + j) * dh : a.V + ((size_t)q * B + j) * dh;
         float part = 0.f, vv[PL];
 #pragma unroll
         for (int t = 0; t < PL; ++t) {
@@ -122,7 +143,15 @@ __global__ __launch_bounds__(kVT) void verify_kernel(VerifyArgs a) {
 }  // namespace
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(verify_kernel, dim3(a.n_req), dim3(kVT), 0, s, a);
+  const size_t kv = 2ull * a.B * a.dh * sizeof(float);
+  const int staged = kv <= kVerifyKVBytes ? 1 : 0;
+  const size_t smem = staged ? kv : 0;
+  if (smem > 0) {
+    const hipError_t e = hipFuncSetAttribute((const void*)verify_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)smem);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(verify_kernel, dim3(a.n_req), dim3(kVT), smem, s, a, staged);
   return hipGetLastError();
 }
 
