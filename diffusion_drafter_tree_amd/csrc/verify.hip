@@ -20,6 +20,8 @@
 // request's token, depth and parent arrays and its target are read into LDS
 // once (the walks are chains of dependent reads), and so are its K and V rows
 // when they fit (kVerifyKVBytes), so that a query's ancestors are LDS reads.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -36,7 +38,9 @@ __global__ __launch_bounds__(kVT) void verify_kernel(VerifyArgs a, int kv_staged
   __shared__ int s_best;
   __shared__ int s_tok[kMaxTreeB], s_dep[kMaxTreeB], s_par[kMaxTreeB], s_tgt[32];
   extern __shared__ float s_kv[];   // [2][B][dh] when kv_staged
-  const int q = blockIdx.x, tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  // blockIdx.y = g of G workgroups a request: workgroup 0 also does the
+  // acceptance; the query rows go round-robin over the G * 16 waves
+  const int q = blockIdx.x, g = blockIdx.y, G = gridDim.y, tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int L = a.L, B = a.B, dh = a.dh;
   const int n = min(max(a.n_sel[q], 0), B);
   for (int i = tid; i < B; i += kVT) {
@@ -60,7 +64,7 @@ __global__ __launch_bounds__(kVT) void verify_kernel(VerifyArgs a, int kv_staged
   if (tid == 0) s_best = -1;
   __syncthreads();
   // ---- acceptance: deepest node whose whole root path matches the target
-  for (int i = tid; i < n; i += kVT) {
+  for (int i = tid; i < (g == 0 ? n : 0); i += kVT) {
     const int d = dep[i];
     bool ok = d >= 1 && d <= L;
     int v = i, steps = 0;
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(kVT) void verify_kernel(VerifyArgs a, int kv_staged
     if (ok) atomicMax(&s_best, (d << 16) | i);
   }
   __syncthreads();
-  if (tid == 0) {
+  if (g == 0 && tid == 0) {
     const int b = s_best;
     const int dbest = b < 0 ? 0 : b >> 16;
     a.acc_len[q] = 1 + dbest;
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(kVT) void verify_kernel(VerifyArgs a, int kv_staged
   const int words = (B + 63) / 64;
   const float scale = 1.0f / sqrtf((float)dh);
   constexpr int PL = kMaxDh / kWave;   // head-dimension elements per lane
-  for (int i = w; i < B; i += kVT / kWave) {
+  for (int i = g * (kVT / kWave) + w; i < B; i += G * (kVT / kWave)) {
     float* orow = a.out + ((size_t)q * B + i) * dh;
     if (i >= n) {
       for (int e = lane; e < dh; e += kWave) orow[e] = 0.f;
@@ -151,7 +155,9 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t s) {
                                              (int)smem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(verify_kernel, dim3(a.n_req), dim3(kVT), smem, s, a, staged);
+  // up to four workgroups a request, each with at least one query row a wave
+  const int G = std::max(1, std::min(4, (a.B + kVT / kWave - 1) / (kVT / kWave)));
+  hipLaunchKernelGGL(verify_kernel, dim3(a.n_req, G), dim3(kVT), smem, s, a, staged);
   return hipGetLastError();
 }
 
