@@ -13,8 +13,9 @@
 //   attention   out[i] = sum_j softmax_j(<Q[i], K[j]> / sqrt(dh)) V[j] over
 //               the nodes j whose bit is set in mask row i (the node and its
 //               ancestors); rows past n_sel are zero.
-// One 1024-thread workgroup per request: a thread per node walks its root path
-// for the acceptance; a wave per query row iterates over the set bits of its
+// Up to four 1024-thread workgroups per request. In workgroup 0 a thread per
+// node walks its root path for the acceptance. A wave per query row (rows
+// round-robin over all the request's waves) iterates over the set bits of its
 // mask row with a running (online) softmax, its lanes over the head
 // dimension, each dot product added across the wave in a fixed order. The
 // request's token, depth and parent arrays and its target are read into LDS
