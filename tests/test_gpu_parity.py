@@ -14,6 +14,7 @@ from diffusion_drafter_tree_amd import inputs as I
 from diffusion_drafter_tree_amd import ops
 from oracle import check as CK
 from oracle import dartree_oracle as O
+from tests import _parity_pool as PP
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
@@ -56,7 +57,32 @@ def check(cfg, seed=0, t=0, mode="build", chunks=None, requests=None):
     rep = CK.check_round(cfg, hd, rnd, out, tol=TOL, requests=requests)
     say(f"  ok: nodes={rep.nodes_checked} ties(level/topB)={rep.tie_events_level}/{rep.tie_events_topB} "
         f"max|dscore|={rep.max_score_err:.2e} max|dh|={rep.max_h_err:.2e}")
+    PP.log_case(f"{cfg.name} seed={seed} t={t} mode={mode}", rep)
     return out, rep
+
+
+def check_many_rounds(cfg, ts, seed=0, label=None):
+    """Full-round parity on many seeded rounds: the rounds are drawn and
+    checked against the oracle in spawned worker processes while this process
+    runs them on the GPU, one round at a time."""
+    hd, dhd = device_head(cfg, seed)
+    rep, ties, n = CK.Report(), 0, 0
+    label = label or f"{cfg.name} rounds {ts[0]}..{ts[-1]}"
+    with PP.pool() as ex:
+        futs = []
+        for t, rnd in zip(ts, ex.map(PP.gen_round, [cfg] * len(ts), [seed] * len(ts), ts)):
+            out = run_gpu(cfg, hd, dhd, rnd)
+            futs.append(ex.submit(PP.check_job, cfg, seed, t, out, None, TOL))
+        for f in futs:
+            r, tb = f.result()
+            rep.merge(r)
+            ties += tb
+            n += 1
+            if n % 100 == 0:
+                PP.log_case(f"{label} progress", rounds=n)
+    PP.log_case(label, rep, rounds=n, rows=n * cfg.n_req * cfg.L, rows_tied_at_K=ties,
+                tie_events_per_1000_rounds=1000.0 * (rep.tie_events_level + rep.tie_events_topB) / max(n, 1))
+    return rep
 
 
 SMALL = {
@@ -105,9 +131,26 @@ def test_step_entry_points_match_fused_round(name):
         assert np.array_equal(a[k], c[k]), k
 
 
-def test_metric_config_qwen3_4b():
-    for t in range(2):
-        check(I.CONFIGS["qwen3_4b"], t=t)
+@pytest.mark.parametrize("chunk", range(4))
+def test_metric_config_qwen3_4b_1000_rounds(chunk):
+    """All 1000 seeded rounds of the metric config, 250 per case: the whole
+    round (16,000 candidate rows bit-exact, every level replayed, top-B,
+    emission and mask) against the oracle."""
+    ts = list(range(chunk * 250, (chunk + 1) * 250))
+    check_many_rounds(I.CONFIGS["qwen3_4b"], ts)
+
+
+def test_tiny_config_500_seeds():
+    """The tiny fp32 config on 500 head-and-round seeds."""
+    cfg = I.CONFIGS["tiny"]
+    rep = CK.Report()
+    for seed in range(500):
+        hd = I.make_head(cfg, seed)
+        dhd = ops.DeviceHead(hd)
+        rnd = I.make_round(cfg, seed, 0)
+        out = run_gpu(cfg, hd, dhd, rnd)
+        rep.merge(CK.check_round(cfg, hd, rnd, out, tol=TOL))
+    PP.log_case("tiny 500 seeds", rep, rounds=500)
 
 
 def test_fixed_width_qwen3_8b():
@@ -118,19 +161,119 @@ def test_concurrent_c4():
     check(I.CONFIGS["concurrent_c4"])
 
 
-def test_stress_64req_sampled():
-    check(I.CONFIGS["stress_64req"], requests=[0, 31, 63])
+@pytest.mark.parametrize("t", [0, 1])
+def test_stress_64req_all_requests(t):
+    """Every one of the 64 requests of a stress round (K = 512, r = 512, the
+    general tree kernel), checked in eight-request slices by worker
+    processes."""
+    cfg = I.CONFIGS["stress_64req"]
+    hd, dhd = device_head(cfg)
+    say(f"case stress_64req all requests t={t}")
+    rnd = I.make_round(cfg, 0, t)
+    out = run_gpu(cfg, hd, dhd, rnd)
+    del rnd
+    rep, ties = CK.Report(), 0
+    with PP.pool() as ex:
+        futs = [ex.submit(PP.check_job, cfg, 0, t, out, list(range(q0, q0 + 8)), TOL) for q0 in range(0, 64, 8)]
+        for f in futs:
+            r, tb = f.result()
+            rep.merge(r)
+            ties += tb
+    assert rep.nodes_checked == cfg.n_req * cfg.L * cfg.W
+    PP.log_case(f"stress_64req t={t} all 64 requests", rep, rows_tied_at_K=ties)
 
 
 def test_repeat_runs_are_bit_identical():
+    """100 runs of one round: every output bit-identical (a race in any
+    kernel would show as a difference between runs)."""
     cfg = I.CONFIGS["qwen3_4b"]
     hd, dhd = device_head(cfg)
     rnd = I.make_round(cfg, 0, 5)
-    say("case repeat-determinism qwen3_4b x4")
-    outs = [run_gpu(cfg, hd, dhd, rnd) for _ in range(4)]
-    for o in outs[1:]:
+    say("case repeat-determinism qwen3_4b x100")
+    rb = ops.RoundBuffers(cfg)
+    logits, hin = ops.to_device(rnd.logits), ops.to_device(rnd.H)
+    ref = None
+    for i in range(100):
+        ops.build_round(rb.dims, dhd, logits, hin, rb)
+        torch.cuda.synchronize()
+        o = rb.numpy()
+        if ref is None:
+            ref = o
+            continue
         for k in o:
-            assert np.array_equal(o[k], outs[0][k]), k
+            assert np.array_equal(o[k], ref[k]), (i, k)
+    PP.log_case("repeat-determinism qwen3_4b", runs=100)
+
+
+def _tie_head_round(cfg, seed, huge_gap):
+    """U = 0 (the corrected distribution is the base one, so children of one
+    parent with equal base logits tie exactly in fp32 and fp64 alike) and
+    base logits on a grid of 0.5 (many exact ties among the candidates). With
+    ``huge_gap``, the first candidate of each position sits 240 above the
+    rest: its log q is exactly 0 in both precisions, so with beta = 0 a chain
+    of nodes ties its parent across depths."""
+    import dataclasses
+    hd = I.make_head(cfg, seed)
+    hd = dataclasses.replace(hd, U=np.zeros_like(hd.U))
+    rnd = I.make_round(cfg, seed, 0)
+    x = np.round(I.as_f64(rnd.logits, cfg.logits_dtype) * 2) / 2
+    if huge_gap:
+        for q in range(cfg.n_req):
+            for i in range(cfg.L):
+                x[q, i, int(np.argmax(x[q, i]))] = 240.0
+    else:
+        # force exact ties at both cuts of the first position: the W-th and
+        # (W+1)-th best base logits, and the B-th and (B+1)-th, made equal
+        # (the higher token id takes the lower one's value)
+        for q in range(cfg.n_req):
+            order = np.lexsort((np.arange(cfg.V), -x[q, 0]))
+            for cut in (cfg.W, cfg.B):
+                a, b = order[cut - 1], order[cut]
+                x[q, 0, max(a, b)] = x[q, 0, min(a, b)]
+                order = np.lexsort((np.arange(cfg.V), -x[q, 0]))
+    rnd.logits = I.f32_to_bf16_bits(x.astype(np.float32)) if cfg.logits_dtype == "bf16" else x.astype(np.float32)
+    return hd, rnd
+
+
+@pytest.mark.parametrize("name,huge_gap", [("fast_ties", False), ("fast_ties_depth", True),
+                                           ("general_ties", False), ("general_ties_depth", True)])
+def test_exact_ties_at_the_cut_follow_the_comparator(name, huge_gap):
+    """Exact ties (equal in fp32 and in fp64) at the top-W and top-B cuts
+    must be settled by the comparator -- token ascending among children of
+    one parent, depth ascending across depths -- so the kept sets equal the
+    oracle's with no tie event at all."""
+    # one depth without the gap: every child has the root as its parent, so
+    # equal base logits give bit-equal scores at the W and B cuts. With the
+    # gap, each level's survivors are the chain node and its best children
+    # (other parents' children sit ~240 lower), so exact ties again fall
+    # between children of one parent, and across depths on the chain.
+    base = dict(n_req=2, V=6000, L=8 if huge_gap else 1, K=64, W=6, B=5 if huge_gap else 4, D=64,
+                beta=0.0 if huge_gap else -0.1)
+    if name.startswith("fast"):
+        cfg = I.small_variant("qwen3_4b", name=name, r=256, **base)
+    else:
+        cfg = I.small_variant("qwen3_4b", name=name, r=64, **base)
+    hd, rnd = _tie_head_round(cfg, 11, huge_gap)
+    dhd = ops.DeviceHead(hd)
+    say(f"case exact ties {name}")
+    out = run_gpu(cfg, hd, dhd, rnd)
+    rep = CK.check_round(cfg, hd, rnd, out, tol=TOL)
+    ties = PP.boundary_ties(rnd.logits, cfg.logits_dtype, cfg.K)
+    PP.log_case(f"exact ties {name}", rep, rows_tied_at_K=ties)
+    assert ties > 0
+    if not huge_gap:
+        # the oracle itself sees exact ties at both cuts
+        for r in O.round_all(cfg, hd, rnd):
+            sb = sorted((nd.sbeta for nd in r.levels[1]), reverse=True)
+            allc = sorted(O.corrected_logprobs(r.cand_vals[0], np.zeros((cfg.K, cfg.r)), r.h[0]), reverse=True)
+            assert allc[cfg.W - 1] == allc[cfg.W] and sb[cfg.B - 1] == sb[cfg.B]
+    assert rep.tie_events_level == 0 and rep.tie_events_topB == 0, rep.tie_log
+    if huge_gap:
+        # the chain of first candidates scores exactly 0 at every depth, and
+        # the selection takes it depth by depth
+        for q in range(cfg.n_req):
+            zero = [i for i in range(int(out["n_sel"][q])) if out["score"][q, i] == 0.0]
+            assert [int(out["depth"][q, i]) for i in zero] == list(range(1, cfg.B + 1)), (q, zero)
 
 
 def _request_sizes(cfg):

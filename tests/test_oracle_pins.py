@@ -559,3 +559,53 @@ def test_tree_attention_scale_is_one_over_sqrt_dh():
     wide = O.tree_attention(np.hstack([Q, Q]), np.hstack([K, K]), np.hstack([V, V]), mask, n)[:, :dh]
     scaled = O.tree_attention(Q * 2 ** 0.25, K * 2 ** 0.25, V, mask, n)
     assert np.allclose(wide, scaled, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# the oracle's exact widening of bf16 bit patterns, pinned to the bfloat16
+# definition (1 sign bit, 8 exponent bits with bias 127, 7 fraction bits; the
+# value is (-1)^s * 2^(e-127) * (1 + f/128) for 0 < e < 255 and
+# (-1)^s * 2^-126 * (f/128) for e = 0), not to the float32 bit view the
+# oracle uses
+# ----------------------------------------------------------------------------
+def _bf16_value_by_definition(bits: int) -> float:
+    s, e, f = bits >> 15, (bits >> 7) & 0xFF, bits & 0x7F
+    assert e != 0xFF
+    mag = math.ldexp(1.0 + f / 128.0, e - 127) if e else math.ldexp(f / 128.0, -126)
+    return -mag if s else mag
+
+
+@pytest.mark.parametrize("bits,value", [
+    (0x3F80, 1.0), (0xC020, -2.5), (0x4049, 3.140625), (0x3F81, 1.0078125), (0x0000, 0.0),
+    (0x7F7F, 3.3895313892515355e38),     # largest finite bf16, (2 - 2^-7) * 2^127
+    (0x0001, 2.0 ** -133),               # smallest subnormal
+    (0x0080, 2.0 ** -126),               # smallest normal
+    (0xFF7F, -3.3895313892515355e38),
+    (0x4780, 65536.0),                   # beyond the fp16 range
+])
+def test_widen_bf16_hand_patterns(bits, value):
+    got = O.widen(np.array([bits], np.uint16), "bf16")
+    assert got.dtype == np.float64 and got[0] == value
+    assert _bf16_value_by_definition(bits) == value
+
+
+def test_widen_bf16_negative_zero_keeps_its_sign():
+    got = O.widen(np.array([0x8000], np.uint16), "bf16")[0]
+    assert got == 0.0 and math.copysign(1.0, got) == -1.0
+
+
+def test_widen_bf16_every_finite_pattern_matches_the_definition():
+    bits = np.array([b for b in range(1 << 16) if ((b >> 7) & 0xFF) != 0xFF], np.uint16)
+    got = O.widen(bits, "bf16")
+    ref = np.array([_bf16_value_by_definition(int(b)) for b in bits], np.float64)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), (bits >> 15).astype(bool))
+    # a 2-D array keeps its shape
+    assert O.widen(bits[:12].reshape(3, 4), "bf16").shape == (3, 4)
+
+
+def test_widen_f32_is_exact():
+    x = np.array([1.0, -0.1, 3.4028234663852886e38, 1.401298464324817e-45], np.float32)
+    got = O.widen(x, "f32")
+    assert got.dtype == np.float64
+    assert [float(v) for v in got] == [1.0, float(np.float32(-0.1)), 3.4028234663852886e38, 2.0 ** -149]
