@@ -21,6 +21,8 @@ ERR_HIP = 4
 F32 = 0
 BF16 = 1
 
+NOALLOC_SCRATCH_BYTES = 32 << 20   # DARTREE_NOALLOC_SCRATCH_BYTES
+
 
 class Dims(ctypes.Structure):
     _fields_ = [("n_req", c_int32), ("L", c_int32), ("V", c_int32), ("K", c_int32), ("W", c_int32),
@@ -64,6 +66,9 @@ SIGNATURES = {
     "dartree_build_round": (c_int32, [PD, PH, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, PS,
                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_size_t, c_void_p]),
+    "dartree_build_round_noalloc": (c_int32, [PD, PH, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, PS,
+                                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, c_void_p]),
     "dartree_set_stage_events": (c_int32, [POINTER(c_void_p), c_int32]),
     "dartree_serial_workspace_size": (c_int32, [PD, POINTER(c_size_t)]),
     "dartree_verify_tree": (c_int32, [PD, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

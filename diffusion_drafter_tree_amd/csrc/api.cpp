@@ -9,6 +9,7 @@
 
 #include "../../include/dartree.h"
 #include "kernels.h"
+#include "api_internal.h"
 
 namespace {
 
@@ -391,6 +392,29 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
                                    int32_t* parent, float* score, int32_t* slot, uint64_t* mask, void* ws,
                                    size_t ws_bytes, void* stream) {
   g_err[0] = 0;
+  return dartree::build_round_impl(dims, head, logits, H_or_h, cand_ids, cand_logit, h, st, n_sel, tok, depth,
+                                   parent, score, slot, mask, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace dartree {
+
+dartree_status set_error(dartree_status s, const char* msg) { return fail(s, "%s", msg); }
+
+size_t round_workspace_bytes(const dartree_dims* dims) { return ws_layout(dims).total; }
+
+dartree_status check_round_dims(const dartree_dims* dims) {
+  TRY(check_dims(dims));
+  if (!ws_layout(dims).plan.ok) return fail(DARTREE_ERR_UNSUPPORTED, "no top-K plan for V=%d K=%d", dims->V, dims->K);
+  return DARTREE_OK;
+}
+
+dartree_status build_round_impl(const dartree_dims* dims, const dartree_head* head, const void* logits,
+                                const void* H_or_h, int32_t* cand_ids, float* cand_logit, float* h,
+                                dartree_supertree* st, int32_t* n_sel, int32_t* tok, int32_t* depth,
+                                int32_t* parent, float* score, int32_t* slot, uint64_t* mask, void* ws,
+                                size_t ws_bytes, void* stream) {
   TRY(check_dims(dims));
   TRY(check_head(dims, head));
   REQ_PTR(logits, 16);
@@ -467,6 +491,10 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
   st->next_depth = dims->L + 1;
   return DARTREE_OK;
 }
+
+}  // namespace dartree
+
+extern "C" {
 
 dartree_status dartree_serial_workspace_size(const dartree_dims* dims, size_t* bytes) {
   g_err[0] = 0;

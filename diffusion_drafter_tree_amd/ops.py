@@ -182,6 +182,18 @@ def build_round(dims: C.Dims, head: DeviceHead, logits: torch.Tensor, H_or_h: to
            "build_round")
 
 
+def build_round_noalloc(dims: C.Dims, head: DeviceHead, logits: torch.Tensor, H_or_h: torch.Tensor,
+                        rb: RoundBuffers, stream=None):
+    """The whole round through dartree_build_round_noalloc: the library's own
+    device scratch instead of rb.ws (which is not touched)."""
+    rb.st.next_depth = 1
+    _check(C.load().dartree_build_round_noalloc(ctypes.byref(dims), ctypes.byref(head.c), _p(logits), _p(H_or_h),
+                                                _p(rb.cand_ids), _p(rb.cand_logit), _p(rb.h), ctypes.byref(rb.st),
+                                                _p(rb.n_sel), _p(rb.tok), _p(rb.depth), _p(rb.parent),
+                                                _p(rb.score), _p(rb.slot), _p(rb.mask), _stream(stream)),
+           "build_round_noalloc")
+
+
 def run_steps(dims: C.Dims, head: DeviceHead, logits: torch.Tensor, H_or_h: torch.Tensor, rb: RoundBuffers,
               depth_chunks=None, stream=None):
     """The round through the individual entry points: head_states (D > 0),

@@ -217,6 +217,26 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
                                    int32_t* parent, float* score, int32_t* slot, uint64_t* mask, void* ws,
                                    size_t ws_bytes, void* stream);
 
+/* dartree_build_round without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, meaning, layouts, outputs
+ * and errors as dartree_build_round, minus ws / ws_bytes: the round's scratch
+ * (the scan's sorted slice lists, the fp16 copy of A) lives in a device array
+ * the library owns, DARTREE_NOALLOC_SCRATCH_BYTES per GPU (each GPU the call
+ * runs on holds its own copy until the process ends; the first call on a
+ * device looks its address up). The call allocates and frees nothing.
+ * Sizes whose workspace (dartree_workspace_size) exceeds the array return
+ * DARTREE_ERR_UNSUPPORTED before anything is enqueued. Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller. The array keeps
+ * the last call's contents; nothing in it has to start at zero. */
+#define DARTREE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+dartree_status dartree_build_round_noalloc(const dartree_dims* dims, const dartree_head* head, const void* logits,
+                                           const void* H_or_h, int32_t* cand_ids, float* cand_logit, float* h,
+                                           dartree_supertree* st, int32_t* n_sel, int32_t* tok, int32_t* depth,
+                                           int32_t* parent, float* score, int32_t* slot, uint64_t* mask,
+                                           void* stream);
+
 /* How dartree_build_round runs for these sizes; a host-only query (no device
  * work, no allocation), valid whenever dartree_workspace_size succeeds.
  *   n_launches      kernel launches per round (2: scan, tree; 3 with a separate

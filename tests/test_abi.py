@@ -271,3 +271,25 @@ def test_struct_layouts_match_the_header(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(py), cname
         for fname, _ in py._fields_:
             assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
+
+
+def test_noalloc_round_rejects_sizes_beyond_its_scratch(lib):
+    # 256 requests at K = 512: 64 MiB of slice lists, beyond the 32 MiB the
+    # allocation-free round holds; rejected on the host before any device call
+    d = dims(n_req=256, K=512, r=512, D=4096)
+    st, need = ws_size(lib, d)
+    assert st == C.OK and need > C.NOALLOC_SCRATCH_BYTES
+    head = C.Head(A=None, E=16, U=16, Pt=16)
+    sup = C.Supertree(tok=16, parent_slot=16, cum=16, sbeta=16, count=16, state=16, next_depth=1)
+    p = ctypes.c_void_p(16)
+    s = lib.dartree_build_round_noalloc(ctypes.byref(d), ctypes.byref(head), p, p, p, p, p, ctypes.byref(sup),
+                                        p, p, p, p, p, p, p, None)
+    assert s == C.ERR_UNSUPPORTED
+    assert "allocation-free" in C.last_error()
+    # the metric config's scratch fits
+    st, need = ws_size(lib, dims())
+    assert st == C.OK and need <= C.NOALLOC_SCRATCH_BYTES
+    # invalid dims are reported like dartree_build_round reports them
+    s = lib.dartree_build_round_noalloc(ctypes.byref(dims(beta=0.5)), ctypes.byref(head), p, p, p, p, p,
+                                        ctypes.byref(sup), p, p, p, p, p, p, p, None)
+    assert s == C.ERR_INVALID_ARGUMENT
