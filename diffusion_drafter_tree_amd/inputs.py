@@ -190,3 +190,47 @@ def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
 def small_variant(base: str = "tiny", **kw) -> Config:
     """A config derived from a preset, for parity tests at oracle-friendly sizes."""
     return CONFIGS[base].with_(**kw)
+
+
+# ----------------------------------------------------------------------------
+# the drafter's LM head (the step before the candidates): hidden states X and
+# head rows Wlm, both bf16
+# ----------------------------------------------------------------------------
+LMHEAD_STREAM = 2**32 - 2
+
+
+def make_lmhead(cfg: Config, seed: int = 0, chunk_rows: int = 16384) -> np.ndarray:
+    """Wlm [V][D] bf16 bits, entries N(0, sigma^2 / D) rounded to bf16, drawn
+    in chunks of rows (so a full-vocabulary head never holds fp32 copies of
+    more than one chunk)."""
+    rng = np.random.default_rng([seed, cfg.cfg_id, LMHEAD_STREAM])
+    V, D = cfg.V, cfg.D
+    out = np.empty((V, D), np.uint16)
+    scale = np.float32(cfg.sigma / np.sqrt(D))
+    for v0 in range(0, V, chunk_rows):
+        v1 = min(V, v0 + chunk_rows)
+        out[v0:v1] = f32_to_bf16_bits(rng.standard_normal((v1 - v0, D), dtype=np.float32) * scale)
+    return out
+
+
+def make_lmhead_states(cfg: Config, Wlm: np.ndarray, seed: int = 0, t: int = 0) -> np.ndarray:
+    """Hidden states X [n][L][D] bf16 bits whose logits look like the
+    configs' base logits: noise N(0, 1) plus, per (request, position), n_boost
+    distinct ids u with boost a_u ~ U(lo, hi) * decay^d (d = 1-based row of
+    the block) added along Wlm[u] / sigma^2, so that token u's logit gains
+    about a_u. Draw order: noise [n,L,D]; ids per row without replacement;
+    boosts [n,L,n_boost]."""
+    rng = np.random.default_rng([seed, cfg.cfg_id, t, 1])
+    n, L, V, D = cfg.n_req, cfg.L, cfg.V, cfg.D
+    x = rng.standard_normal((n, L, D), dtype=np.float32)
+    nb = min(cfg.n_boost, V)
+    ids = np.empty((n, L, nb), dtype=np.int64)
+    for q in range(n):
+        for i in range(L):
+            ids[q, i] = rng.choice(V, size=nb, replace=False)
+    a = rng.uniform(cfg.boost_lo, cfg.boost_hi, size=(n, L, nb)).astype(np.float32)
+    a = (a * (cfg.decay ** np.arange(1, L + 1, dtype=np.float64))[None, :, None]).astype(np.float32)
+    w32 = bf16_bits_to_f32(Wlm[ids.reshape(-1)]).reshape(n, L, nb, D)
+    x += np.einsum("qlb,qlbd->qld", a, w32).astype(np.float32) / np.float32(cfg.sigma ** 2)
+    return f32_to_bf16_bits(x)
+

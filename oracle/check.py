@@ -305,3 +305,47 @@ def check_round(cfg, head, rnd, gpu: Dict[str, np.ndarray], tol: float = 1e-4,
                     _fail(f"{where}: padding wrong at {i}")
             rep.merge(check_selection(levels, gst, sel, cfg.B, tol, where, budget=bq))
     return rep
+
+
+def check_lmhead_topk(gpu_ids: np.ndarray, gpu_vals: np.ndarray, X: np.ndarray, Wlm: np.ndarray, K: int,
+                      tol: float = 1e-4, rows=None, where="") -> Report:
+    """Fused LM head + top-K against the oracle's fp64 logits. The HIP path
+    accumulates the logits in fp32, so near-ties (within ``tol``) at the K-th
+    logit may legitimately resolve either way. Per row: ids distinct and in
+    range; each value within ``tol`` of the oracle's logit of its id; the
+    row's order follows the HIP path's own values (descending, ids ascending
+    among equal values) and never inverts two oracle logits by more than
+    ``tol``; and the set is a valid top-K (no excluded token's logit beats a
+    chosen one's by more than ``tol``). A set that differs from the oracle's
+    counts as a tie event. ``X`` [R][D] and ``Wlm`` [V][D] are float64."""
+    rep = Report()
+    rows = range(X.shape[0]) if rows is None else rows
+    for i in rows:
+        logits = np.asarray(X[i], np.float64) @ np.asarray(Wlm, np.float64).T
+        ids = np.asarray(gpu_ids[i], np.int64)
+        vals = np.asarray(gpu_vals[i], np.float64)
+        V = logits.shape[0]
+        n = min(K, V)
+        w = f"{where} row {i}"
+        if np.any(ids[:n] < 0) or np.any(ids[:n] >= V) or len(set(ids[:n].tolist())) != n:
+            _fail(f"{w}: ids out of range or repeated: {ids[:8]}")
+        err = np.abs(vals[:n] - logits[ids[:n]])
+        rep.max_score_err = max(rep.max_score_err, float(err.max()))
+        if err.max() > tol:
+            j = int(err.argmax())
+            _fail(f"{w}: value of id {ids[j]} is {vals[j]:.7f}, oracle {logits[ids[j]]:.7f}")
+        for j in range(1, n):
+            if not (vals[j - 1] > vals[j] or (vals[j - 1] == vals[j] and ids[j - 1] < ids[j])):
+                _fail(f"{w}: order broken at {j}: ({vals[j-1]}, {ids[j-1]}) then ({vals[j]}, {ids[j]})")
+            if logits[ids[j]] > logits[ids[j - 1]] + tol:
+                _fail(f"{w}: positions {j-1}, {j} invert oracle logits by more than tol")
+        o_ids, _ = O.topk_candidates(logits, n)
+        chosen = set(ids[:n].tolist())
+        if chosen != set(o_ids.tolist()):
+            score = {v: float(logits[v]) for v in range(V)}
+            _check_cut(chosen, score, tol, w, "chosen")
+            rep.tie_events_level += 1
+            rep.tie_log.append(f"{w}: K-th oracle logit {logits[o_ids[-1]]:.9f}")
+        rep.nodes_checked += n
+    return rep
+

@@ -47,6 +47,9 @@ notes of the repository):
       attends to the nodes whose bit is set in mask row i, softmax of the
       scaled dot products (the prefix's keys, which every node also sees, are
       left out of this synthetic step).
+  R15 the drafter's LM head (the step before the candidates) is a synthetic
+      bf16 matrix Wlm [V][D] over the block's final hidden states X [R][D]:
+      base logits = X Wlm^T; the pages give no architecture or precision.
   R13 the Markov head of section 4.3 (Table 3), whose architecture the pages
       do not state, is the synthetic head with A = 0: a node's state is
       tanh(E[u] + h_d), so its children's distribution depends on its token
@@ -87,6 +90,32 @@ def topk_candidates(row: np.ndarray, K: int):
     order = np.lexsort((ids, -v))
     sel = order[:K]
     return sel.astype(np.int64), v[sel]
+
+
+# ----------------------------------------------------------------------------
+# the step before a1: the drafter's LM head (blog section 3.1, basic flow: one
+# block-parallel forward of the drafter gives the block's base logits, from
+# which the candidates are taken)
+# ----------------------------------------------------------------------------
+def lmhead_logits(X: np.ndarray, Wlm: np.ndarray) -> np.ndarray:
+    """Base logits of a synthetic drafter LM head: logits[i][v] = sum_j
+    X[i][j] * Wlm[v][j] for hidden states X [R][D] and head rows Wlm [V][D]
+    (both widened to float64; one library matrix product)."""
+    return np.asarray(X, dtype=np.float64) @ np.asarray(Wlm, dtype=np.float64).T
+
+
+def lmhead_topk(X: np.ndarray, Wlm: np.ndarray, K: int):
+    """Candidates straight from the hidden states: the base logits of the LM
+    head, then the K best of each row as in topk_candidates (value descending,
+    token id ascending). Returns (ids int64[R][K], values float64[R][K],
+    logits float64[R][V])."""
+    logits = lmhead_logits(X, Wlm)
+    R = logits.shape[0]
+    ids = np.empty((R, K), np.int64)
+    vals = np.empty((R, K), np.float64)
+    for i in range(R):
+        ids[i], vals[i] = topk_candidates(logits[i], K)
+    return ids, vals, logits
 
 
 # ----------------------------------------------------------------------------
