@@ -331,6 +331,47 @@ dartree_status dartree_topk_candidates(const dartree_dims* dims, const void* log
   return DARTREE_OK;
 }
 
+dartree_status lmhead_check(const dartree_dims* dims, dartree::LmheadPlan* p) {
+  TRY(check_dims(dims));
+  if (dims->weight_dtype != DARTREE_BF16)
+    return fail(DARTREE_ERR_UNSUPPORTED, "the fused LM head takes bf16 hidden states and head rows");
+  *p = dartree::lmhead_plan(dims->n_req * dims->L, dims->V, dims->D, dims->K);
+  if (!p->ok)
+    return fail(DARTREE_ERR_UNSUPPORTED,
+                "fused LM head limits: K <= 64, D >= 256 and a multiple of 256, V <= 262144 (got K=%d D=%d V=%d)",
+                dims->K, dims->D, dims->V);
+  return DARTREE_OK;
+}
+
+dartree_status dartree_lmhead_workspace_size(const dartree_dims* dims, size_t* bytes) {
+  g_err[0] = 0;
+  dartree::LmheadPlan p;
+  TRY(lmhead_check(dims, &p));
+  if (!bytes) return fail(DARTREE_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = (p.list_bytes + 255) & ~(size_t)255;
+  return DARTREE_OK;
+}
+
+dartree_status dartree_lmhead_topk(const dartree_dims* dims, const void* X, const void* Wlm, int32_t* cand_ids,
+                                   float* cand_logit, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  dartree::LmheadPlan p;
+  TRY(lmhead_check(dims, &p));
+  REQ_PTR(X, 16);
+  REQ_PTR(Wlm, 16);
+  REQ_PTR(cand_ids, 4);
+  REQ_PTR(cand_logit, 4);
+  REQ_PTR(ws, 256);
+  if (ws_bytes < p.list_bytes)
+    return fail(DARTREE_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", ws_bytes, p.list_bytes);
+  hipError_t e = dartree::launch_lmhead_topk(p, static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(Wlm),
+                                             dims->n_req * dims->L, dims->V, dims->D, dims->K,
+                                             static_cast<uint64_t*>(ws), cand_ids, cand_logit,
+                                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "lmhead launch");
+  return DARTREE_OK;
+}
+
 dartree_status dartree_expand_depth(const dartree_dims* dims, const dartree_head* head, const int32_t* cand_ids,
                                     const float* cand_logit, const float* h, dartree_supertree* st,
                                     int32_t depth_begin, int32_t depth_end, void* stream) {

@@ -101,6 +101,21 @@ hipError_t launch_tree_fast(const TreePlan& p, const TreeArgs& a, hipStream_t s)
 
 hipError_t launch_mask(int n_req, int B, const int32_t* n_sel, const int32_t* parent, uint64_t* mask, hipStream_t s);
 
+// ---- the drafter's LM head fused with the top-K (the step before a1) ---------
+struct LmheadPlan {
+  int S;           // vocabulary slabs (workgroups per 16 rows)
+  int ntiles;      // 16-column tiles of the vocabulary
+  int slab_cols;   // columns of the widest slab
+  int kc;          // D chunk staged in LDS
+  int ring;        // k-steps of head loads in flight a wave
+  size_t smem, list_bytes;
+  bool ok;
+};
+// bf16 X [rows][D] and Wlm [V][D]; K <= 64, D a multiple of 256
+LmheadPlan lmhead_plan(int rows, int V, int D, int K);
+hipError_t launch_lmhead_topk(const LmheadPlan& p, const uint16_t* X, const uint16_t* Wlm, int rows, int V, int D,
+                              int K, uint64_t* lists, int32_t* cand_ids, float* cand_logit, hipStream_t s);
+
 // ---- heap-serial construction (the "pop then correct" baseline) -------------
 constexpr int kSerialMaxB = 511;   // pop indices pack into 9 bits of the node key
 struct SerialArgs {

@@ -1,0 +1,291 @@
+// The drafter's LM head fused with the top-K of its logits: candidates taken
+// straight from the block's hidden states, the logits never written out.
+//
+// DARTree (marsggbo blog, section 3.1, basic flow): one block-parallel forward
+// of the diffusion drafter gives the block's base logits, and each position's
+// K best tokens are the candidates the tree is built from. Here the base
+// logits are logits[i][v] = sum_j X[i][j] * Wlm[v][j] for the block's final
+// hidden states X [rows][D] and a synthetic head Wlm [V][D], both bf16.
+//
+// Launch 1 (lmhead_topk_kernel), grid S x ceil(rows / 16): workgroup (s, g)
+// owns rows 16g..16g+15 and slab s of the vocabulary (consecutive 16-column
+// tiles, ntiles * s / S .. ntiles * (s + 1) / S). Eight waves; wave w takes
+// the slab's tiles w, w + 8, ... Per D chunk staged in LDS (the 16 hidden rows,
+// bf16), each wave streams its tiles' head rows through a register ring of
+// k-steps (16 bytes a lane a step, loads issued RING steps ahead) into
+// v_mfma_f32_16x16x32_bf16 (products of bf16 are exact, fp32 accumulation)
+// and adds each finished tile into the slab's logits in LDS. Then one wave per
+// row selects the row's K best logits of the slab exactly: the K-th largest
+// 32-bit order key by a bit search over ballot counts, the keys above it and
+// the lowest columns among those equal to it, sorted by a 64-lane network, and
+// writes them as a sorted list of (value key << 32 | ~id).
+// Launch 2 (lmhead_merge_kernel): the S lists of each row merged into its K
+// candidates (value descending, id ascending) by bitonic list merges.
+//
+// The head's HBM stream is the whole cost: V * D * 2 bytes (778 MB at
+// V = 151936, D = 2560) against 2 * rows * V * D flops (12.4 GFLOP at 16
+// rows), 16 flop a byte, far below the bf16 MFMA ridge. The slab lists are
+// rows * S * K * 8 bytes (2 MiB at 16 rows, S = 256, K = 64).
+#include "common.h"
+#include "kernels.h"
+
+namespace dartree {
+
+namespace {
+
+constexpr int kLT = 512;                // threads a workgroup
+constexpr int kLW = kLT / kWave;        // 8 waves
+constexpr int kTPW = 8;                 // tiles a wave may own: a slab has <= 64 tiles
+constexpr int kSlabTiles = kLW * kTPW;  // 64 tiles, 1024 columns
+constexpr int kMaxSlabs = 256;          // slabs a row: 16 lists a merge wave
+constexpr size_t kLdsMax = 160 * 1024;
+
+struct LmArgs {
+  const uint16_t* X;   // [rows][D]
+  const uint16_t* W;   // [V][D]
+  int rows, V, D, K, S, ntiles, kc, slab_cols;
+  uint64_t* lists;     // [rows][S][K]
+};
+
+template <int RING>
+__global__ __launch_bounds__(kLT) void lmhead_topk_kernel(LmArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int s = blockIdx.x, r0 = blockIdx.y * 16;
+  const int nr = min(16, a.rows - r0);
+  const int t0 = (int)((int64_t)s * a.ntiles / a.S), t1 = (int)((int64_t)(s + 1) * a.ntiles / a.S);
+  const int nt = t1 - t0;
+  const int col0 = t0 * 16;
+  const int ncol = min(t1 * 16, a.V) - col0;
+  const int XSTR = a.kc + 8;           // bf16 elements; rows 16 bytes apart in bank terms
+  const int LSTR = a.slab_cols + 4;    // floats
+  LDS uint16_t* Xs = (LDS uint16_t*)smem;
+  LDS float* lg = (LDS float*)(smem + (size_t)16 * XSTR * 2);
+  LDS uint64_t* sel = (LDS uint64_t*)(smem + (size_t)16 * XSTR * 2 + (size_t)16 * LSTR * 4);
+
+  for (int i = tid; i < 16 * LSTR; i += kLT) lg[i] = 0.f;
+
+  const int my_nt = nt > w ? (nt - w + kLW - 1) / kLW : 0;
+  const int m16 = lane & 15, sub = (lane >> 4) * 8;
+
+  for (int c0 = 0; c0 < a.D; c0 += a.kc) {
+    const int kc = min(a.kc, a.D - c0);   // a multiple of 32 * RING
+    // every wave is done with the previous chunk (and lg is cleared) before
+    // the hidden rows of this chunk are staged
+    __syncthreads();
+    const int vpr = kc / 8;   // 16-byte vectors a row
+    for (int i = tid; i < 16 * vpr; i += kLT) {
+      const int r = i / vpr, c = (i - r * vpr) * 8;
+      u16x8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (r < nr) v = *reinterpret_cast<const u16x8_t*>(a.X + (size_t)(r0 + r) * a.D + c0 + c);
+      *reinterpret_cast<LDS u16x8_t*>(Xs + r * XSTR + c) = v;
+    }
+    __syncthreads();
+
+    // The wave's work in this chunk: its tiles j = 0..my_nt-1, each nks
+    // k-steps of 32, taken in groups of RING k-steps (nks is a multiple of
+    // RING). Two register rings alternate: while one group's MFMAs read one
+    // ring, the next group's loads are in flight into the other, issued at the
+    // start of the group. Past the last group the loads repeat the last group
+    // (every load is issued, so the compiler's wait for a ring counts exactly
+    // the RING younger loads of the other one).
+    const int nks = kc / 32;
+    const int gpt = nks / RING;          // groups a tile
+    const int ngroups = my_nt * gpt;
+    if (ngroups > 0) {
+      auto load_group = [&](u16x8_t (&r)[RING], int g) {
+        g = min(g, ngroups - 1);
+        const int j = g / gpt, kg = g - j * gpt;
+        const int col = min(col0 + (w + j * kLW) * 16 + m16, a.V - 1);
+        const u16x8_t* src = reinterpret_cast<const u16x8_t*>(a.W + (size_t)col * a.D + c0 + kg * RING * 32 + sub);
+#pragma unroll
+        for (int u = 0; u < RING; ++u) r[u] = src[u * 4];
+      };
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      auto mma_group = [&](const u16x8_t (&r)[RING], int g) {
+        const int j = g / gpt, kg = g - j * gpt;
+        const LDS uint16_t* xs = Xs + m16 * XSTR + kg * RING * 32 + sub;
+#pragma unroll
+        for (int u = 0; u < RING; ++u) {
+          const u16x8_t xa = *reinterpret_cast<const LDS u16x8_t*>(xs + u * 32);
+          acc = mfma_bf16(xa, r[u], acc);
+        }
+        if (kg == gpt - 1) {
+          // tile j done for this chunk: rows 4 (lane / 16) + e, column m16
+          LDS float* dst = lg + (4 * (lane >> 4)) * LSTR + (w + j * kLW) * 16 + m16;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[e * LSTR] += acc[e];
+          acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+      };
+      u16x8_t ra[RING], rb[RING];
+      load_group(ra, 0);
+      for (int g = 0; g < ngroups; g += 2) {
+        load_group(rb, g + 1);
+        mma_group(ra, g);
+        load_group(ra, g + 2);
+        if (g + 1 < ngroups) mma_group(rb, g + 1);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- the slab's K best of each row: one wave a row --------------------------
+  constexpr int NJ = kSlabTiles * 16 / kWave;   // 16 keys a lane at most
+  LDS uint64_t* sw = sel + w * kWave;
+  for (int r = w; r < nr; r += kLW) {
+    const LDS float* rowp = lg + r * LSTR;
+    uint32_t vk[NJ];
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int c = lane + jj * kWave;
+      vk[jj] = c < ncol ? f32_key(rowp[c]) : 0u;   // 0: no column (finite logits never map to 0)
+    }
+    const int nj = (ncol + kWave - 1) / kWave;
+    // T = the K-th largest key of the slab (0 when the slab holds <= K
+    // columns): the largest t with at least K keys >= t, bit by bit
+    uint32_t T = 0u;
+    if (ncol > a.K) {
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t t = T | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+          if (jj < nj) cnt += __popcll(__ballot(vk[jj] >= t));
+        if (cnt >= a.K) T = t;
+      }
+    }
+    int gt = 0;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+      if (jj < nj) gt += __popcll(__ballot(vk[jj] > T));
+    const int need_eq = a.K - gt;   // keys equal to T taken, lowest columns first
+    int base = 0, eq_seen = 0;
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      if (jj < nj) {
+        const bool eq = T != 0u && vk[jj] == T;
+        const uint64_t be = __ballot(eq);
+        const bool take = vk[jj] > T || (eq && eq_seen + (int)mbcnt64(be) < need_eq);
+        const uint64_t bt = __ballot(take);
+        if (take) {
+          const uint32_t id = (uint32_t)(col0 + lane + jj * kWave);
+          sw[base + (int)mbcnt64(bt)] = ((uint64_t)vk[jj] << 32) | (uint64_t)(0xFFFFFFFFu - id);
+        }
+        base += __popcll(bt);
+        eq_seen += __popcll(be);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t key = lane < base ? sw[lane] : 0ull;
+    uint32_t hi = (uint32_t)(key >> 32), lo = (uint32_t)key;
+    wave_sort_desc(hi, lo);
+    if (lane < a.K)
+      a.lists[((size_t)(r0 + r) * a.S + s) * a.K + lane] = ((uint64_t)hi << 32) | lo;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// The S sorted lists of each row (K <= 64 keys each, descending, zero
+// padded) merged into the row's K best, one workgroup a row: wave w merges
+// lists w, w + 16, ... pairwise in registers (the elementwise maximum of one
+// descending list and the other reversed holds the 64 best of both as a
+// bitonic sequence, which six half-cleaner stages sort descending), the 16
+// waves' results meet in LDS, and wave 0 merges those the same way.
+constexpr int kMT = 1024, kMW = kMT / kWave;
+
+__device__ __forceinline__ void merge_into(uint32_t& ah, uint32_t& al, uint64_t b) {
+  const uint32_t bh = lane_rev((uint32_t)(b >> 32)), bl = lane_rev((uint32_t)b);
+  const bool tb = (((uint64_t)bh << 32) | bl) > (((uint64_t)ah << 32) | al);
+  ah = tb ? bh : ah;
+  al = tb ? bl : al;
+  bitonic_stage<64, 32>(ah, al);
+  bitonic_stage<64, 16>(ah, al);
+  bitonic_stage<64, 8>(ah, al);
+  bitonic_stage<64, 4>(ah, al);
+  bitonic_stage<64, 2>(ah, al);
+  bitonic_stage<64, 1>(ah, al);
+}
+
+__global__ __launch_bounds__(kMT) void lmhead_merge_kernel(const uint64_t* __restrict__ lists, int S, int K,
+                                                           int32_t* __restrict__ cand_ids,
+                                                           float* __restrict__ cand_logit) {
+  __shared__ uint64_t part[kMW][kWave];
+  const int row = blockIdx.x, lane = lane_id(), w = threadIdx.x / kWave;
+  const uint64_t* L = lists + (size_t)row * S * K;
+  const bool v = lane < K;
+  uint32_t ah = 0u, al = 0u;
+  if (w < S) {
+    const uint64_t k0 = v ? L[(size_t)w * K + lane] : 0ull;
+    ah = (uint32_t)(k0 >> 32);
+    al = (uint32_t)k0;
+    for (int sl = w + kMW; sl < S; sl += kMW) merge_into(ah, al, v ? L[(size_t)sl * K + lane] : 0ull);
+  }
+  part[w][lane] = ((uint64_t)ah << 32) | al;
+  __syncthreads();
+  if (w == 0) {
+    for (int i = 1; i < kMW; ++i) merge_into(ah, al, part[i][lane]);
+    if (v) {
+      const bool ok = (ah | al) != 0u;
+      cand_ids[(size_t)row * K + lane] = ok ? (int32_t)(0xFFFFFFFFu - al) : -1;
+      cand_logit[(size_t)row * K + lane] = ok ? key_to_f32(ah) : -__builtin_huge_valf();
+    }
+  }
+}
+
+}  // namespace
+
+LmheadPlan lmhead_plan(int rows, int V, int D, int K) {
+  LmheadPlan p{};
+  p.ok = false;
+  if (rows < 1 || V < 1 || K < 1 || K > kWave || K > V || D < 256 || D % 256 != 0) return p;
+  p.ntiles = (V + 15) / 16;
+  p.S = min(kMaxSlabs, p.ntiles);
+  const int tiles_per_slab = (p.ntiles + p.S - 1) / p.S;
+  if (tiles_per_slab > kSlabTiles) return p;
+  p.slab_cols = tiles_per_slab * 16;
+  p.ring = D % 512 == 0 ? 16 : 8;
+  const size_t fixed = (size_t)16 * (p.slab_cols + 4) * 4 + (size_t)kLW * kWave * 8;
+  const int step = 32 * p.ring;
+  // the largest chunk of D (a multiple of 32 * ring) whose staged rows fit
+  int kc = D;
+  while (kc > step && fixed + (size_t)16 * (kc + 8) * 2 > kLdsMax) kc -= step;
+  if (fixed + (size_t)16 * (kc + 8) * 2 > kLdsMax) return p;
+  p.kc = kc;
+  p.smem = fixed + (size_t)16 * (kc + 8) * 2;
+  p.list_bytes = (size_t)rows * p.S * K * sizeof(uint64_t);
+  p.ok = true;
+  return p;
+}
+
+hipError_t launch_lmhead_topk(const LmheadPlan& p, const uint16_t* X, const uint16_t* Wlm, int rows, int V, int D,
+                              int K, uint64_t* lists, int32_t* cand_ids, float* cand_logit, hipStream_t s) {
+  LmArgs a{};
+  a.X = X;
+  a.W = Wlm;
+  a.rows = rows;
+  a.V = V;
+  a.D = D;
+  a.K = K;
+  a.S = p.S;
+  a.ntiles = p.ntiles;
+  a.kc = p.kc;
+  a.slab_cols = p.slab_cols;
+  a.lists = lists;
+  const dim3 grid((unsigned)p.S, (unsigned)((rows + 15) / 16));
+  const void* fn = p.ring == 16 ? (const void*)lmhead_topk_kernel<16> : (const void*)lmhead_topk_kernel<8>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.smem);
+  if (e != hipSuccess) return e;
+  if (p.ring == 16)
+    hipLaunchKernelGGL((lmhead_topk_kernel<16>), grid, dim3(kLT), p.smem, s, a);
+  else
+    hipLaunchKernelGGL((lmhead_topk_kernel<8>), grid, dim3(kLT), p.smem, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lmhead_merge_kernel, dim3(rows), dim3(kMT), 0, s, lists, p.S, K, cand_ids, cand_logit);
+  return hipGetLastError();
+}
+
+}  // namespace dartree

@@ -153,6 +153,20 @@ def topk_candidates(dims: C.Dims, logits: torch.Tensor, cand_ids: torch.Tensor, 
                                             ws.numel(), _stream(stream)), "topk_candidates")
 
 
+def lmhead_workspace_size(dims: C.Dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(C.load().dartree_lmhead_workspace_size(ctypes.byref(dims), ctypes.byref(n)), "lmhead_workspace_size")
+    return int(n.value)
+
+
+def lmhead_topk(dims: C.Dims, X: torch.Tensor, Wlm: torch.Tensor, cand_ids: torch.Tensor, cand_logit: torch.Tensor,
+                ws: torch.Tensor, stream=None):
+    """Candidates straight from the drafter's hidden states through
+    dartree_lmhead_topk (the LM head fused with the top-K)."""
+    _check(C.load().dartree_lmhead_topk(ctypes.byref(dims), _p(X), _p(Wlm), _p(cand_ids), _p(cand_logit), _p(ws),
+                                        ws.numel(), _stream(stream)), "lmhead_topk")
+
+
 def expand_depth(dims: C.Dims, head: DeviceHead, cand_ids: torch.Tensor, cand_logit: torch.Tensor,
                  h: torch.Tensor, rb: RoundBuffers, depth_begin: int, depth_end: int, stream=None):
     _check(C.load().dartree_expand_depth(ctypes.byref(dims), ctypes.byref(head.c), _p(cand_ids), _p(cand_logit),

@@ -168,6 +168,24 @@ dartree_status dartree_head_states(const dartree_dims* dims, const void* H, cons
 dartree_status dartree_topk_candidates(const dartree_dims* dims, const void* logits, int32_t* cand_ids,
                                        float* cand_logit, void* ws, size_t ws_bytes, void* stream);
 
+/* The step before a1, fused with it (marsggbo section 3.1, basic flow: one
+ * block-parallel forward of the diffusion drafter gives the block's base
+ * logits, whose K best tokens per position are the candidates): for each of
+ * the n*L rows of X[n][L][D] (the block's final hidden states, bf16), the base
+ * logits logits[v] = sum_j X[j] * Wlm[v][j] of a drafter LM head Wlm[V][D]
+ * (bf16; products exact, fp32 accumulation) and their K best, written as
+ * cand_ids[n][L][K] int32 / cand_logit[n][L][K] fp32 in the order of
+ * dartree_topk_candidates (value descending, ties by token id ascending). The
+ * logits themselves are never written to memory. Uses dims n_req, L, V, K, D
+ * and weight_dtype (must be DARTREE_BF16; UNSUPPORTED otherwise); limits
+ * K <= 64, D >= 256 and a multiple of 256 (UNSUPPORTED otherwise). ws is a
+ * device workspace of dartree_lmhead_workspace_size bytes (256-byte aligned),
+ * overwritten. The fp32 accumulation order is the kernel's: a logit within
+ * its rounding of the K-th may fall on either side of the cut. */
+dartree_status dartree_lmhead_workspace_size(const dartree_dims* dims, size_t* bytes);
+dartree_status dartree_lmhead_topk(const dartree_dims* dims, const void* X, const void* Wlm, int32_t* cand_ids,
+                                   float* cand_logit, void* ws, size_t ws_bytes, void* stream);
+
 /* Steps a2 + a3 (marsggbo section 3.1, depth-by-depth expansion and the score
  * equation; AINews: one batched head call per depth): expands depths
  * depth_begin..depth_end (1 <= depth_begin <= depth_end <= L, and depth_begin
