@@ -30,8 +30,11 @@ class Dims(ctypes.Structure):
                 ("logits_dtype", c_int32), ("weight_dtype", c_int32)]
 
 
+HEAD_EXACT = 1   # DARTREE_HEAD_EXACT
+
+
 class Head(ctypes.Structure):
-    _fields_ = [("A", c_void_p), ("E", c_void_p), ("U", c_void_p), ("Pt", c_void_p)]
+    _fields_ = [("A", c_void_p), ("E", c_void_p), ("U", c_void_p), ("Pt", c_void_p), ("flags", c_int32)]
 
 
 class RoundInfo(ctypes.Structure):
@@ -58,6 +61,7 @@ SIGNATURES = {
     "dartree_round_plan": (c_int32, [PD, POINTER(RoundInfo)]),
     "dartree_workspace_init": (c_int32, [PD, c_void_p, c_size_t, c_void_p]),
     "dartree_head_states": (c_int32, [PD, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "dartree_head_check": (c_int32, [PD, PH, c_void_p, c_void_p]),
     "dartree_topk_candidates": (c_int32, [PD, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "dartree_expand_depth": (c_int32, [PD, PH, c_void_p, c_void_p, c_void_p, PS, c_int32, c_int32, c_void_p]),
     "dartree_select_topB": (c_int32, [PD, PS, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -100,6 +100,7 @@ dartree_status check_ws(const dartree_dims* d, void* ws, size_t ws_bytes, WsLayo
 
 dartree_status check_head(const dartree_dims* d, const dartree_head* h) {
   if (!h) return fail(DARTREE_ERR_INVALID_ARGUMENT, "head is NULL");
+  if (h->flags & ~DARTREE_HEAD_EXACT) return fail(DARTREE_ERR_INVALID_ARGUMENT, "unknown head flags 0x%x", h->flags);
   if (h->A != nullptr) REQ_PTR(h->A, 16);   // NULL: the Markov head (A = 0)
   REQ_PTR(h->E, 16);
   REQ_PTR(h->U, 16);
@@ -148,6 +149,7 @@ dartree::TreeArgs tree_args(const dartree_dims* dims, const dartree_head* head, 
   a.beta = dims->beta;
   a.bf16 = dims->weight_dtype == DARTREE_BF16;
   if (head) {
+    a.exact = (head->flags & DARTREE_HEAD_EXACT) != 0;
     a.A = head->A;
     a.E = head->E;
     a.U = head->U;
@@ -226,7 +228,7 @@ const char* dartree_status_string(dartree_status s) {
 
 const char* dartree_last_error(void) { return g_err; }
 
-int32_t dartree_version(void) { return 2; }
+int32_t dartree_version(void) { return 3; }
 
 dartree_status dartree_round_plan(const dartree_dims* dims, dartree_round_info* info) {
   g_err[0] = 0;
@@ -285,6 +287,20 @@ dartree_status dartree_workspace_init(const dartree_dims* dims, void* ws, size_t
   WsLayout w;
   TRY(check_ws(dims, ws, ws_bytes, &w));
   (void)stream;   // the current kernels keep no state in the workspace between calls
+  return DARTREE_OK;
+}
+
+dartree_status dartree_head_check(const dartree_dims* dims, const dartree_head* head, int32_t* flags, void* stream) {
+  g_err[0] = 0;
+  TRY(check_dims(dims));
+  TRY(check_head(dims, head));
+  REQ_PTR(flags, 4);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dims->weight_dtype == DARTREE_BF16
+                     ? dartree::launch_head_check(static_cast<const uint16_t*>(head->A),
+                                                  static_cast<const uint16_t*>(head->U), dims->V, dims->r, flags, s)
+                     : dartree::launch_fill_u32(flags, 1, 0u, s);
+  if (e != hipSuccess) return hip_fail(e, "head check launch");
   return DARTREE_OK;
 }
 

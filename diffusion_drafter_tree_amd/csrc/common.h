@@ -340,8 +340,11 @@ __device__ __forceinline__ h16x2_t pkrtz(float a, float b) {
   return __builtin_bit_cast(h16x2_t, (fp16x2_t)__builtin_amdgcn_cvt_pkrtz(a, b));
 }
 
-// 8 bf16 weights as fp16 (exact for every bf16 value of magnitude >= 2^-17
-// or zero; smaller ones are truncated by at most 2^-25)
+// 8 bf16 weights as fp16: exact for bf16 values of magnitude in [2^-17, 2^16)
+// or zero; smaller ones are truncated by at most 2^-25; magnitudes of 2^16 or
+// more are beyond fp16 and come out as +-65504 (rounding toward zero), so
+// callers must keep such weights away (the block-decoding kernel's
+// precondition)
 __device__ __forceinline__ h16x8_t bf16x8_to_f16(u16x8_t x) {
   h16x8_t r;
 #pragma unroll

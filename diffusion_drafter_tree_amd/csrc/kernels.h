@@ -52,6 +52,7 @@ struct TreeArgs {
   int n_req, L, V, K, W, B, r;
   float beta;
   bool bf16;
+  bool exact;                 // the head asks for the exact (split-bf16) general kernel
   const void* A;
   const void* E;
   const void* U;
@@ -154,5 +155,9 @@ struct VerifyArgs {
 };
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t s);
 hipError_t launch_fill_u32(void* p, size_t n_words, uint32_t value, hipStream_t s);
+
+// bf16 head weights beyond fp16's range (magnitude >= 2^16): *flags gets
+// bit 0 for A (r x r, may be null), bit 1 for U (V x r)
+hipError_t launch_head_check(const uint16_t* A, const uint16_t* U, int V, int r, int32_t* flags, hipStream_t s);
 
 }  // namespace dartree

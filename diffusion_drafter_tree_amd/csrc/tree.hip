@@ -851,6 +851,50 @@ hipError_t launch_mask(int n_req, int B, const int32_t* n_sel, const int32_t* pa
   return hipGetLastError();
 }
 
+namespace {
+
+// 1 when either bf16 half of x has magnitude >= 2^16 (exponent field >= 143:
+// beyond fp16's largest finite value; infinities and NaNs included)
+__device__ __forceinline__ bool beyond_f16(uint32_t x) {
+  return (x & 0x7FFFu) >= 0x4780u || ((x >> 16) & 0x7FFFu) >= 0x4780u;
+}
+
+__global__ __launch_bounds__(256) void head_check_kernel(const uint16_t* __restrict__ A, size_t nA,
+                                                         const uint16_t* __restrict__ U, size_t nU,
+                                                         int32_t* __restrict__ flags) {
+  const size_t T = (size_t)gridDim.x * blockDim.x, t0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int f = 0;
+  // whole 16-byte vectors, then the elements of a ragged end
+  const size_t vA = nA / 8, vU = nU / 8;
+  for (size_t i = t0; i < vU; i += T) {
+    const u32x4_t v = reinterpret_cast<const u32x4_t*>(U)[i];
+    if (beyond_f16(v.x) || beyond_f16(v.y) || beyond_f16(v.z) || beyond_f16(v.w)) f |= 2;
+  }
+  for (size_t i = vU * 8 + t0; i < nU; i += T)
+    if (beyond_f16(U[i])) f |= 2;
+  if (A) {
+    for (size_t i = t0; i < vA; i += T) {
+      const u32x4_t v = reinterpret_cast<const u32x4_t*>(A)[i];
+      if (beyond_f16(v.x) || beyond_f16(v.y) || beyond_f16(v.z) || beyond_f16(v.w)) f |= 1;
+    }
+    for (size_t i = vA * 8 + t0; i < nA; i += T)
+      if (beyond_f16(A[i])) f |= 1;
+  }
+  // one global atomic a wave, and only from a wave that found something
+  const int wf = (__ballot(f & 1) ? 1 : 0) | (__ballot(f & 2) ? 2 : 0);
+  if (wf && lane_id() == 0) __hip_atomic_fetch_or(flags, wf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+hipError_t launch_head_check(const uint16_t* A, const uint16_t* U, int V, int r, int32_t* flags, hipStream_t s) {
+  hipError_t e = launch_fill_u32(flags, 1, 0u, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(head_check_kernel, dim3(1024), dim3(256), 0, s, A, A ? (size_t)r * r : 0, U, (size_t)V * r,
+                     flags);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_u32(void* p, size_t n_words, uint32_t value, hipStream_t s) {
   if (n_words == 0) return hipSuccess;
   size_t g = (n_words + 255) / 256;

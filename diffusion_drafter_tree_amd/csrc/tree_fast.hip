@@ -12,9 +12,13 @@
 // then depth, token and parent slot ascending.
 //
 // Numerics: parent states as two fp16 planes (hi + lo, within 2^-20 of the
-// fp32 state), weights as fp16 (exact for bf16 values of magnitude >= 2^-17),
-// products on v_mfma_f32_16x16x32_f16 with fp32 accumulation; fp32
-// log-softmax on the hardware exp2 / log2.
+// fp32 state; the root state h_0 scaled by a power of two into fp16 range
+// first), weights as fp16: exact for bf16 values of magnitude in
+// [2^-17, 2^16) or zero, smaller ones truncated by at most 2^-25, and values
+// of magnitude 2^16 or more beyond fp16's range -- a head with such A or U
+// entries must go to the general kernel (DARTREE_HEAD_EXACT, found by
+// dartree_head_check). Products on v_mfma_f32_16x16x32_f16 with fp32
+// accumulation; fp32 log-softmax on the hardware exp2 / log2.
 //
 // Prologue: the scan's sorted slice lists merged per row (one wave per row),
 // A fragments from the fp16 copy the scan launch staged, the root state split.
@@ -374,6 +378,18 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       for (int i = 0; i < 4; ++i) araw[t][i] = *reinterpret_cast<const u16x8_t*>(arow + kstep(i) * 32);
     }
   }
+  if (expand && a.d0 == 1 && w == 0) {
+    // The root state h_0 is not bounded like the tanh states below it: it is
+    // held in the fp16 planes as h_0 * 2^-t, with t the smallest shift that
+    // brings max |h_0| under 2^15, and the depth-1 products it feeds (its Z
+    // row and its A*s) are multiplied by 2^t again. Power-of-two scaling is
+    // exact, and t = 0 leaves every value as it was.
+    const float m = wave_max_f32(fmaxf(fmaxf(fabsf(h0[0]), fabsf(h0[1])), fmaxf(fabsf(h0[2]), fabsf(h0[3]))));
+    const int t = m >= 32768.f ? __builtin_amdgcn_frexp_expf(m) - 15 : 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h0[e] = __builtin_amdgcn_ldexpf(h0[e], -t);
+    if (lane == 0) s.misc[8] = t;
+  }
   if (expand) {
     // parents of the first expanded depth: the root (state h_0) or the stored level
     if (a.d0 > 1) Wp = min(max(a.st_count[(size_t)q * L + a.d0 - 2], 1), W);
@@ -451,6 +467,8 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
     }
   }
   lds_sync();
+  // 2^t of the root state's scale (1 when the launch starts below depth 1)
+  const float root_scale = __builtin_amdgcn_ldexpf(1.f, s.misc[8]);
 
   // ---- the depth loop ----------------------------------------------------------
   for (int d = a.d0; d <= a.d1; ++d) {
@@ -532,6 +550,7 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       float zs = 0.f;
 #pragma unroll
       for (int qq = 0; qq < C::KQ; ++qq) zs += s.Zp[(qq * 16 + p) * C::ZSTR + kk];
+      if (d == 1) zs *= root_scale;
       const float z = v ? zs + s.clog[(d - 1) * KC + kk] : -__builtin_huge_valf();
       const int tok = s.cid[(d - 1) * KC + kk];
       const float cp = d == 1 ? 0.f : s.lv_cum[(d - 2) * W + p];
@@ -645,6 +664,7 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
         const f32x4_t a0 = *reinterpret_cast<const LDS f32x4_t*>(s.AS + p * ASTR + j0);
         const f32x4_t a1 = *reinterpret_cast<const LDS f32x4_t*>(s.AS + (16 + p) * ASTR + j0);
         as4 = a0 + a1;
+        if (d == 1) as4 *= root_scale;
       }
       const u32x2_t e2 = *reinterpret_cast<const LDS u32x2_t*>(s.EC + (size_t)k * RT + j0);
       const f32x4_t h4 = *reinterpret_cast<const LDS f32x4_t*>(s.hb + j0);
@@ -867,7 +887,7 @@ TreePlan tree_fast_plan(const TreeArgs& a) {
   p.ok = false;
   const bool al = ((((uintptr_t)a.A) | ((uintptr_t)a.E) | ((uintptr_t)a.U) | ((uintptr_t)a.h) |
                     ((uintptr_t)a.st_state)) & 15u) == 0;
-  if (!a.bf16 || a.r != RT || !(a.K == 16 || a.K == 32 || a.K == 64) || a.W > kWMax || a.W < 1 || a.V < a.K ||
+  if (a.exact || !a.bf16 || a.r != RT || !(a.K == 16 || a.K == 32 || a.K == 64) || a.W > kWMax || a.W < 1 || a.V < a.K ||
       a.L > kLMax || a.B > 1024 || !al || (a.lists && a.S > kMaxMergeS))
     return p;
   p.mode = 3;

@@ -56,15 +56,28 @@ def to_device(arr: Optional[np.ndarray], device="cuda") -> Optional[torch.Tensor
 class DeviceHead:
     """Head weights resident on the GPU."""
 
-    def __init__(self, head: I.Head, device="cuda", markov: bool = False):
+    def __init__(self, head: I.Head, device="cuda", markov: bool = False, exact: bool = False):
         """``markov``: pass no A (the Markov-head variant, A = 0); the kernels
-        then skip the A s_parent contraction."""
+        then skip the A s_parent contraction. ``exact``: set
+        DARTREE_HEAD_EXACT (the general kernel for every shape; needed for a
+        head that head_check flags)."""
         self.A = None if markov else to_device(head.A, device)
         self.E = to_device(head.E, device)
         self.U = to_device(head.U, device)
         self.Pt = to_device(head.Pt, device)
         self.c = C.Head(A=self.A.data_ptr() if self.A is not None else None, E=self.E.data_ptr(),
-                        U=self.U.data_ptr(), Pt=self.Pt.data_ptr() if self.Pt is not None else None)
+                        U=self.U.data_ptr(), Pt=self.Pt.data_ptr() if self.Pt is not None else None,
+                        flags=C.HEAD_EXACT if exact else 0)
+
+
+def head_check(dims: C.Dims, head: DeviceHead, stream=None) -> int:
+    """dartree_head_check: bit 0 when A, bit 1 when U holds entries beyond
+    fp16's range (the block-decoding kernel's precondition). Waits for the
+    result (meant for once per head)."""
+    flags = torch.full((1,), -1, dtype=torch.int32, device=head.E.device)
+    _check(C.load().dartree_head_check(ctypes.byref(dims), ctypes.byref(head.c), _p(flags), _stream(stream)),
+           "head_check")
+    return int(flags.item())
 
 
 def workspace_size(dims: C.Dims) -> int:

@@ -91,13 +91,34 @@ typedef struct {
  * over a node's children is conditioned on that node's token alone). It is the head with A = 0, so a
  * state is tanh(E[u] + h_d), a function of the node's token and depth; the
  * kernels then skip the A s_parent contraction and the scan launch stages no
- * A fragments (dartree_round_plan counts those 16 workgroups regardless). */
+ * A fragments (dartree_round_plan counts those 16 workgroups regardless).
+ *
+ * flags: 0, or DARTREE_HEAD_EXACT. Precondition of the block-decoding tree
+ * kernel (bf16 weights, r = 256, K in {16, 32, 64}, W <= 16; see
+ * dartree_round_plan): it multiplies A and U in fp16, so every entry of A and
+ * U must have magnitude below 2^16 (fp16's range; entries below 2^-17 are
+ * truncated by at most 2^-25). dartree_head_check finds entries beyond it; a
+ * head that has any must carry DARTREE_HEAD_EXACT, which sends every call to
+ * the general kernel (three-part bf16 states, exact products, fp32
+ * accumulation) at its cost. The root state h_0 needs no such care (it is
+ * rescaled by a power of two inside the kernel). */
+#define DARTREE_HEAD_EXACT 1
 typedef struct {
   const void* A;
   const void* E;
   const void* U;
   const void* Pt;
+  int32_t flags;
 } dartree_head;
+
+/* Range check of a bf16 head for the block-decoding kernel (see dartree_head):
+ * enqueues a scan of A (r x r; skipped when NULL) and U (V x r) that writes
+ * *flags (one int32 in device memory) = bit 0 when some entry of A, bit 1
+ * when some entry of U has magnitude >= 2^16 (or is not finite); 0 means the
+ * head meets the precondition. Reads 2 r (V + r) bytes; meant for once per
+ * head, not per round. fp32 heads (weight_dtype DARTREE_F32) always give 0.
+ * Errors as for the other calls. */
+dartree_status dartree_head_check(const dartree_dims* dims, const dartree_head* head, int32_t* flags, void* stream);
 
 /* The supertree: W slots per depth, kept in rank order (slot 0 best).
  *   tok         [n][L][W] int32  token id (pad -1)

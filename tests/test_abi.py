@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dartree_version() == 2
+    assert lib.dartree_version() == 3
     assert C.status_string(0) == "DARTREE_OK"
     assert C.status_string(3) == "DARTREE_ERR_WORKSPACE_TOO_SMALL"
     assert C.status_string(99) == "DARTREE_UNKNOWN_STATUS"
@@ -293,3 +293,11 @@ def test_noalloc_round_rejects_sizes_beyond_its_scratch(lib):
     s = lib.dartree_build_round_noalloc(ctypes.byref(dims(beta=0.5)), ctypes.byref(head), p, p, p, p, p,
                                         ctypes.byref(sup), p, p, p, p, p, p, p, None)
     assert s == C.ERR_INVALID_ARGUMENT
+
+
+def test_unknown_head_flags_are_rejected_before_any_device_call(lib):
+    d = dims()
+    head = C.Head(A=16, E=16, U=16, Pt=16, flags=4)
+    flags = ctypes.c_void_p(16)
+    assert lib.dartree_head_check(ctypes.byref(d), ctypes.byref(head), flags, None) == C.ERR_INVALID_ARGUMENT
+    assert "flags" in C.last_error()

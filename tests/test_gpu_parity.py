@@ -4,6 +4,7 @@ Bar: candidate ids, parents, emission and masks bit-exact; fp32 scores within
 1e-4 absolute of the fp64 oracle; kept sets may differ only at near-ties
 (gap <= 1e-4), which the tie-aware checker replays.
 """
+import copy
 import sys
 
 import numpy as np
@@ -655,3 +656,88 @@ def test_tree_mask_on_handmade_parents():
                     break
                 j = p
         assert np.array_equal(got[q], exp), q
+
+
+# ---- the block-decoding kernel's numeric precondition (fp16 weights) ---------
+def _range_case(seed=4):
+    """A block-decoding shape (bf16 weights, r = 256, K = 64) with the head
+    state supplied directly (D = 0)."""
+    import dataclasses
+    cfg = I.small_variant("qwen3_4b", name="range", n_req=2, V=6000, L=6, K=64, W=12, B=40, r=256, D=0)
+    hd = I.make_head(cfg, seed)
+    rnd = I.make_round(cfg, seed, 0)
+    return cfg, dataclasses.replace(hd, A=hd.A.copy(), E=hd.E.copy(), U=hd.U.copy()), rnd
+
+
+def test_head_check_flags_weights_beyond_fp16():
+    cfg, hd, _ = _range_case()
+    dims = ops.make_dims(cfg)
+    assert ops.head_check(dims, ops.DeviceHead(hd)) == 0
+    assert ops.head_check(dims, ops.DeviceHead(hd, markov=True)) == 0
+    hd.U[5, 7] = I.f32_to_bf16_bits(np.array([70000.0], np.float32))[0]
+    assert ops.head_check(dims, ops.DeviceHead(hd)) == 2
+    hd.A[3, 4] = I.f32_to_bf16_bits(np.array([-1e5], np.float32))[0]
+    assert ops.head_check(dims, ops.DeviceHead(hd)) == 3
+    assert ops.head_check(dims, ops.DeviceHead(hd, markov=True)) == 2
+    # 65280 (the largest bf16 below 2^16) is within fp16's range
+    _, hd2, _ = _range_case()
+    hd2.U[:, 3] = I.f32_to_bf16_bits(np.full(cfg.V, 65280.0, np.float32))
+    assert ops.head_check(dims, ops.DeviceHead(hd2)) == 0
+
+
+def test_head_beyond_fp16_runs_exactly_on_the_general_kernel():
+    """One state column j of U holds 69632 (beyond fp16) for half of the
+    tokens and 59904 (within it) for the other half, and only the root state
+    reaches it (h_0[j] = 1e-3; A[j, :], E[:, j] and h_d[j] zero below the
+    root, so every later state has s[j] = 0): the two halves' depth-1 logits
+    differ by ~0.97, which the fp16 kernel would clamp to ~0.56. head_check
+    flags U, and with DARTREE_HEAD_EXACT the round matches the oracle; the
+    fp16 kernel, whose precondition the head breaks, does not."""
+    cfg, hd, rnd = _range_case()
+    j = 37
+    big = np.random.default_rng(0).random(cfg.V) < 0.5
+    hd.U[:, j] = I.f32_to_bf16_bits(np.where(big, 70000.0, 60000.0).astype(np.float32))
+    hd.A[j, :] = 0
+    hd.E[:, j] = 0
+    h = rnd.h.copy()
+    h[:, 0, j] = 1e-3
+    h[:, 1:, j] = 0.0
+    rnd.h = h
+    dims = ops.make_dims(cfg)
+    dx = ops.DeviceHead(hd, exact=True)
+    assert ops.head_check(dims, dx) == 2
+    say("case head beyond fp16, exact general kernel")
+    out = run_gpu(cfg, hd, dx, rnd)
+    rep = CK.check_round(cfg, hd, rnd, out, tol=TOL)
+    PP.log_case("head beyond fp16 (exact)", rep)
+    say("case head beyond fp16 on the fp16 kernel (precondition broken: must differ)")
+    bad = run_gpu(cfg, hd, ops.DeviceHead(hd), rnd)
+    with pytest.raises(CK.ParityError):
+        CK.check_round(cfg, hd, rnd, bad, tol=TOL)
+
+
+def test_large_root_state_is_rescaled_on_the_fp16_kernel():
+    """h_0[j] = 70000 (beyond fp16) with U[c, j] = 2^-10 u_c, u_c uniform
+    in [0, 1): the root's depth-1 logits get 68 u_c, which a state clamped to
+    fp16's 65504 would turn into 64 u_c (the oracle run with that clamp
+    differs from the true one, so the case can tell). The block-decoding
+    kernel scales the root state by a power of two and must match the
+    oracle."""
+    cfg, hd, rnd = _range_case(5)
+    j = 101
+    u = np.random.default_rng(1).random(cfg.V).astype(np.float32)
+    hd.U[:, j] = I.f32_to_bf16_bits(2.0 ** -10 * u)
+    h = rnd.h.copy()
+    h[:, 0, j] = 70000.0
+    rnd.h = h
+    clamped = copy.deepcopy(rnd)
+    clamped.h[:, 0, j] = 65504.0
+    a = O.round_all(cfg, hd, rnd)[0].levels[1]
+    b = O.round_all(cfg, hd, clamped)[0].levels[1]
+    assert max(abs(x.sbeta - y.sbeta) for x, y in zip(a, b)) > 1e-2
+    dhd = ops.DeviceHead(hd)
+    assert ops.head_check(ops.make_dims(cfg), dhd) == 0
+    say("case large root state on the fp16 kernel")
+    out = run_gpu(cfg, hd, dhd, rnd)
+    rep = CK.check_round(cfg, hd, rnd, out, tol=TOL)
+    PP.log_case("large root state (fp16 kernel)", rep)
