@@ -205,8 +205,10 @@ dartree_status plan_round(const WsLayout& w, bool lbf, uint64_t* lists, int32_t*
   }
   *tp = dartree::tree_plan(ta);
   if (!(tp->ok && tp->mode == 3)) {
+    // the lists go to their own merge launch; plan the tree kernel without them
     ta.lists = nullptr;
     ta.S = 0;
+    *tp = dartree::tree_plan(ta);
   }
   return check_tree_plan(ta, tp);
 }
@@ -287,6 +289,16 @@ dartree_status dartree_workspace_init(const dartree_dims* dims, void* ws, size_t
   WsLayout w;
   TRY(check_ws(dims, ws, ws_bytes, &w));
   (void)stream;   // the current kernels keep no state in the workspace between calls
+  return DARTREE_OK;
+}
+
+dartree_status dartree_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  g_err[0] = 0;
+  REQ_PTR(buf, 16);
+  REQ_PTR(sink, 4);
+  if (bytes == 0 || bytes % 16 != 0) return fail(DARTREE_ERR_INVALID_ARGUMENT, "bytes=%zu: a positive multiple of 16", bytes);
+  hipError_t e = dartree::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream read launch");
   return DARTREE_OK;
 }
 

@@ -117,6 +117,9 @@ LmheadPlan lmhead_plan(int rows, int V, int D, int K);
 hipError_t launch_lmhead_topk(const LmheadPlan& p, const uint16_t* X, const uint16_t* Wlm, int rows, int V, int D,
                               int K, uint64_t* lists, int32_t* cand_ids, float* cand_logit, hipStream_t s);
 
+// measurement utility: one read of bytes (a multiple of 16) at buf
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
+
 // ---- heap-serial construction (the "pop then correct" baseline) -------------
 constexpr int kSerialMaxB = 511;   // pop indices pack into 9 bits of the node key
 struct SerialArgs {

@@ -300,3 +300,10 @@ def set_stage_events(events: Optional[list]):
             e.record()
     arr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(int(e.cuda_event)) for e in events])
     _check(lib.dartree_set_stage_events(arr, 4), "set_stage_events")
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Measurement utility: one read-only pass over buf (dartree_stream_read)."""
+    nbytes = (buf.numel() * buf.element_size()) // 16 * 16
+    _check(C.load().dartree_stream_read(_p(buf), nbytes, _p(sink), _stream(stream)), "stream_read")
+

@@ -347,6 +347,13 @@ dartree_status dartree_verify_tree(const dartree_dims* dims, const int32_t* n_se
                                    const int32_t* target, const float* Q, const float* K, const float* V, int32_t dh,
                                    int32_t* accepted_len, int32_t* accepted_nodes, float* attn_out, void* stream);
 
+/* Measurement utility (not part of a round's computation): one read-only
+ * pass over `bytes` bytes (a positive multiple of 16) at the device pointer
+ * buf (16-byte aligned), 16-byte vector loads, 256 workgroups of 512 threads;
+ * the achievable HBM read rate the logits scan and the LM head are compared
+ * with. sink is a device word the kernel may write (never in practice). */
+dartree_status dartree_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Profiling hook (not part of a round's computation). When set, every
  * following dartree_build_round on this thread records events[0] before its
  * first launch, events[1] after the logits scan (with the head tiles),
