@@ -200,6 +200,23 @@ __device__ __forceinline__ void wave_sort_desc(uint32_t& hi, uint32_t& lo) {
   bitonic_stage<64, 1>(hi, lo);
 }
 
+// Merges a descending 64-key list held one key per lane (hi, lo) with the
+// descending list b (one key per lane) and keeps the 64 largest, descending:
+// the elementwise maximum of one list and the other reversed holds the 64
+// best of both as a bitonic sequence, which six half-cleaner stages sort.
+__device__ __forceinline__ void wave_merge_desc(uint32_t& ah, uint32_t& al, uint64_t b) {
+  const uint32_t bh = lane_rev((uint32_t)(b >> 32)), bl = lane_rev((uint32_t)b);
+  const bool tb = (((uint64_t)bh << 32) | bl) > (((uint64_t)ah << 32) | al);
+  ah = tb ? bh : ah;
+  al = tb ? bl : al;
+  bitonic_stage<64, 32>(ah, al);
+  bitonic_stage<64, 16>(ah, al);
+  bitonic_stage<64, 8>(ah, al);
+  bitonic_stage<64, 4>(ah, al);
+  bitonic_stage<64, 2>(ah, al);
+  bitonic_stage<64, 1>(ah, al);
+}
+
 // Wave reductions; the result is wave-uniform.
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   v = min(v, dpp<kDppXor1>(v));

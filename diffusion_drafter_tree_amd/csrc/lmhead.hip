@@ -196,19 +196,6 @@ __global__ __launch_bounds__(kLT) void lmhead_topk_kernel(LmArgs a) {
 // waves' results meet in LDS, and wave 0 merges those the same way.
 constexpr int kMT = 1024, kMW = kMT / kWave;
 
-__device__ __forceinline__ void merge_into(uint32_t& ah, uint32_t& al, uint64_t b) {
-  const uint32_t bh = lane_rev((uint32_t)(b >> 32)), bl = lane_rev((uint32_t)b);
-  const bool tb = (((uint64_t)bh << 32) | bl) > (((uint64_t)ah << 32) | al);
-  ah = tb ? bh : ah;
-  al = tb ? bl : al;
-  bitonic_stage<64, 32>(ah, al);
-  bitonic_stage<64, 16>(ah, al);
-  bitonic_stage<64, 8>(ah, al);
-  bitonic_stage<64, 4>(ah, al);
-  bitonic_stage<64, 2>(ah, al);
-  bitonic_stage<64, 1>(ah, al);
-}
-
 __global__ __launch_bounds__(kMT) void lmhead_merge_kernel(const uint64_t* __restrict__ lists, int S, int K,
                                                            int32_t* __restrict__ cand_ids,
                                                            float* __restrict__ cand_logit) {
@@ -221,12 +208,12 @@ __global__ __launch_bounds__(kMT) void lmhead_merge_kernel(const uint64_t* __res
     const uint64_t k0 = v ? L[(size_t)w * K + lane] : 0ull;
     ah = (uint32_t)(k0 >> 32);
     al = (uint32_t)k0;
-    for (int sl = w + kMW; sl < S; sl += kMW) merge_into(ah, al, v ? L[(size_t)sl * K + lane] : 0ull);
+    for (int sl = w + kMW; sl < S; sl += kMW) wave_merge_desc(ah, al, v ? L[(size_t)sl * K + lane] : 0ull);
   }
   part[w][lane] = ((uint64_t)ah << 32) | al;
   __syncthreads();
   if (w == 0) {
-    for (int i = 1; i < kMW; ++i) merge_into(ah, al, part[i][lane]);
+    for (int i = 1; i < kMW; ++i) wave_merge_desc(ah, al, part[i][lane]);
     if (v) {
       const bool ok = (ah | al) != 0u;
       cand_ids[(size_t)row * K + lane] = ok ? (int32_t)(0xFFFFFFFFu - al) : -1;

@@ -167,9 +167,9 @@ int32_t dartree_version(void);
  * these dims (bytes). */
 dartree_status dartree_workspace_size(const dartree_dims* dims, size_t* bytes);
 
-/* Prepare a freshly allocated workspace (zeroes its per-row tickets). The
- * kernels leave the tickets at zero when they finish, so this is needed once
- * per allocation, not per round. */
+/* Prepare a workspace for these dims. The current kernels keep no state in
+ * the workspace between calls, so this only validates; calling it once per
+ * allocation keeps callers correct should a future layout need set-up. */
 dartree_status dartree_workspace_init(const dartree_dims* dims, void* ws, size_t ws_bytes, void* stream);
 
 /* Step a0 (synthetic head input; marsggbo section 3.1: one block-parallel
