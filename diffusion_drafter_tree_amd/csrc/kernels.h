@@ -91,6 +91,7 @@ struct TreeArgs {
 struct TreePlan {
   int mode;          // 0 VALU, 1 MFMA general, 2 MFMA resident/prefetched, 3 block-decoding kernel
   int kq;            // k-groups of the score contraction (mode 2)
+  bool planes;       // mode 1: parents' states held as split bf16 planes
   size_t smem;       // dynamic LDS bytes
   bool ok;
 };

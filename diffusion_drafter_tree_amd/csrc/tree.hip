@@ -24,7 +24,10 @@
 // registers (wave w owns rows 16w..16w+15), keeps the parents' split states in
 // LDS, and prefetches the next depth's U fragments (registers), E rows and h
 // row (LDS) while the current depth runs, so the dependent chain never waits
-// on global memory. Mode 1 is the same arithmetic with loads issued per tile.
+// on global memory. Mode 1 is the same arithmetic with loads issued per tile:
+// weight fragments are read with 4-lane groups on one 64-byte segment and
+// permuted to the operand lanes, and the parents' states are kept as split
+// planes when they fit in LDS (else split per fragment from fp32 rows).
 //
 // Emission order (depth, parent's emitted index, token) equals the order of
 // the nodes' token paths, so each level records the lexicographic rank of its
@@ -41,6 +44,7 @@ constexpr int kT = 1024;
 constexpr int kWaves = kT / kWave;
 constexpr int kSelCap = 1024;
 constexpr size_t kMaxSmem = 160 * 1024;
+constexpr int kGB = 8;   // mode 1: weight fragments in flight per tile batch
 
 __device__ __forceinline__ float ldw(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
 __device__ __forceinline__ float ldw(const float* p, size_t i) { return p[i]; }
@@ -54,8 +58,8 @@ __device__ __forceinline__ float ldw(const float* p, size_t i) { return p[i]; }
 struct Lay {
   LDS int* cid;       // mode 2: [L][K]; else [K] (current depth)
   LDS float* clog;
-  LDS float* Sf;      // modes 0/1: [W][r+1] fp32 parent states
-  LDS uint16_t* Sh;   // mode 2: [16][r+8] split parent states
+  LDS float* Sf;      // mode 0, mode 1 without planes: [W][r+1] fp32 parent states
+  LDS uint16_t* Sh;   // mode 2: [16][r+8], mode 1 with planes: [ceil16(W)][r+8] split parent states
   LDS uint16_t* Sm;
   LDS uint16_t* Sl;
   LDS float* Zp;      // [KQ][W][K+4] partial corrected logits; slice 0 then holds cum
@@ -92,7 +96,10 @@ struct LayOff {
 
 __host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-__host__ __device__ inline LayOff lay_off(int L, int K, int W, int B, int r, int mode, int KQ) {
+// pl: mode 1 keeps the parents' states as split planes of ceil16(W) rows
+// (written once per state, read by every tile) instead of fp32 rows split on
+// the fly per fragment.
+__host__ __device__ inline LayOff lay_off(int L, int K, int W, int B, int r, int mode, int KQ, bool pl = false) {
   LayOff o{};
   size_t off = 0;
   auto take = [&](size_t b) {
@@ -105,10 +112,12 @@ __host__ __device__ inline LayOff lay_off(int L, int K, int W, int B, int r, int
   const size_t outn = (size_t)(W > B ? W : B);
   o.cid = take(4 * ncand);
   o.clog = take(4 * ncand);
-  o.sf = mode != 2 ? take(4ul * W * (r + 1)) : 0;
-  o.sh = mode == 2 ? take(2ul * 16 * (r + 8)) : 0;
-  o.sm = mode == 2 ? take(2ul * 16 * (r + 8)) : 0;
-  o.sl = mode == 2 ? take(2ul * 16 * (r + 8)) : 0;
+  const bool planes = mode == 2 || (mode == 1 && pl);
+  const size_t prows = mode == 2 ? 16 : (size_t)(W + 15) / 16 * 16;
+  o.sf = planes ? 0 : take(4ul * W * (r + 1));
+  o.sh = planes ? take(2ul * prows * (r + 8)) : 0;
+  o.sm = planes ? take(2ul * prows * (r + 8)) : 0;
+  o.sl = planes ? take(2ul * prows * (r + 8)) : 0;
   o.zp = take(4ul * KQ * W * (K + 4));
   o.as = take(4ul * W * (r + 1));
   o.cp = take(4ul * W);
@@ -197,7 +206,45 @@ __device__ __forceinline__ void split_frag(const LDS float* src, bool valid, u16
   }
 }
 
+// Coalesced weight fragments. The MFMA operand layout puts 16 different rows
+// on adjacent lanes (lane n + 16c: row n, 16-byte chunk c), so a direct load
+// touches a cache line per lane. Loading instead with lane 4n + c reading
+// chunk c of row n makes each 4-lane group read one 64-byte segment; four
+// ds_bpermute then move each lane's 16 bytes to its operand lane.
+__device__ __forceinline__ int coal_row(int lane) { return lane >> 2; }
+// rows 8..15 take their chunks in the order 2, 3, 0, 1, so that each 32-lane
+// half of a permute reads 32 different source lanes modulo 32 (no LDS bank
+// conflicts); every 4-lane group still reads one 64-byte segment
+__device__ __forceinline__ int coal_col(int lane) { return ((lane & 3) ^ ((lane >> 5) << 1)) * 8; }
+__device__ __forceinline__ u16x8_t to_mfma_lanes(u16x8_t v, int lane) {
+  const int n = lane & 15, c = lane >> 4;
+  const int src = (n * 4 + (c ^ ((n >> 3) << 1))) * 4;   // byte index of the lane that loaded row n, chunk c
+  const u32x4_t x = __builtin_bit_cast(u32x4_t, v);
+  u32x4_t y;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)x[i]);
+  return __builtin_bit_cast(u16x8_t, y);
+}
+
 // ---- mode 1: MFMA with loads issued per tile ---------------------------------
+// The three bf16 fragments of parent row p at columns j0..j0+7: read from the
+// split planes (PL) or split from the fp32 row on the fly.
+template <bool PL>
+__device__ __forceinline__ void state_frag(const Lay& s, int r, int p, bool pv, int j0, u16x8_t& fh, u16x8_t& fm,
+                                           u16x8_t& fl) {
+  if (PL) {
+    const int o = p * (r + 8) + j0;
+    fh = *reinterpret_cast<const LDS u16x8_t*>(s.Sh + o);
+    fm = *reinterpret_cast<const LDS u16x8_t*>(s.Sm + o);
+    fl = *reinterpret_cast<const LDS u16x8_t*>(s.Sl + o);
+  } else {
+    split_frag(s.Sf + (size_t)(pv ? p : 0) * (r + 1) + j0, pv, fh, fm, fl);
+  }
+}
+
+// Weight fragments of one tile are loaded GB k-steps at a time (all loads of
+// a batch in flight together), then consumed in order.
+template <bool PL, int GB>
 __device__ __forceinline__ void z_mfma_general(const Lay& s, const uint16_t* __restrict__ U, int Wp, int K, int r) {
   const int lane = lane_id(), w = threadIdx.x / kWave;
   const int MT = (Wp + 15) / 16, NT = (K + 15) / 16, KS = r / 32;
@@ -207,20 +254,20 @@ __device__ __forceinline__ void z_mfma_general(const Lay& s, const uint16_t* __r
     const int p = mt * 16 + (lane & 15);
     const int k = nt * 16 + (lane & 15);
     const bool pv = p < Wp, kv = k < K;
-    const uint16_t* urow = U + (size_t)(kv ? s.cid[k] : 0) * r + sub;
-    const LDS float* srow = s.Sf + (size_t)(pv ? p : 0) * (r + 1) + sub;
+    // coalesced rows; a candidate column >= K re-reads a valid row and feeds only discarded outputs
+    const uint16_t* urow = U + (size_t)s.cid[min(nt * 16 + coal_row(lane), K - 1)] * r + coal_col(lane);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < KS; k0 += 4) {
-      u16x8_t b[4];
+    for (int k0 = 0; k0 < KS; k0 += GB) {
+      u16x8_t b[GB];
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < GB; ++g)
         if (k0 + g < KS) b[g] = *reinterpret_cast<const u16x8_t*>(urow + (k0 + g) * 32);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < GB; ++g) {
         if (k0 + g < KS) {
-          if (!kv) b[g] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+          b[g] = to_mfma_lanes(b[g], lane);
           u16x8_t fh, fm, fl;
-          split_frag(srow + (k0 + g) * 32, pv, fh, fm, fl);
+          state_frag<PL>(s, r, p, pv, (k0 + g) * 32 + sub, fh, fm, fl);
           acc = mfma_bf16(fl, b[g], acc);
           acc = mfma_bf16(fm, b[g], acc);
           acc = mfma_bf16(fh, b[g], acc);
@@ -235,28 +282,28 @@ __device__ __forceinline__ void z_mfma_general(const Lay& s, const uint16_t* __r
   }
 }
 
+template <bool PL, int GB>
 __device__ __forceinline__ void as_mfma_general(const Lay& s, const uint16_t* __restrict__ A, int Wp, int r) {
   const int lane = lane_id(), w = threadIdx.x / kWave;
   const int MT = r / 16, NT = (Wp + 15) / 16, KS = r / 32;
   const int sub = (lane >> 4) * 8;
   for (int t = w; t < MT * NT; t += kWaves) {
     const int mt = t / NT, nt = t - mt * NT;
-    const int j = mt * 16 + (lane & 15);
     const int p = nt * 16 + (lane & 15);
     const bool pv = p < Wp;
-    const uint16_t* arow = A + (size_t)j * r + sub;
-    const LDS float* srow = s.Sf + (size_t)(pv ? p : 0) * (r + 1) + sub;
+    const uint16_t* arow = A + (size_t)(mt * 16 + coal_row(lane)) * r + coal_col(lane);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < KS; k0 += 4) {
-      u16x8_t av[4];
+    for (int k0 = 0; k0 < KS; k0 += GB) {
+      u16x8_t av[GB];
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < GB; ++g)
         if (k0 + g < KS) av[g] = *reinterpret_cast<const u16x8_t*>(arow + (k0 + g) * 32);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < GB; ++g) {
         if (k0 + g < KS) {
+          av[g] = to_mfma_lanes(av[g], lane);
           u16x8_t fh, fm, fl;
-          split_frag(srow + (k0 + g) * 32, pv, fh, fm, fl);
+          state_frag<PL>(s, r, p, pv, (k0 + g) * 32 + sub, fh, fm, fl);
           acc = mfma_bf16(av[g], fl, acc);
           acc = mfma_bf16(av[g], fm, acc);
           acc = mfma_bf16(av[g], fh, acc);
@@ -310,9 +357,11 @@ __device__ __forceinline__ void level_lex(const Lay& s, int d, int W, int cnt) {
   }
 }
 
-template <typename WT, int MODE, int KSQ, int EPT>
+template <typename WT, int MODE, int KSQ, int EPT, bool PL = false>
 __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
-  const Lay s = make_lay(lay_off(a.L, a.K, a.W, a.B, a.r, MODE, KQ));
+  // split planes hold the parents' states (mode 2 always, mode 1 with PL)
+  constexpr bool kPl = MODE == 2 || (MODE == 1 && PL);
+  const Lay s = make_lay(lay_off(a.L, a.K, a.W, a.B, a.r, MODE, KQ, PL));
   const int q = blockIdx.x, tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int L = a.L, K = a.K, W = a.W, r = a.r, B = a.B;
   // this request's width and budget (per-request values clamped to [1, W], [1, B])
@@ -352,10 +401,16 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
     }
   }
   int Wp = 1;
+  if (MODE == 1 && PL && expand) {
+    // padding rows of the planes feed only discarded outputs; clear them anyway
+    const int n = (W + 15) / 16 * 16 * (r + 8);
+    for (int i = tid; i < n; i += kT) s.Sh[i] = s.Sm[i] = s.Sl[i] = 0;
+    __syncthreads();
+  }
   if (expand) {
     if (a.d0 == 1) {
       for (int j = tid; j < r; j += kT) {
-        if (MODE == 2) split_store(s, r, 0, j, hq[j]);
+        if (kPl) split_store(s, r, 0, j, hq[j]);
         else s.Sf[j] = hq[j];
       }
       if (tid == 0) s.cumP[0] = 0.f;
@@ -363,7 +418,7 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
       Wp = min(max(a.st_count[(size_t)q * L + a.d0 - 2], 1), W);
       const float* st = a.st_state + (size_t)q * W * r;
       for (int i = tid; i < Wp * r; i += kT) {
-        if (MODE == 2) split_store(s, r, i / r, i % r, st[i]);
+        if (kPl) split_store(s, r, i / r, i % r, st[i]);
         else s.Sf[(i / r) * (r + 1) + i % r] = st[i];
       }
       for (int i = tid; i < Wp; i += kT) s.cumP[i] = a.st_cum[lw + (size_t)(a.d0 - 2) * W + i];
@@ -417,6 +472,13 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
     if (a.d0 < L) load_e(a.d0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the LDS-direct loads have landed
   }
+  // modes 0/1: candidates of the first depth (later depths are loaded one depth ahead)
+  int c_nx = 0;
+  float l_nx = 0.f;
+  if (MODE != 2 && expand && tid < K) {
+    c_nx = cid_g[(size_t)(a.d0 - 1) * K + tid];
+    l_nx = clog_g[(size_t)(a.d0 - 1) * K + tid];
+  }
   __syncthreads();
 
   for (int d = a.d0; d <= a.d1; ++d) {
@@ -424,10 +486,14 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
     const LDS int* cidd = MODE == 2 ? s.cid + (size_t)(d - 1) * K : s.cid;
     const LDS float* clogd = MODE == 2 ? s.clog + (size_t)(d - 1) * K : s.clog;
     if (MODE != 2) {
-      for (int k = tid; k < K; k += kT) {
-        const int c = cid_g[(size_t)(d - 1) * K + k];
-        s.cid[k] = (c < 0 || c >= a.V) ? 0 : c;
-        s.clog[k] = clog_g[(size_t)(d - 1) * K + k];
+      // this depth's candidates came in during the previous depth (K <= kT)
+      if (tid < K) {
+        s.cid[tid] = (c_nx < 0 || c_nx >= a.V) ? 0 : c_nx;
+        s.clog[tid] = l_nx;
+        if (d < a.d1) {
+          c_nx = cid_g[(size_t)d * K + tid];
+          l_nx = clog_g[(size_t)d * K + tid];
+        }
       }
       __syncthreads();
     }
@@ -476,8 +542,8 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
         if (d + 1 < L) load_e(d + 1);
       }
     } else if (MODE == 1) {
-      z_mfma_general(s, reinterpret_cast<const uint16_t*>(U), Wp, K, r);
-      if (need_state && !markov) as_mfma_general(s, reinterpret_cast<const uint16_t*>(A), Wp, r);
+      z_mfma_general<PL, kGB>(s, reinterpret_cast<const uint16_t*>(U), Wp, K, r);
+      if (need_state && !markov) as_mfma_general<PL, kGB>(s, reinterpret_cast<const uint16_t*>(A), Wp, r);
     } else {
       z_valu<WT>(s, U, Wp, K, r);
       if (need_state && !markov) as_valu<WT>(s, A, Wp, r);
@@ -556,6 +622,26 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
     if (ns > kSelCap) ns = select_exact<EPT>(keys, pays, Wq, sel);
     const int nk = select_rank(ns, Wq, sel);
 
+    // mode 1: thread tid owns entries 8j..8j+7 of survivor sl's new state (W r
+    // <= 8192 makes one vector per thread enough); its E row and h row loads go
+    // out now and land while the new level is written
+    const int r8 = r / 8;
+    const bool sv = MODE == 1 && need_state && tid < nk * r8;
+    int sv_sl = 0, sv_j0 = 0, sv_ps = 0;
+    u16x8_t ev8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    float hv8[8];
+    if (MODE == 1 && sv) {
+      sv_sl = tid / r8;
+      sv_j0 = (tid - sv_sl * r8) * 8;
+      const int i = s.opay[sv_sl];
+      sv_ps = i / K;
+      const int tok = cidd[i - sv_ps * K];
+      ev8 = *reinterpret_cast<const u16x8_t*>(reinterpret_cast<const uint16_t*>(E) + (size_t)tok * r + sv_j0);
+      const float* hd = hq + (size_t)d * r + sv_j0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv8[e] = hd[e];
+    }
+
     // ---- the new level --------------------------------------------------------
     const size_t orow = lw + (size_t)(d - 1) * W;
     for (int sl = tid; sl < W; sl += kT) {
@@ -593,7 +679,35 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
       const float* hd = hq + (size_t)d * r;
       float* st_out = a.st_state + (size_t)q * W * r;
       const int row0 = (d - 1) * W;
-      for (int i = tid; i < nk * r; i += kT) {
+      if (MODE == 1 && sv) {
+        float v8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          v8[e] = tanhf(((markov ? 0.f : s.AS[(size_t)sv_ps * (r + 1) + sv_j0 + e]) + bf16_to_f32(ev8[e])) + hv8[e]);
+        if (kPl) {
+          u16x8_t fh, fm, fl;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            uint32_t h, m, l;
+            split3(v8[e], h, m, l);
+            fh[e] = (unsigned short)h;
+            fm[e] = (unsigned short)m;
+            fl[e] = (unsigned short)l;
+          }
+          const int o = sv_sl * (r + 8) + sv_j0;
+          *reinterpret_cast<LDS u16x8_t*>(s.Sh + o) = fh;
+          *reinterpret_cast<LDS u16x8_t*>(s.Sm + o) = fm;
+          *reinterpret_cast<LDS u16x8_t*>(s.Sl + o) = fl;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s.Sf[sv_sl * (r + 1) + sv_j0 + e] = v8[e];
+        }
+        if (d == a.d1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) st_out[(size_t)sv_sl * r + sv_j0 + e] = v8[e];
+        }
+      }
+      for (int i = tid; MODE != 1 && i < nk * r; i += kT) {
         const int sl = i / r, j = i - sl * r;
         const int ps = s.lv_ps[row0 + sl];
         float ev, hv;
@@ -605,7 +719,7 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
           hv = hd[j];
         }
         const float v = tanhf(((markov ? 0.f : s.AS[(size_t)ps * (r + 1) + j]) + ev) + hv);
-        if (MODE == 2) split_store(s, r, sl, j, v);
+        if (kPl) split_store(s, r, sl, j, v);
         else s.Sf[sl * (r + 1) + j] = v;
         if (d == a.d1) st_out[i] = v;
       }
@@ -802,7 +916,8 @@ TreePlan tree_plan(const TreeArgs& a) {
   }
   p.mode = mode;
   p.kq = KQ;
-  p.smem = lay_off(a.L, a.K, a.W, a.B, a.r, mode, KQ).total;
+  p.planes = mode == 1 && lay_off(a.L, a.K, a.W, a.B, a.r, 1, KQ, true).total <= kMaxSmem;
+  p.smem = lay_off(a.L, a.K, a.W, a.B, a.r, mode, KQ, p.planes).total;
   p.ok = p.smem <= kMaxSmem;
   return p;
 }
@@ -811,12 +926,12 @@ hipError_t launch_tree(const TreePlan& p, const TreeArgs& a, hipStream_t s) {
   if (p.mode == 3) return launch_tree_fast(p, a, s);
   dim3 grid(a.n_req), block(kT);
   hipError_t e = hipSuccess;
-#define DT_TREE(T, M, KS, EP)                                                                              \
+#define DT_TREE(T, M, KS, ...)                                                                             \
   do {                                                                                                     \
-    e = hipFuncSetAttribute((const void*)tree_kernel<T, M, KS, EP>,                                        \
+    e = hipFuncSetAttribute((const void*)tree_kernel<T, M, KS, __VA_ARGS__>,                               \
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.smem);                      \
     if (e != hipSuccess) return e;                                                                         \
-    hipLaunchKernelGGL((tree_kernel<T, M, KS, EP>), grid, block, p.smem, s, a, p.kq);                      \
+    hipLaunchKernelGGL((tree_kernel<T, M, KS, __VA_ARGS__>), grid, block, p.smem, s, a, p.kq);             \
   } while (0)
   if (p.mode == 2) {
     const int ksq = 8 / p.kq;
@@ -825,7 +940,11 @@ hipError_t launch_tree(const TreePlan& p, const TreeArgs& a, hipStream_t s) {
   } else {
     // keys per thread: parents per wave times 64-lane groups of candidates
     const int ept = ((a.W + kWaves - 1) / kWaves) * ((a.K + kWave - 1) / kWave);
-    if (p.mode == 1) {
+    if (p.mode == 1 && p.planes) {
+      if (ept <= 4) DT_TREE(uint16_t, 1, 1, 4, true);
+      else if (ept <= 8) DT_TREE(uint16_t, 1, 1, 8, true);
+      else DT_TREE(uint16_t, 1, 1, 16, true);
+    } else if (p.mode == 1) {
       if (ept <= 4) DT_TREE(uint16_t, 1, 1, 4);
       else if (ept <= 8) DT_TREE(uint16_t, 1, 1, 8);
       else DT_TREE(uint16_t, 1, 1, 16);
