@@ -39,7 +39,8 @@ class Head(ctypes.Structure):
 
 class RoundInfo(ctypes.Structure):
     _fields_ = [("n_launches", c_int32), ("scan_slices", c_int32), ("scan_workgroups", c_int32),
-                ("merge_separate", c_int32), ("tree_kernel", c_int32), ("tree_lds_bytes", c_int32)]
+                ("merge_separate", c_int32), ("tree_kernel", c_int32), ("tree_lds_bytes", c_int32),
+                ("tree_parts", c_int32)]
 
 
 class Supertree(ctypes.Structure):
@@ -77,6 +78,7 @@ SIGNATURES = {
     "dartree_lmhead_topk": (c_int32, [PD, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "dartree_stream_read": (c_int32, [c_void_p, c_size_t, c_void_p, c_void_p]),
     "dartree_set_stage_events": (c_int32, [POINTER(c_void_p), c_int32]),
+    "dartree_set_split_wait": (c_int32, [c_int32]),
     "dartree_serial_workspace_size": (c_int32, [PD, POINTER(c_size_t)]),
     "dartree_verify_tree": (c_int32, [PD, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),

@@ -2,6 +2,7 @@
 // dispatch. Every entry point validates completely before it enqueues.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -16,6 +17,8 @@ namespace {
 thread_local char g_err[512] = "";
 thread_local hipEvent_t g_stage_ev[4] = {nullptr, nullptr, nullptr, nullptr};
 thread_local bool g_stage_on = false;
+// bound of the split tree kernel's wait for another part's slice (microseconds)
+std::atomic<uint32_t> g_split_wait_us{200};
 
 void stage_mark(int i, hipStream_t s) {
   if (g_stage_on) (void)hipEventRecord(g_stage_ev[i], s);
@@ -70,9 +73,21 @@ dartree_status check_dims(const dartree_dims* d) {
 struct WsLayout {
   dartree::ScanPlan plan;
   size_t lists_off, afrag_off, total;   // afrag_off = 0: no A fragment copy
+  int split;                            // general kernel: workgroups per request
+  size_t xch_off, xflag_off;            // its exchange slices and flags (split > 1)
 };
 
-WsLayout ws_layout(const dartree_dims* d) {
+// The general MFMA tree kernel (bf16 weights, r % 32 == 0, outside the
+// block-decoding shapes) spreads a request over up to 4 workgroups while
+// n_req * parts stays within the 256 compute units of an MI355X.
+int split_parts(const dartree_dims* d) {
+  if (d->weight_dtype != DARTREE_BF16 || d->r % 32 != 0) return 1;
+  if (d->r == 256 && (d->K == 16 || d->K == 32 || d->K == 64) && d->W <= 16) return 1;
+  const int per = 256 / d->n_req;
+  return per >= 4 ? 4 : per >= 2 ? 2 : 1;
+}
+
+WsLayout ws_layout(const dartree_dims* d, bool allow_split = true) {
   WsLayout w{};
   const int rows = d->n_req * d->L;
   w.plan = dartree::scan_plan(rows, d->V, d->K, d->logits_dtype == DARTREE_BF16);
@@ -86,11 +101,19 @@ WsLayout ws_layout(const dartree_dims* d) {
     w.total += dartree::kAFragBytes;
   }
   if (w.total == 0) w.total = 256;
+  w.split = allow_split ? split_parts(d) : 1;
+  if (w.split > 1) {
+    w.xch_off = w.total;
+    const size_t row = (size_t)(d->K + 15) / 16 * 16 + d->r;   // Z blocks, then AS
+    w.total += ((size_t)d->n_req * d->L * d->W * row * sizeof(float) + 255) & ~(size_t)255;
+    w.xflag_off = w.total;
+    w.total += ((size_t)d->n_req * w.split * d->L * sizeof(uint32_t) + 255) & ~(size_t)255;
+  }
   return w;
 }
 
-dartree_status check_ws(const dartree_dims* d, void* ws, size_t ws_bytes, WsLayout* out) {
-  *out = ws_layout(d);
+dartree_status check_ws(const dartree_dims* d, void* ws, size_t ws_bytes, WsLayout* out, bool allow_split = true) {
+  *out = ws_layout(d, allow_split);
   if (!out->plan.ok) return fail(DARTREE_ERR_UNSUPPORTED, "no top-K plan for V=%d K=%d", d->V, d->K);
   REQ_PTR(ws, 256);
   if (ws_bytes < out->total)
@@ -167,6 +190,7 @@ dartree::TreeArgs tree_args(const dartree_dims* dims, const dartree_head* head, 
   a.b_req = st->budget;
   a.d0 = d0;
   a.d1 = d1;
+  a.split = 1;
   return a;
 }
 
@@ -230,7 +254,7 @@ const char* dartree_status_string(dartree_status s) {
 
 const char* dartree_last_error(void) { return g_err; }
 
-int32_t dartree_version(void) { return 3; }
+int32_t dartree_version(void) { return 4; }
 
 dartree_status dartree_round_plan(const dartree_dims* dims, dartree_round_info* info) {
   g_err[0] = 0;
@@ -241,6 +265,11 @@ dartree_status dartree_round_plan(const dartree_dims* dims, dartree_round_info* 
   dartree_supertree st{};
   dartree::TreeArgs ta = tree_args(dims, nullptr, nullptr, nullptr, nullptr, &st, 1, dims->L);
   set_tree_out(ta, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, reinterpret_cast<uint64_t*>(256));
+  if (w.split > 1) {
+    ta.split = w.split;
+    ta.xch = reinterpret_cast<float*>(256);
+    ta.xflag = reinterpret_cast<uint32_t*>(256);
+  }
   dartree::TreePlan tp;
   alignas(16) static uint64_t dummy_lists[2];
   TRY(plan_round(w, dims->logits_dtype == DARTREE_BF16, dummy_lists, nullptr, nullptr, ta, &tp));
@@ -256,6 +285,7 @@ dartree_status dartree_round_plan(const dartree_dims* dims, dartree_round_info* 
                           ((tp.mode == 3 && w.afrag_off) ? dartree::kAFragWaves : 0);
   info->tree_kernel = tp.mode == 3 ? 1 : 0;
   info->tree_lds_bytes = (int32_t)tp.smem;
+  info->tree_parts = tp.mode == 1 ? tp.split : 1;
   return DARTREE_OK;
 }
 
@@ -270,6 +300,14 @@ dartree_status dartree_set_stage_events(void* const* events, int32_t n) {
     if (!events[i]) return fail(DARTREE_ERR_INVALID_ARGUMENT, "stage event %d is NULL", i);
   for (int i = 0; i < 4; ++i) g_stage_ev[i] = static_cast<hipEvent_t>(events[i]);
   g_stage_on = true;
+  return DARTREE_OK;
+}
+
+dartree_status dartree_set_split_wait(int32_t microseconds) {
+  g_err[0] = 0;
+  if (microseconds < 0 || microseconds > 1000000)
+    return fail(DARTREE_ERR_INVALID_ARGUMENT, "split wait of %d us: 0 .. 1000000", microseconds);
+  g_split_wait_us.store((uint32_t)microseconds);
   return DARTREE_OK;
 }
 
@@ -471,7 +509,9 @@ namespace dartree {
 
 dartree_status set_error(dartree_status s, const char* msg) { return fail(s, "%s", msg); }
 
-size_t round_workspace_bytes(const dartree_dims* dims) { return ws_layout(dims).total; }
+size_t round_workspace_bytes(const dartree_dims* dims, bool allow_split) {
+  return ws_layout(dims, allow_split).total;
+}
 
 dartree_status check_round_dims(const dartree_dims* dims) {
   TRY(check_dims(dims));
@@ -483,7 +523,7 @@ dartree_status build_round_impl(const dartree_dims* dims, const dartree_head* he
                                 const void* H_or_h, int32_t* cand_ids, float* cand_logit, float* h,
                                 dartree_supertree* st, int32_t* n_sel, int32_t* tok, int32_t* depth,
                                 int32_t* parent, float* score, int32_t* slot, uint64_t* mask, void* ws,
-                                size_t ws_bytes, void* stream) {
+                                size_t ws_bytes, void* stream, bool allow_split) {
   TRY(check_dims(dims));
   TRY(check_head(dims, head));
   REQ_PTR(logits, 16);
@@ -500,13 +540,19 @@ dartree_status build_round_impl(const dartree_dims* dims, const dartree_head* he
   TRY(check_tree_out(n_sel, tok, depth, parent, score, slot));
   REQ_PTR(mask, 8);
   WsLayout w;
-  TRY(check_ws(dims, ws, ws_bytes, &w));
+  TRY(check_ws(dims, ws, ws_bytes, &w, allow_split));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool lbf = dims->logits_dtype == DARTREE_BF16, wbf = dims->weight_dtype == DARTREE_BF16;
   const int rows = dims->n_req * dims->L;
   const float* hin = static_cast<const float*>(H_or_h);
   dartree::TreeArgs ta = tree_args(dims, head, cand_ids, cand_logit, dims->D > 0 ? h : hin, st, 1, dims->L);
   set_tree_out(ta, n_sel, tok, depth, parent, score, slot, mask);
+  if (w.split > 1) {
+    ta.split = w.split;
+    ta.xch = reinterpret_cast<float*>(static_cast<char*>(ws) + w.xch_off);
+    ta.xflag = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + w.xflag_off);
+    ta.split_wait = g_split_wait_us.load() * 100u;
+  }
   uint64_t* lists = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + w.lists_off);
   dartree::TreePlan tp;
   TRY(plan_round(w, lbf, lists, cand_ids, cand_logit, ta, &tp));
@@ -528,6 +574,11 @@ dartree_status build_round_impl(const dartree_dims* dims, const dartree_head* he
   }
   sa.cand_ids = cand_ids;
   sa.cand_logit = cand_logit;
+  if (tp.mode == 1 && tp.split > 1) {
+    // the split tree kernel's flags start at zero
+    sa.clear = ta.xflag;
+    sa.n_clear = dims->n_req * tp.split * dims->L;
+  }
   const bool fuse_head = dims->D > 0 && dartree::head_mfma_ok(wbf, H_or_h, head->Pt, dims->D, dims->r);
   if (fuse_head) {
     sa.H = static_cast<const uint16_t*>(H_or_h);

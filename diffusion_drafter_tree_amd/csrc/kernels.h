@@ -26,6 +26,9 @@ struct ScanArgs {
   const uint16_t* A;
   uint16_t* a_frag;
   int n_afrag;
+  // words zeroed by the launch (the split tree kernel's flags), 0 for none
+  uint32_t* clear;
+  int n_clear;
 };
 constexpr int kAFragWaves = 16;                        // tree waves holding A fragments
 constexpr size_t kAFragBytes = (size_t)256 * 256 * 2;  // one fp16 copy of A
@@ -87,11 +90,19 @@ struct TreeArgs {
   float* score;               // [n][B]
   int32_t* slot;              // [n][B]
   uint64_t* mask;             // [n][B][ceil(B/64)]
+  // general MFMA kernel only: a request over `split` workgroups (1: one),
+  // exchanging contraction slices through xch [n][L][W][ceil16(K) + r] and the
+  // per-depth flags xflag [n][split][L] (zero at launch)
+  int split;
+  float* xch;
+  uint32_t* xflag;
+  uint32_t split_wait;        // longest wait for another part's slice, in 10 ns ticks
 };
 struct TreePlan {
   int mode;          // 0 VALU, 1 MFMA general, 2 MFMA resident/prefetched, 3 block-decoding kernel
   int kq;            // k-groups of the score contraction (mode 2)
   bool planes;       // mode 1: parents' states held as split bf16 planes
+  int split;         // mode 1: workgroups per request
   size_t smem;       // dynamic LDS bytes
   bool ok;
 };

@@ -65,7 +65,9 @@ extern "C" dartree_status dartree_build_round_noalloc(const dartree_dims* dims, 
   dartree::set_error(DARTREE_OK, "");
   dartree_status s = dartree::check_round_dims(dims);
   if (s != DARTREE_OK) return s;
-  const size_t need = dartree::round_workspace_bytes(dims);
+  // the split tree kernel's exchange area when it fits, else one workgroup a request
+  const bool split = dartree::round_workspace_bytes(dims, true) <= kNoAllocScratchBytes;
+  const size_t need = dartree::round_workspace_bytes(dims, split);
   if (need > kNoAllocScratchBytes) {
     char msg[256];
     snprintf(msg, sizeof(msg),
@@ -78,5 +80,5 @@ extern "C" dartree_status dartree_build_round_noalloc(const dartree_dims* dims, 
   s = scratch_for_current_device(&ws);
   if (s != DARTREE_OK) return s;
   return dartree::build_round_impl(dims, head, logits, H_or_h, cand_ids, cand_logit, h, st, n_sel, tok, depth, parent,
-                                   score, slot, mask, ws, kNoAllocScratchBytes, stream);
+                                   score, slot, mask, ws, kNoAllocScratchBytes, stream, split);
 }

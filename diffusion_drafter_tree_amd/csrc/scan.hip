@@ -768,10 +768,15 @@ __device__ void head_block_big(const ScanArgs& a, HeadBigSmem& sm, int tile) {
   }
 }
 
+__device__ __forceinline__ void clear_words(const ScanArgs& a) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n_clear; i += gridDim.x * blockDim.x) a.clear[i] = 0u;
+}
+
 template <bool BF16, int NV>
 __global__ __launch_bounds__(kT) void scan_kernel(ScanArgs a) {
   __shared__ KernelSmem smem;
   const int b = blockIdx.x;
+  clear_words(a);
   if (b < a.n_scan) {
     if (threadIdx.x < 8) smem.scan.misc[threadIdx.x] = 0;
     if (BF16)
@@ -797,6 +802,7 @@ template <bool BF16, int NV>
 __global__ __launch_bounds__(kWideT) __attribute__((amdgpu_waves_per_eu(8))) void scan_wide_kernel(ScanArgs a) {
   __shared__ WideKernelSmem<kWideT> smem;
   const int b = blockIdx.x;
+  clear_words(a);
   const int mixed = a.n_scan + a.n_head;
   if (b < mixed) {
     const int f1 = (int)(((long long)(b + 1) * a.n_head) / mixed);

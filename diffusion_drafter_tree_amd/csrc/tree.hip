@@ -244,13 +244,16 @@ __device__ __forceinline__ void state_frag(const Lay& s, int r, int p, bool pv, 
 
 // Weight fragments of one tile are loaded GB k-steps at a time (all loads of
 // a batch in flight together), then consumed in order.
+// Z tiles of candidate blocks n0..n1-1 (16 candidates each); AS tiles of
+// A-row blocks m0..m1-1. Tile t goes to wave (t + wofs) mod 16.
 template <bool PL, int GB>
-__device__ __forceinline__ void z_mfma_general(const Lay& s, const uint16_t* __restrict__ U, int Wp, int K, int r) {
+__device__ __forceinline__ void z_mfma_general(const Lay& s, const uint16_t* __restrict__ U, int Wp, int K, int r,
+                                               int n0, int n1, int wofs) {
   const int lane = lane_id(), w = threadIdx.x / kWave;
-  const int MT = (Wp + 15) / 16, NT = (K + 15) / 16, KS = r / 32;
+  const int MT = (Wp + 15) / 16, NT = n1 - n0, KS = r / 32;
   const int sub = (lane >> 4) * 8;
-  for (int t = w; t < MT * NT; t += kWaves) {
-    const int mt = t / NT, nt = t - mt * NT;
+  for (int t = (w + kWaves - wofs) % kWaves; t < MT * NT; t += kWaves) {
+    const int mt = t / NT, nt = n0 + t % NT;
     const int p = mt * 16 + (lane & 15);
     const int k = nt * 16 + (lane & 15);
     const bool pv = p < Wp, kv = k < K;
@@ -283,12 +286,13 @@ __device__ __forceinline__ void z_mfma_general(const Lay& s, const uint16_t* __r
 }
 
 template <bool PL, int GB>
-__device__ __forceinline__ void as_mfma_general(const Lay& s, const uint16_t* __restrict__ A, int Wp, int r) {
+__device__ __forceinline__ void as_mfma_general(const Lay& s, const uint16_t* __restrict__ A, int Wp, int r, int m0,
+                                                int m1, int wofs) {
   const int lane = lane_id(), w = threadIdx.x / kWave;
-  const int MT = r / 16, NT = (Wp + 15) / 16, KS = r / 32;
+  const int MT = m1 - m0, NT = (Wp + 15) / 16, KS = r / 32;
   const int sub = (lane >> 4) * 8;
-  for (int t = w; t < MT * NT; t += kWaves) {
-    const int mt = t / NT, nt = t - mt * NT;
+  for (int t = (w + kWaves - wofs) % kWaves; t < MT * NT; t += kWaves) {
+    const int mt = m0 + t / NT, nt = t % NT;
     const int p = nt * 16 + (lane & 15);
     const bool pv = p < Wp;
     const uint16_t* arow = A + (size_t)(mt * 16 + coal_row(lane)) * r + coal_col(lane);
@@ -362,7 +366,13 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
   // split planes hold the parents' states (mode 2 always, mode 1 with PL)
   constexpr bool kPl = MODE == 2 || (MODE == 1 && PL);
   const Lay s = make_lay(lay_off(a.L, a.K, a.W, a.B, a.r, MODE, KQ, PL));
-  const int q = blockIdx.x, tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  // mode 1 may split a request over a.split workgroups (parts): part p
+  // computes its share of the contraction tiles and publishes it; every part
+  // then runs the same selection and state update; part 0 writes the outputs
+  const int nsplit = MODE == 1 ? a.split : 1;
+  const int q = blockIdx.x / nsplit, part = blockIdx.x % nsplit;
+  const bool lead = part == 0;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int L = a.L, K = a.K, W = a.W, r = a.r, B = a.B;
   // this request's width and budget (per-request values clamped to [1, W], [1, B])
   const int Wq = a.w_req ? min(max(a.w_req[q], 1), W) : W;
@@ -542,8 +552,134 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
         if (d + 1 < L) load_e(d + 1);
       }
     } else if (MODE == 1) {
-      z_mfma_general<PL, kGB>(s, reinterpret_cast<const uint16_t*>(U), Wp, K, r);
-      if (need_state && !markov) as_mfma_general<PL, kGB>(s, reinterpret_cast<const uint16_t*>(A), Wp, r);
+      const uint16_t* U16 = reinterpret_cast<const uint16_t*>(U);
+      const uint16_t* A16 = reinterpret_cast<const uint16_t*>(A);
+      const bool with_as = need_state && !markov;
+      const int NZ = (K + 15) / 16, NA = r / 16;
+      auto z_of = [&](int pt, int& n0, int& n1) {
+        n0 = NZ * pt / nsplit;
+        n1 = NZ * (pt + 1) / nsplit;
+      };
+      auto a_of = [&](int pt, int& m0, int& m1) {
+        m0 = NA * pt / nsplit;
+        m1 = NA * (pt + 1) / nsplit;
+      };
+      // a part's tiles: Z on waves 0.., then AS on the following waves
+      auto contract = [&](int pt) {
+        int n0, n1, m0, m1;
+        z_of(pt, n0, n1);
+        a_of(pt, m0, m1);
+        z_mfma_general<PL, kGB>(s, U16, Wp, K, r, n0, n1, 0);
+        if (with_as) as_mfma_general<PL, kGB>(s, A16, Wp, r, m0, m1, ((Wp + 15) / 16 * (n1 - n0)) % kWaves);
+      };
+      contract(part);
+      if (nsplit > 1) {
+        // Publish this part's Z and AS columns, then raise its flag. An
+        // exchange row holds the Z columns in 16-column blocks (NZ * 16,
+        // columns >= K unused) and then the r AS columns; rows of a (request,
+        // depth) are consecutive. Slices move as 16-byte buffer accesses with
+        // the sc1 policy (coherent across the XCDs' L2 caches, as the agent-
+        // scope atomics are); the flag goes up once every wave's stores have
+        // completed.
+        __syncthreads();
+        const int XS = NZ * 16 + r;
+        float* xd = a.xch + ((size_t)q * L + d - 1) * W * XS;
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(xd, 0, W * XS * 4, 0x00020000);
+        int n0, n1, m0, m1;
+        z_of(part, n0, n1);
+        a_of(part, m0, m1);
+        {
+          const int nz4 = (n1 - n0) * 4, na4 = with_as ? (m1 - m0) * 4 : 0, nv = nz4 + na4;
+          for (int i = tid; i < Wp * nv; i += kT) {
+            const int p = i / nv, c = i - p * nv;
+            const int col = c < nz4 ? n0 * 16 + 4 * c : NZ * 16 + m0 * 16 + 4 * (c - nz4);
+            f32x4_t v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              v[e] = c < nz4 ? (col + e < K ? s.Zp[p * (K + 4) + col + e] : 0.f) : s.AS[p * (r + 1) + col - NZ * 16 + e];
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), xr, (p * XS + col) * 4, 0, 16);
+          }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        uint32_t* fl = a.xflag + (size_t)q * nsplit * L;
+        if (tid == 0) __hip_atomic_store(fl + (size_t)part * L + d - 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the other parts' flags, each waited for at most a.split_wait ticks of
+        // the 100 MHz wall clock; a part that has not published (not resident,
+        // or preempted) is computed here, and not waited for again in this launch
+        if (tid < nsplit && tid != part) {
+          int ok = 0;
+          if (!((s.misc[11] >> tid) & 1)) {
+            const uint32_t* f = fl + (size_t)tid * L + d - 1;
+            const uint64_t t0 = wall_clock64();
+            while (true) {
+              if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+                ok = 1;
+                break;
+              }
+              if (wall_clock64() - t0 >= (uint64_t)a.split_wait) break;
+              __builtin_amdgcn_s_sleep(2);
+            }
+            if (!ok) lds_or(&s.misc[11], 1 << tid);
+          }
+          s.misc[12 + tid] = ok;
+        }
+        asm volatile("" ::: "memory");
+        __syncthreads();
+        // the published slices of the other parts: at most 3 vectors a thread
+        // (W (K + r) <= 16384), all loads issued before the LDS writes; an
+        // index past the end re-reads the last vector
+        int beg[5], c0[4], nz4[4], nv[4];
+        int total = 0;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          beg[pt] = total;
+          c0[pt] = nz4[pt] = nv[pt] = 0;
+          if (pt < nsplit && pt != part && s.misc[12 + pt]) {
+            z_of(pt, n0, n1);
+            a_of(pt, m0, m1);
+            nz4[pt] = (n1 - n0) * 4;
+            nv[pt] = nz4[pt] + (with_as ? (m1 - m0) * 4 : 0);
+            c0[pt] = (n0 << 16) | (m0 * 16);   // first Z block, first AS column
+            total += Wp * nv[pt];
+          }
+        }
+        beg[4] = total;
+        auto item = [&](int i, int& p, int& col) {
+          const int pt = i < beg[1] ? 0 : i < beg[2] ? 1 : i < beg[3] ? 2 : 3;
+          const int j = i - beg[pt];
+          p = j / nv[pt];
+          const int c = j - p * nv[pt];
+          col = c < nz4[pt] ? (c0[pt] >> 16) * 16 + 4 * c : NZ * 16 + (c0[pt] & 0xFFFF) + 4 * (c - nz4[pt]);
+        };
+        if (total > 0) {
+          constexpr int kG = 3;
+          f32x4_t gv[kG];
+#pragma unroll
+          for (int u = 0; u < kG; ++u) {
+            int p, col;
+            item(min(tid + u * kT, total - 1), p, col);
+            gv[u] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, (p * XS + col) * 4, 0, 16));
+          }
+#pragma unroll
+          for (int u = 0; u < kG; ++u) {
+            if (tid + u * kT < total) {
+              int p, col;
+              item(tid + u * kT, p, col);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (col < NZ * 16) {
+                  if (col + e < K) s.Zp[p * (K + 4) + col + e] = gv[u][e];
+                } else {
+                  s.AS[p * (r + 1) + col - NZ * 16 + e] = gv[u][e];
+                }
+              }
+            }
+          }
+        }
+        for (int pt = 0; pt < nsplit; ++pt)
+          if (pt != part && !s.misc[12 + pt]) contract(pt);
+      }
     } else {
       z_valu<WT>(s, U, Wp, K, r);
       if (need_state && !markov) as_valu<WT>(s, A, Wp, r);
@@ -656,11 +792,13 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
         s.lv_k[row] = k;
         s.lv_cum[row] = cum;
         s.lv_sb[row] = sb;
-        a.st_tok[orow + sl] = cidd[k];
-        a.st_parent[orow + sl] = d == 1 ? 0 : p;
-        a.st_cum[orow + sl] = cum;
-        a.st_sbeta[orow + sl] = sb;
-      } else {
+        if (lead) {
+          a.st_tok[orow + sl] = cidd[k];
+          a.st_parent[orow + sl] = d == 1 ? 0 : p;
+          a.st_cum[orow + sl] = cum;
+          a.st_sbeta[orow + sl] = sb;
+        }
+      } else if (lead) {
         a.st_tok[orow + sl] = -1;
         a.st_parent[orow + sl] = -1;
         a.st_cum[orow + sl] = -__builtin_huge_valf();
@@ -669,7 +807,7 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
     }
     if (tid == 0) {
       s.lv_cnt[d - 1] = nk;
-      a.st_count[(size_t)q * L + d - 1] = nk;
+      if (lead) a.st_count[(size_t)q * L + d - 1] = nk;
     }
     if (MODE == 2) __builtin_amdgcn_s_waitcnt(0x0F70);   // next depth's E rows and h row have landed
     __syncthreads();
@@ -702,7 +840,7 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) s.Sf[sv_sl * (r + 1) + sv_j0 + e] = v8[e];
         }
-        if (d == a.d1) {
+        if (d == a.d1 && lead) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) st_out[(size_t)sv_sl * r + sv_j0 + e] = v8[e];
         }
@@ -734,7 +872,7 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
     __syncthreads();
   }
 
-  if (!a.do_select) return;
+  if (!a.do_select || !lead) return;
 
   // ---- deferred global top-B ---------------------------------------------------
   if (!(expand && a.d0 == 1)) {
@@ -917,14 +1055,17 @@ TreePlan tree_plan(const TreeArgs& a) {
   p.mode = mode;
   p.kq = KQ;
   p.planes = mode == 1 && lay_off(a.L, a.K, a.W, a.B, a.r, 1, KQ, true).total <= kMaxSmem;
+  p.split = (mode == 1 && a.split > 1 && a.xch && a.xflag) ? a.split : 1;
   p.smem = lay_off(a.L, a.K, a.W, a.B, a.r, mode, KQ, p.planes).total;
   p.ok = p.smem <= kMaxSmem;
   return p;
 }
 
-hipError_t launch_tree(const TreePlan& p, const TreeArgs& a, hipStream_t s) {
-  if (p.mode == 3) return launch_tree_fast(p, a, s);
-  dim3 grid(a.n_req), block(kT);
+hipError_t launch_tree(const TreePlan& p, const TreeArgs& a0, hipStream_t s) {
+  if (p.mode == 3) return launch_tree_fast(p, a0, s);
+  TreeArgs a = a0;
+  a.split = p.mode == 1 ? p.split : 1;
+  dim3 grid(a.n_req * a.split), block(kT);
   hipError_t e = hipSuccess;
 #define DT_TREE(T, M, KS, ...)                                                                             \
   do {                                                                                                     \

@@ -285,6 +285,13 @@ def verify_tree(dims: C.Dims, n_sel: torch.Tensor, tok: torch.Tensor, depth: tor
            "verify_tree")
 
 
+def set_split_wait(microseconds: int):
+    """Bound of the split general tree kernel's wait for another part of a
+    request (dartree_set_split_wait); 0 makes every part compute the whole
+    contraction itself."""
+    _check(C.load().dartree_set_split_wait(int(microseconds)), "set_split_wait")
+
+
 def set_stage_events(events: Optional[list]):
     """Profiling hook: record the given four torch.cuda.Event objects around the
     stages of every following build_round on this thread (scan, merge, tree

@@ -289,9 +289,14 @@ dartree_status dartree_build_round_noalloc(const dartree_dims* dims, const dartr
  *   tree_kernel     1 = block-decoding kernel (K <= 64, W <= 16, r = 256, bf16
  *                   weights), 0 = general kernel
  *   tree_lds_bytes  dynamic LDS of the tree launch
+ *   tree_parts      workgroups per request of the tree launch: the general
+ *                   kernel with bf16 weights (r % 32 == 0) spreads a request
+ *                   over up to 4 workgroups while n_req * parts <= 256, each
+ *                   computing a share of the depth's contraction tiles and
+ *                   exchanging them through the workspace; 1 otherwise
  * Errors: INVALID_ARGUMENT (bad dims or NULL info), UNSUPPORTED (no plan). */
 typedef struct {
-  int32_t n_launches, scan_slices, scan_workgroups, merge_separate, tree_kernel, tree_lds_bytes;
+  int32_t n_launches, scan_slices, scan_workgroups, merge_separate, tree_kernel, tree_lds_bytes, tree_parts;
 } dartree_round_info;
 dartree_status dartree_round_plan(const dartree_dims* dims, dartree_round_info* info);
 
@@ -366,6 +371,17 @@ dartree_status dartree_stream_read(const void* buf, size_t bytes, uint32_t* sink
  * while set; n = 0 (events may be NULL) clears the hook. Returns
  * INVALID_ARGUMENT for any other n or NULL handles. */
 dartree_status dartree_set_stage_events(void* const* events, int32_t n);
+
+/* Bound, in microseconds (0 .. 1000000, default 200), of how long a
+ * workgroup of the split general tree kernel (dartree_round_info.tree_parts
+ * > 1) waits for another part of its request to publish a depth's
+ * contraction slice before computing that slice itself; a part that missed
+ * the bound is not waited for again in that launch. Results do not depend on
+ * it: 0 makes every part compute the whole contraction (the path a part takes
+ * when its partners are not resident, e.g. on a GPU shared with other work).
+ * Process-wide; applies to rounds launched after the call. INVALID_ARGUMENT
+ * outside the range. */
+dartree_status dartree_set_split_wait(int32_t microseconds);
 
 #ifdef __cplusplus
 }

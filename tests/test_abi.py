@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dartree_version() == 3
+    assert lib.dartree_version() == 4
     assert C.status_string(0) == "DARTREE_OK"
     assert C.status_string(3) == "DARTREE_ERR_WORKSPACE_TOO_SMALL"
     assert C.status_string(99) == "DARTREE_UNKNOWN_STATUS"
@@ -301,3 +301,32 @@ def test_unknown_head_flags_are_rejected_before_any_device_call(lib):
     flags = ctypes.c_void_p(16)
     assert lib.dartree_head_check(ctypes.byref(d), ctypes.byref(head), flags, None) == C.ERR_INVALID_ARGUMENT
     assert "flags" in C.last_error()
+
+
+def test_split_wait_bounds(lib):
+    assert lib.dartree_set_split_wait(-1) == C.ERR_INVALID_ARGUMENT
+    assert lib.dartree_set_split_wait(1000001) == C.ERR_INVALID_ARGUMENT
+    assert lib.dartree_set_split_wait(0) == C.OK
+    assert lib.dartree_set_split_wait(200) == C.OK
+
+
+def test_general_kernel_parts_and_exchange_space(lib):
+    """bf16 weights outside the block-decoding shapes: up to 4 workgroups a
+    request while n_req * parts <= 256, with room in the workspace for the
+    exchanged slices [n][L][W][K + r] fp32 and the flags [n][parts][L]."""
+    def plan(**kw):
+        info = C.RoundInfo()
+        assert lib.dartree_round_plan(ctypes.byref(dims(**kw)), ctypes.byref(info)) == C.OK
+        return info
+    stress = dict(n_req=64, K=512, W=12, B=64, r=512, D=4096)
+    assert plan(**stress).tree_parts == 4
+    assert plan(**dict(stress, n_req=100)).tree_parts == 2
+    assert plan(**dict(stress, n_req=200)).tree_parts == 1
+    assert plan(**dict(stress, weight_dtype=C.F32)).tree_parts == 1
+    assert plan().tree_parts == 1            # block-decoding shape
+    st, n = ws_size(lib, dims(**stress))
+    assert st == C.OK
+    lists = 64 * 16 * 4 * 512 * 8    # 1024 rows x 4 slices x K keys of 8 bytes
+    xch = 64 * 16 * 12 * (512 + 512) * 4
+    flags = 64 * 4 * 16 * 4
+    assert lists + xch + flags <= n <= lists + xch + flags + 3 * 256

@@ -132,6 +132,24 @@ def test_step_entry_points_match_fused_round(name):
         assert np.array_equal(a[k], c[k]), k
 
 
+@pytest.mark.parametrize("name", ["bf16_multichunk", "wide_W32_K256", "big_B200", "beta0"])
+def test_split_parts_computing_alone_match_the_exchange(name):
+    """The general kernel spreads a request over several workgroups that
+    exchange contraction slices; with the wait bound at 0 every part computes
+    the whole contraction itself (the path of a part whose partners are not
+    resident). Both runs must give identical bits, and match the oracle."""
+    cfg = SMALL[name].with_(name=name)
+    assert ops.round_plan(ops.make_dims(cfg))["tree_parts"] > 1
+    a, _ = check(cfg)
+    try:
+        ops.set_split_wait(0)
+        b, _ = check(cfg)
+    finally:
+        ops.set_split_wait(200)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
 @pytest.mark.parametrize("chunk", range(4))
 def test_metric_config_qwen3_4b_1000_rounds(chunk):
     """All 1000 seeded rounds of the metric config, 250 per case: the whole
