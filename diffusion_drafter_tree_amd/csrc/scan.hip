@@ -698,9 +698,17 @@ __device__ void afrag_block(const ScanArgs& a, int tw) {
 // stage's LDS write then counts exactly the three younger stages' loads, and
 // the per-stage barriers wait for LDS traffic only, so about three stages of
 // loads stay in flight.
-__device__ void head_block_big(const ScanArgs& a, HeadBigSmem& sm, int tile) {
+//
+// Workgroups go to the eight XCDs in turn, and head workgroup f lands on XCD
+// f mod 8 (both in a head-only launch and when the head tiles are spread one
+// in 33 blocks through the stress round's scan grid). Tiles are handed out so
+// that each XCD takes one contiguous run of row-major tiles: its L2 then
+// fetches a few row blocks of H (and the P blocks) once instead of every row
+// block. Any order gives the same results.
+__device__ void head_block_big(const ScanArgs& a, HeadBigSmem& sm, int f) {
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int ntn = a.r / kHB;
+  const int tile = a.n_head % 8 == 0 ? (f % 8) * (a.n_head / 8) + f / 8 : f;
   const int nt = tile % ntn, mt = tile / ntn;
   const int m0 = mt * kHB, n0 = nt * kHB;
   const int sr = tid >> 4, sc = (tid & 15) * 8;   // staging: row 0..63, column 0..120
