@@ -337,6 +337,26 @@ __device__ __forceinline__ uint32_t wave_mth_largest_sorted(uint32_t v, bool val
   return readlane(k, m - 1);
 }
 
+// Coalesced weight fragments. The MFMA operand layout puts 16 different rows
+// on adjacent lanes (lane n + 16c: row n, 16-byte chunk c), so a direct load
+// touches a cache line per lane. Loading instead with lane 4n + c reading
+// chunk c of row n makes each 4-lane group read one 64-byte segment; four
+// ds_bpermute then move each lane's 16 bytes to its operand lane.
+__device__ __forceinline__ int coal_row(int lane) { return lane >> 2; }
+// rows 8..15 take their chunks in the order 2, 3, 0, 1, so that each 32-lane
+// half of a permute reads 32 different source lanes modulo 32 (no LDS bank
+// conflicts); every 4-lane group still reads one 64-byte segment
+__device__ __forceinline__ int coal_col(int lane) { return ((lane & 3) ^ ((lane >> 5) << 1)) * 8; }
+__device__ __forceinline__ u16x8_t to_mfma_lanes(u16x8_t v, int lane) {
+  const int n = lane & 15, c = lane >> 4;
+  const int src = (n * 4 + (c ^ ((n >> 3) << 1))) * 4;   // byte index of the lane that loaded row n, chunk c
+  const u32x4_t x = __builtin_bit_cast(u32x4_t, v);
+  u32x4_t y;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)x[i]);
+  return __builtin_bit_cast(u16x8_t, y);
+}
+
 // Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4 and 8 inside each
 // 16-lane row (lanes without a source add zero), then row 0's total into row
 // 1 and row 1's into rows 2 and 3 (row_bcast:15), then row 1's running total

@@ -12,7 +12,8 @@
 // tiles, ntiles * s / S .. ntiles * (s + 1) / S). Eight waves; wave w takes
 // the slab's tiles w, w + 8, ... Per D chunk staged in LDS (the 16 hidden rows,
 // bf16), each wave streams its tiles' head rows through a register ring of
-// k-steps (16 bytes a lane a step, loads issued RING steps ahead) into
+// k-steps (16 bytes a lane a step, four adjacent lanes on one 64-byte segment
+// of a head row, permuted to the operand lanes; loads issued RING steps ahead) into
 // v_mfma_f32_16x16x32_bf16 (products of bf16 are exact, fp32 accumulation)
 // and adds each finished tile into the slab's logits in LDS. Then one wave per
 // row selects the row's K best logits of the slab exactly: the K-th largest
@@ -93,11 +94,14 @@ __global__ __launch_bounds__(kLT) void lmhead_topk_kernel(LmArgs a) {
     const int gpt = nks / RING;          // groups a tile
     const int ngroups = my_nt * gpt;
     if (ngroups > 0) {
+      // head rows read with four adjacent lanes on one 64-byte segment, then
+      // permuted to the MFMA operand lanes (coal_row / to_mfma_lanes)
       auto load_group = [&](u16x8_t (&r)[RING], int g) {
         g = min(g, ngroups - 1);
         const int j = g / gpt, kg = g - j * gpt;
-        const int col = min(col0 + (w + j * kLW) * 16 + m16, a.V - 1);
-        const u16x8_t* src = reinterpret_cast<const u16x8_t*>(a.W + (size_t)col * a.D + c0 + kg * RING * 32 + sub);
+        const int col = min(col0 + (w + j * kLW) * 16 + coal_row(lane), a.V - 1);
+        const u16x8_t* src =
+            reinterpret_cast<const u16x8_t*>(a.W + (size_t)col * a.D + c0 + kg * RING * 32 + coal_col(lane));
 #pragma unroll
         for (int u = 0; u < RING; ++u) r[u] = src[u * 4];
       };
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(kLT) void lmhead_topk_kernel(LmArgs a) {
 #pragma unroll
         for (int u = 0; u < RING; ++u) {
           const u16x8_t xa = *reinterpret_cast<const LDS u16x8_t*>(xs + u * 32);
-          acc = mfma_bf16(xa, r[u], acc);
+          acc = mfma_bf16(xa, to_mfma_lanes(r[u], lane), acc);
         }
         if (kg == gpt - 1) {
           // tile j done for this chunk: rows 4 (lane / 16) + e, column m16

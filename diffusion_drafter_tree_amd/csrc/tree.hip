@@ -206,26 +206,6 @@ __device__ __forceinline__ void split_frag(const LDS float* src, bool valid, u16
   }
 }
 
-// Coalesced weight fragments. The MFMA operand layout puts 16 different rows
-// on adjacent lanes (lane n + 16c: row n, 16-byte chunk c), so a direct load
-// touches a cache line per lane. Loading instead with lane 4n + c reading
-// chunk c of row n makes each 4-lane group read one 64-byte segment; four
-// ds_bpermute then move each lane's 16 bytes to its operand lane.
-__device__ __forceinline__ int coal_row(int lane) { return lane >> 2; }
-// rows 8..15 take their chunks in the order 2, 3, 0, 1, so that each 32-lane
-// half of a permute reads 32 different source lanes modulo 32 (no LDS bank
-// conflicts); every 4-lane group still reads one 64-byte segment
-__device__ __forceinline__ int coal_col(int lane) { return ((lane & 3) ^ ((lane >> 5) << 1)) * 8; }
-__device__ __forceinline__ u16x8_t to_mfma_lanes(u16x8_t v, int lane) {
-  const int n = lane & 15, c = lane >> 4;
-  const int src = (n * 4 + (c ^ ((n >> 3) << 1))) * 4;   // byte index of the lane that loaded row n, chunk c
-  const u32x4_t x = __builtin_bit_cast(u32x4_t, v);
-  u32x4_t y;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) y[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)x[i]);
-  return __builtin_bit_cast(u16x8_t, y);
-}
-
 // ---- mode 1: MFMA with loads issued per tile ---------------------------------
 // The three bf16 fragments of parent row p at columns j0..j0+7: read from the
 // split planes (PL) or split from the fp32 row on the fly.
