@@ -150,6 +150,42 @@ def test_split_parts_computing_alone_match_the_exchange(name):
         assert np.array_equal(a[k], b[k]), k
 
 
+def test_split_rounds_sharing_the_gpu_match_rounds_alone():
+    """Two 64-request rounds of the general kernel (four workgroups a request,
+    one a CU for their LDS) launched together on two streams: 512 workgroups
+    for 256 CUs, so parts of a round are not all resident at once and wait for
+    each other only up to the bound, then compute the missing slices
+    themselves. Every output must equal the same rounds run one after the
+    other, bit for bit, and the oracle on sampled requests."""
+    cfg = I.small_variant("stress_64req", name="split_shared", V=8000, L=6, K=512, W=12, B=40, r=512, D=256)
+    plan = ops.round_plan(ops.make_dims(cfg))
+    assert plan["tree_parts"] == 4 and plan["tree_lds_bytes"] > 80 * 1024, plan
+    hd, dhd = device_head(cfg)
+    rnds = [I.make_round(cfg, 0, t) for t in range(2)]
+    ins = [(ops.to_device(r.logits), ops.to_device(r.H)) for r in rnds]
+    alone = []
+    for lg, H in ins:
+        rb = ops.RoundBuffers(cfg)
+        ops.build_round(rb.dims, dhd, lg, H, rb)
+        torch.cuda.synchronize()
+        alone.append(rb.numpy())
+    say("case split_shared: two rounds on two streams")
+    rbs = [ops.RoundBuffers(cfg) for _ in range(2)]
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for (lg, H), rb, st in zip(ins, rbs, streams):
+            ops.build_round(rb.dims, dhd, lg, H, rb, stream=st)
+        torch.cuda.synchronize()
+        for rb, ref in zip(rbs, alone):
+            out = rb.numpy()
+            for k in ref:
+                assert np.array_equal(out[k], ref[k]), k
+    for t in range(2):
+        rep = CK.check_round(cfg, hd, rnds[t], alone[t], tol=TOL, requests=[0, 31, 63])
+        PP.log_case(f"split_shared t={t} requests 0, 31, 63", rep)
+
+
 @pytest.mark.parametrize("chunk", range(4))
 def test_metric_config_qwen3_4b_1000_rounds(chunk):
     """All 1000 seeded rounds of the metric config, 250 per case: the whole
