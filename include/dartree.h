@@ -164,7 +164,11 @@ const char* dartree_last_error(void);
 int32_t dartree_version(void);
 
 /* Scratch needed by dartree_topk_candidates and dartree_build_round for
- * these dims (bytes). */
+ * these dims (bytes): the top-K's sorted slice lists, for bf16 weights of rank
+ * 256 an fp16 copy of A, and, when the general tree kernel spreads a request
+ * over several workgroups (dartree_round_info.tree_parts > 1), the area
+ * through which they exchange each depth's contraction slices, with their
+ * flags. Calls that overlap in time must use different workspaces. */
 dartree_status dartree_workspace_size(const dartree_dims* dims, size_t* bytes);
 
 /* Prepare a workspace for these dims. The current kernels keep no state in
