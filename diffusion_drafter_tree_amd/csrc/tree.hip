@@ -606,9 +606,11 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
         }
         asm volatile("" ::: "memory");
         __syncthreads();
-        // the published slices of the other parts: at most 3 vectors a thread
-        // (W (K + r) <= 16384), all loads issued before the LDS writes; an
-        // index past the end re-reads the last vector
+        // the published slices of the other parts, in batches of kG vectors a
+        // thread (one batch at most shapes: W (K + r) <= 16384 columns in all,
+        // three quarters of them from the other parts, plus the rounding of
+        // the parts' block ranges); a batch's loads are all issued before its
+        // LDS writes, and an index past the end re-reads the last vector
         int beg[5], c0[4], nz4[4], nv[4];
         int total = 0;
 #pragma unroll
@@ -632,20 +634,20 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
           const int c = j - p * nv[pt];
           col = c < nz4[pt] ? (c0[pt] >> 16) * 16 + 4 * c : NZ * 16 + (c0[pt] & 0xFFFF) + 4 * (c - nz4[pt]);
         };
-        if (total > 0) {
-          constexpr int kG = 3;
+        constexpr int kG = 3;
+        for (int i0 = 0; i0 < total; i0 += kG * kT) {
           f32x4_t gv[kG];
 #pragma unroll
           for (int u = 0; u < kG; ++u) {
             int p, col;
-            item(min(tid + u * kT, total - 1), p, col);
+            item(min(i0 + tid + u * kT, total - 1), p, col);
             gv[u] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, (p * XS + col) * 4, 0, 16));
           }
 #pragma unroll
           for (int u = 0; u < kG; ++u) {
-            if (tid + u * kT < total) {
+            if (i0 + tid + u * kT < total) {
               int p, col;
-              item(tid + u * kT, p, col);
+              item(i0 + tid + u * kT, p, col);
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 if (col < NZ * 16) {
