@@ -2,11 +2,13 @@
 // device array instead of a caller workspace, for callers that cannot
 // allocate device memory.
 //
-// The scratch of a round is the scan launch's sorted slice lists and the
-// fp16 copy of A for the block-decoding tree kernel (16 MiB at 64 requests,
-// K = 512; 160 KiB at one request, K = 64). Each kernel writes its part of the
-// scratch before any kernel reads it, so nothing in it has to start at zero
-// and no call clears it. Every GPU the library runs on holds its own copy of
+// The scratch of a round is the scan launch's sorted slice lists, the fp16
+// copy of A for the block-decoding tree kernel (16 MiB at 64 requests, K =
+// 512; 160 KiB at one request, K = 64) and, when it fits, the split general
+// kernel's exchange area (its flags are cleared by the round's scan launch);
+// when it does not fit, the round runs the general kernel with one workgroup
+// a request, which gives the same bits. Each kernel writes its part of the
+// scratch before any kernel reads it, so nothing in it has to start at zero. Every GPU the library runs on holds its own copy of
 // the array (kNoAllocScratchBytes) until the process ends; host code reaches
 // it only through the address hipGetSymbolAddress gives for that device.
 #include <hip/hip_runtime.h>

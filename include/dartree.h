@@ -264,12 +264,14 @@ dartree_status dartree_build_round(const dartree_dims* dims, const dartree_head*
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc. Same arguments, meaning, layouts, outputs
  * and errors as dartree_build_round, minus ws / ws_bytes: the round's scratch
- * (the scan's sorted slice lists, the fp16 copy of A) lives in a device array
- * the library owns, DARTREE_NOALLOC_SCRATCH_BYTES per GPU (each GPU the call
- * runs on holds its own copy until the process ends; the first call on a
- * device looks its address up). The call allocates and frees nothing.
- * Sizes whose workspace (dartree_workspace_size) exceeds the array return
- * DARTREE_ERR_UNSUPPORTED before anything is enqueued. Every call on one GPU
+ * (the scan's sorted slice lists, the fp16 copy of A and, when it fits, the
+ * split general kernel's exchange area) lives in a device array the library
+ * owns, DARTREE_NOALLOC_SCRATCH_BYTES per GPU (each GPU the call runs on holds
+ * its own copy until the process ends; the first call on a device looks its
+ * address up). The call allocates and frees nothing. When the exchange area
+ * does not fit, the general kernel keeps one workgroup a request (the same
+ * results). Sizes whose scratch exceeds the array even without the exchange
+ * area return DARTREE_ERR_UNSUPPORTED before anything is enqueued. Every call on one GPU
  * shares that GPU's array: calls that overlap on one GPU (other streams,
  * other threads) race and must be serialised by the caller. The array keeps
  * the last call's contents; nothing in it has to start at zero. */
