@@ -193,6 +193,56 @@ def test_split_rounds_sharing_the_gpu_match_rounds_alone():
         PP.log_case(f"split_shared t={t} requests 0, 31, 63", rep)
 
 
+def test_rejected_calls_leave_every_output_untouched():
+    """Every call validates completely on the host before it enqueues
+    anything: a rejected dartree_build_round (and dartree_topk_candidates)
+    must return its status and leave every output and the workspace byte for
+    byte as they were (canary-filled)."""
+    import ctypes
+    from diffusion_drafter_tree_amd import _lib as C
+    cfg = SMALL["bf16_multichunk"].with_(name="canary")
+    hd, dhd = device_head(cfg)
+    rnd = I.make_round(cfg, 0, 0)
+    logits, H = ops.to_device(rnd.logits), ops.to_device(rnd.H)
+    rb = ops.RoundBuffers(cfg)
+    outs = [rb.cand_ids, rb.cand_logit, rb.h, rb.st_tok, rb.st_parent, rb.st_cum, rb.st_sbeta, rb.st_count,
+            rb.st_state, rb.n_sel, rb.tok, rb.depth, rb.parent, rb.score, rb.slot, rb.mask, rb.ws]
+    for t in outs:
+        t.view(torch.uint8).fill_(0xA5)
+    torch.cuda.synchronize()
+    before = [t.view(torch.uint8).cpu().clone() for t in outs]
+    lib = C.load()
+
+    def build(dims, head=dhd, logits=logits, ws_bytes=rb.ws_bytes):
+        rb.st.next_depth = 1
+        return lib.dartree_build_round(ctypes.byref(dims), ctypes.byref(head.c), ops._p(logits), ops._p(H),
+                                       ops._p(rb.cand_ids), ops._p(rb.cand_logit), ops._p(rb.h), ctypes.byref(rb.st),
+                                       ops._p(rb.n_sel), ops._p(rb.tok), ops._p(rb.depth), ops._p(rb.parent),
+                                       ops._p(rb.score), ops._p(rb.slot), ops._p(rb.mask), ops._p(rb.ws), ws_bytes,
+                                       ops._stream())
+    good = ops.make_dims(cfg)
+    bad_beta = ops.make_dims(cfg.with_(beta=0.5))
+    bad_k = ops.make_dims(cfg.with_(K=cfg.V + 1))
+    bad_flags = copy.copy(dhd)
+    bad_flags.c = C.Head(A=dhd.c.A, E=dhd.c.E, U=dhd.c.U, Pt=dhd.c.Pt, flags=0x100)
+    cases = [
+        ("beta > 0", build(bad_beta), C.ERR_INVALID_ARGUMENT),
+        ("K > V", build(bad_k), C.ERR_INVALID_ARGUMENT),
+        ("workspace too small", build(good, ws_bytes=rb.ws_bytes - 256), C.ERR_WORKSPACE_TOO_SMALL),
+        ("misaligned logits", build(good, logits=logits.view(torch.uint8)[2:]), C.ERR_INVALID_ARGUMENT),
+        ("unknown head flag", build(good, head=bad_flags), C.ERR_INVALID_ARGUMENT),
+        ("topk: workspace too small",
+         lib.dartree_topk_candidates(ctypes.byref(good), ops._p(logits), ops._p(rb.cand_ids), ops._p(rb.cand_logit),
+                                     ops._p(rb.ws), 16, ops._stream()), C.ERR_WORKSPACE_TOO_SMALL),
+    ]
+    torch.cuda.synchronize()
+    for what, got, want in cases:
+        say(f"  rejected call: {what}: {C.status_string(got)}")
+        assert got == want, (what, C.status_string(got), C.last_error())
+    for t, b0 in zip(outs, before):
+        assert torch.equal(t.view(torch.uint8).cpu(), b0)
+
+
 @pytest.mark.parametrize("chunk", range(4))
 def test_metric_config_qwen3_4b_1000_rounds(chunk):
     """All 1000 seeded rounds of the metric config, 250 per case: the whole
