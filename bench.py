@@ -15,6 +15,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -858,6 +859,26 @@ def _oracle_rounds(args):
     return len(rounds), time.perf_counter() - t0
 
 
+def _oracle_heaps(cfg, head, rnd, res):
+    """Context beside the deferred oracle: the oracle's two literal heaps on
+    the first request of the last timed round, each timed alone (ms). The
+    materialised-supertree heap pops the supertree the round built; the
+    serial pop-then-correct heap runs the head at every pop over the full
+    K-ary tree. Widening the head's tables to fp64 is done once, untimed."""
+    from oracle import dartree_oracle as O
+    wd = head.dtype
+    A, E, U = O.widen(head.A, wd), O.widen(head.E, wd), O.widen(head.U, wd)
+    r0 = res[0]
+    t0 = time.perf_counter()
+    O.heap_materialized(r0.levels, cfg.B)
+    t1 = time.perf_counter()
+    O.heap_serial_full(r0.cand_ids, r0.cand_vals, r0.h, A, E, U, cfg.beta, cfg.B)
+    t2 = time.perf_counter()
+    return {"request": 0, "supertree_heap_ms": round(1e3 * (t1 - t0), 3),
+            "serial_full_tree_heap_ms": round(1e3 * (t2 - t1), 3),
+            "note": "one request of the last round; the serial heap's cost is the head run at each of its B pops"}
+
+
 def cpu_baseline(cfg, head, budget_s):
     """The oracle as it stands, on the same workload: on 1 host thread over
     distinct seeded rounds until ~budget_s of CPU time, and on every host
@@ -877,21 +898,29 @@ def cpu_baseline(cfg, head, budget_s):
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
     if ctx:
         ctx.__enter__()
+    times = []
+    heaps = None
     try:
-        t0 = time.perf_counter()
-        done = 0
-        while True:
-            O.round_all(cfg, head, I.make_round(cfg, 0, 1000 + done))
-            done += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s or done >= 1000:
-                break
+        el = 0.0
+        last = None
+        while el < budget_s and len(times) < 1000:
+            rnd = I.make_round(cfg, 0, 1000 + len(times))
+            t0 = time.perf_counter()
+            res = O.round_all(cfg, head, rnd)
+            dt = time.perf_counter() - t0
+            times.append(dt)
+            el += dt
+            last = (rnd, res)
+        heaps = _oracle_heaps(cfg, head, *last) if last else None
     finally:
         if ctx:
             ctx.__exit__(None, None, None)
+    done = len(times)
     one = {"value": round(done / el, 3), "unit": "builds/s", "cores": 1, "kind": "oracle",
+           "median_ms_per_round": round(1e3 * statistics.median(times), 2),
            "sample": f"{done} distinct seeded rounds of {cfg.name} (t = 1000..{999 + done}), numpy fp64, "
-                     f"{el:.1f} s on 1 host thread (round generation excluded)"}
+                     f"{el:.1f} s of oracle time on 1 host thread (round generation not timed)",
+           "literal_heaps": heaps}
     try:
         ncores = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
