@@ -732,10 +732,19 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
         } else if (lane == 0) {
           lds_or(&s.misc[4], 1);
         }
+        // A second bound: this wave alone holds Wq keys at or above the Wq-th
+        // largest of its lane maxima, so the largest such value over the waves
+        // also leaves at least Wq keys. The wave of the best parent usually
+        // gives it, and it is far above the first (the least of the waves'
+        // best keys): tens of survivors instead of hundreds to rank.
+        if (nv >= Wq && Wq <= kWave) {
+          const uint32_t t2 = wave_mth_largest(lmax, v, Wq, 32);
+          if (lane == 0) lds_max((LDS unsigned*)&s.misc[6], t2);
+        }
       }
     }
     __syncthreads();
-    const uint32_t thr = s.misc[4] ? 0u : ~(uint32_t)s.misc[2];
+    const uint32_t thr = max(s.misc[4] ? 0u : ~(uint32_t)s.misc[2], (uint32_t)s.misc[6]);
     int ns = select_compact<EPT>(keys, pays, thr, sel);
     if (ns > kSelCap) ns = select_exact<EPT>(keys, pays, Wq, sel);
     const int nk = select_rank(ns, Wq, sel);
