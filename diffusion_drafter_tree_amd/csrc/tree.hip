@@ -732,13 +732,14 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
         } else if (lane == 0) {
           lds_or(&s.misc[4], 1);
         }
-        // A second bound: this wave alone holds Wq keys at or above the Wq-th
-        // largest of its lane maxima, so the largest such value over the waves
-        // also leaves at least Wq keys. The wave of the best parent usually
-        // gives it, and it is far above the first (the least of the waves'
-        // best keys): tens of survivors instead of hundreds to rank.
-        if (nv >= Wq && Wq <= kWave) {
-          const uint32_t t2 = wave_mth_largest(lmax, v, Wq, 32);
+        // A second bound: a wave holds Wq keys at or above the Wq-th largest
+        // of its lane maxima. Wave 0 holds the best parent's children (the
+        // parents are in rank order), whose Wq-th is usually far above the
+        // first bound (the least of the waves' best keys): tens of survivors
+        // instead of hundreds to rank. Taken from wave 0 alone, through the
+        // 64-lane sort network, so the other waves do not wait on it.
+        if (w == 0 && nv >= Wq && Wq <= kWave) {
+          const uint32_t t2 = wave_mth_largest_sorted(lmax, v, Wq);
           if (lane == 0) lds_max((LDS unsigned*)&s.misc[6], t2);
         }
       }
