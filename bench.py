@@ -505,12 +505,28 @@ def head_at_stress_shape(n_timed=16):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1000.0 / n_timed
+    # the vendor library's GEMM on the same operands, timed the same way
+    # (torch.matmul on bf16 tensors: hipBLASLt; P made contiguous once, outside
+    # the timed calls), for context: what this shape allows a tuned GEMM
+    Hb, P = H.view(torch.bfloat16), Pt.view(torch.bfloat16).t().contiguous()
+    for _ in range(4):
+        torch.matmul(Hb, P)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n_timed):
+        torch.matmul(Hb, P)
+    e1.record()
+    torch.cuda.synchronize()
+    us_lib = e0.elapsed_time(e1) * 1000.0 / n_timed
     flops = 2 * M * D * r
     peak = 2500.0   # TFLOP/s, dense bf16 MFMA
     tf = flops / (us * 1e-6) / 1e12
     return {"kernel": "head tiles of h = P^T H (64 x 64, LDS-staged, v_mfma_f32_16x16x32_bf16)", "bound": "mfma",
             "workload": f"stress_64req head inputs: M={M} D={D} r={r} bf16, fp32 out", "achieved": round(tf, 1),
-            "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4), "us": round(us, 2), "alg_flops": flops}
+            "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4), "us": round(us, 2), "alg_flops": flops,
+            "vendor_gemm_us": round(us_lib, 2),
+            "vendor_gemm_frac": round(flops / (us_lib * 1e-6) / 1e12 / peak, 4),
+            "vendor_gemm": "torch.matmul bf16 (hipBLASLt), bf16 output, same operands"}
 
 
 def scan_at_stress_shape(hbm_peak, read_peak, n_timed=16):

@@ -43,6 +43,7 @@ struct ScanSmem {
   uint64_t out[1024];
   u32x4_t hitq[kHitCap];
   int hitid[kHitCap];
+  int bhist[256];   // lane maxima by distance below the slice's largest key
   int misc[8];
   int wsum[kWaves];
 };
@@ -303,12 +304,14 @@ __device__ void scan_block(const ScanArgs& a, Smem& sm, int blk, const u32x4_t (
   const int m = nact > 0 ? (K + nact - 1) / nact : K;
   if (nact == 0 && tid == 0) sm.misc[4] = 1;   // empty slice: the exact path yields nothing
   bool block_bound = false;
-  if constexpr (WIDE) {
+  {
     // Bound from the whole block: the K-th largest lane maximum, to bin
-    // precision. Lane maxima are binned by their key distance below the
-    // slice's largest key (bin = one bf16 value, or 2^16 fp32 keys; 255
-    // collects the rest); counting down from the top bin, the first bin b*
-    // that brings the count to K gives T, the lowest key bin b* can hold.
+    // precision (at K = 64 about half the survivors of the per-wave bound
+    // below, which remains the fallback). Lane maxima are binned by their
+    // key distance below the slice's largest key (bin = one bf16 value, or
+    // 2^16 fp32 keys; 255 collects the rest); counting down from the top
+    // bin, the first bin b* that brings the count to K gives T, the lowest
+    // key bin b* can hold.
     // At least K lanes, hence K elements, reach T (a histogram of the five
     // vector maxima a lane holds gives a tighter T, but its LDS atomics cost
     // more than the smaller survivor set saves). The slice's largest key
@@ -787,6 +790,7 @@ __global__ __launch_bounds__(kT) void scan_kernel(ScanArgs a) {
   clear_words(a);
   if (b < a.n_scan) {
     if (threadIdx.x < 8) smem.scan.misc[threadIdx.x] = 0;
+    if (threadIdx.x < 256) smem.scan.bhist[threadIdx.x] = 0;
     if (BF16)
       for (int i = threadIdx.x; i < kScanCap + 32; i += kT) smem.scan.key32[i] = 0u;
     __syncthreads();
