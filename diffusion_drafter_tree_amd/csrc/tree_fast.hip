@@ -356,28 +356,6 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       s.clog[i] = clog_g[i];
     }
   }
-  // A fragments: 1 KB contiguous runs of the fp16 copy the scan launch
-  // staged, or (without it) 16 rows x 16 bytes of A per load, converted below
-  if constexpr (markov) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) araw[t][i] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-  } else if (expand && a.a_frag) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        araw[t][i] = *reinterpret_cast<const u16x8_t*>(
-            a.a_frag + ((size_t)((w * 2 + t) * 4 + ((i + zrot) & 3)) * kWave + lane) * 8);
-  } else if (expand) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint16_t* arow = A + (size_t)(aw * 32 + t * 16 + (lane & 15)) * RT + sub;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) araw[t][i] = *reinterpret_cast<const u16x8_t*>(arow + kstep(i) * 32);
-    }
-  }
   if (expand && a.d0 == 1 && w == 0) {
     // The root state h_0 is not bounded like the tanh states below it: it is
     // held in the fp16 planes as h_0 * 2^-t, with t the smallest shift that
@@ -407,6 +385,31 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
         for (int e = 0; e < 4; ++e) v[e] = st[p * RT + j0 + e];
       }
       split_store4(s, p, j0, v);
+    }
+  }
+  // A fragments: 1 KB contiguous runs of the fp16 copy the scan launch
+  // staged, or (without it) 16 rows x 16 bytes of A per load, converted below.
+  // Issued after the parents' states above: their loads are conditional (a
+  // launch that starts below depth 1), so the compiler waits for every
+  // outstanding load where those paths join, which would include these.
+  if constexpr (markov) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) araw[t][i] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  } else if (expand && a.a_frag) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        araw[t][i] = *reinterpret_cast<const u16x8_t*>(
+            a.a_frag + ((size_t)((w * 2 + t) * 4 + ((i + zrot) & 3)) * kWave + lane) * 8);
+  } else if (expand) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t* arow = A + (size_t)(aw * 32 + t * 16 + (lane & 15)) * RT + sub;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) araw[t][i] = *reinterpret_cast<const u16x8_t*>(arow + kstep(i) * 32);
     }
   }
   __syncthreads();
