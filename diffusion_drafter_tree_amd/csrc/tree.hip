@@ -241,10 +241,11 @@ __device__ __forceinline__ void z_mfma_general(const Lay& s, const uint16_t* __r
     const uint16_t* urow = U + (size_t)s.cid[min(nt * 16 + coal_row(lane), K - 1)] * r + coal_col(lane);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < KS; k0 += GB) {
+      // every load of the batch is issued (past the end it re-reads the last
+      // k-step, unused), so the compiler waits for each fragment alone
       u16x8_t b[GB];
 #pragma unroll
-      for (int g = 0; g < GB; ++g)
-        if (k0 + g < KS) b[g] = *reinterpret_cast<const u16x8_t*>(urow + (k0 + g) * 32);
+      for (int g = 0; g < GB; ++g) b[g] = *reinterpret_cast<const u16x8_t*>(urow + min(k0 + g, KS - 1) * 32);
 #pragma unroll
       for (int g = 0; g < GB; ++g) {
         if (k0 + g < KS) {
@@ -280,8 +281,7 @@ __device__ __forceinline__ void as_mfma_general(const Lay& s, const uint16_t* __
     for (int k0 = 0; k0 < KS; k0 += GB) {
       u16x8_t av[GB];
 #pragma unroll
-      for (int g = 0; g < GB; ++g)
-        if (k0 + g < KS) av[g] = *reinterpret_cast<const u16x8_t*>(arow + (k0 + g) * 32);
+      for (int g = 0; g < GB; ++g) av[g] = *reinterpret_cast<const u16x8_t*>(arow + min(k0 + g, KS - 1) * 32);
 #pragma unroll
       for (int g = 0; g < GB; ++g) {
         if (k0 + g < KS) {
