@@ -371,6 +371,13 @@ __device__ __forceinline__ int wave_incl_scan_i32(int x) {
   return x;
 }
 
+// tanh(x) = 1 - 2 / (2^(2 x log2 e) + 1) on the hardware exp2 and reciprocal
+// (each within about 1 ulp): absolute error a few 1e-7, saturating to +-1.
+__device__ __forceinline__ float tanh_fast(float x) {
+  const float e = __builtin_amdgcn_exp2f(x * 2.8853900817779268f);
+  return __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f);
+}
+
 // two fp32 values to fp16, rounding toward zero (v_cvt_pkrtz_f16_f32)
 __device__ __forceinline__ h16x2_t pkrtz(float a, float b) {
   typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));

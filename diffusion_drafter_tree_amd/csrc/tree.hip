@@ -696,12 +696,15 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
         }
       }
       m = wave_max_f32(m);
+      // exp and log on the hardware exp2 / log2 with the change of base by
+      // one multiply (relative error about 1e-7; the terms near the maximum
+      // dominate the sum)
       float ssum = 0.f;
 #pragma unroll
       for (int j = 0; j < EPT; ++j)
-        if (j < KJ && lane + j * kWave < K) ssum += expf(z[j] - m);
+        if (j < KJ && lane + j * kWave < K) ssum += __builtin_amdgcn_exp2f((z[j] - m) * 1.4426950408889634f);
       ssum = wave_sum_f32(ssum);
-      const float lse = m + logf(ssum);
+      const float lse = m + __builtin_amdgcn_logf(ssum) * 0.6931471805599453f;
       const float cp = s.cumP[p];
 #pragma unroll
       for (int j = 0; j < EPT; ++j) {
@@ -813,7 +816,7 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
         float v8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          v8[e] = tanhf(((markov ? 0.f : s.AS[(size_t)sv_ps * (r + 1) + sv_j0 + e]) + bf16_to_f32(ev8[e])) + hv8[e]);
+          v8[e] = tanh_fast(((markov ? 0.f : s.AS[(size_t)sv_ps * (r + 1) + sv_j0 + e]) + bf16_to_f32(ev8[e])) + hv8[e]);
         if (kPl) {
           u16x8_t fh, fm, fl;
 #pragma unroll
@@ -848,7 +851,7 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
           ev = ldw(E, (size_t)s.lv_tok[row0 + sl] * r + j);
           hv = hd[j];
         }
-        const float v = tanhf(((markov ? 0.f : s.AS[(size_t)ps * (r + 1) + j]) + ev) + hv);
+        const float v = tanh_fast(((markov ? 0.f : s.AS[(size_t)ps * (r + 1) + j]) + ev) + hv);
         if (kPl) split_store(s, r, sl, j, v);
         else s.Sf[sl * (r + 1) + j] = v;
         if (d == a.d1) st_out[i] = v;

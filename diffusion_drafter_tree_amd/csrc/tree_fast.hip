@@ -196,13 +196,6 @@ __device__ __forceinline__ void split_store4(const FLay& s, int row, int j0, con
 }
 
 
-// tanh(x) = 1 - 2 / (2^(2 x log2 e) + 1) on the hardware exp2 and reciprocal
-// (each within about 1 ulp): absolute error a few 1e-7, saturating to +-1.
-__device__ __forceinline__ float tanh_fast(float x) {
-  const float e = __builtin_amdgcn_exp2f(x * 2.8853900817779268f);
-  return __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f);
-}
-
 // Path ranks of level d (1-based) from the ranks of level d-1: the order of
 // (parent's path rank, token) among the level's cnt nodes. One wave.
 __device__ __forceinline__ void level_lex_wave(const FLay& s, int d, int W, int cnt, const uint32_t tok,
