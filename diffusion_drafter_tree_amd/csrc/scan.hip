@@ -892,6 +892,62 @@ __global__ __launch_bounds__(kT) void merge_kernel(const uint64_t* __restrict__ 
   }
 }
 
+// The same merge by pairs of lists, for up to eight lists: the lists (padded
+// with empty ones to a power of two) are merged pairwise, level by level, in
+// LDS. Keys are distinct and nonzero (0 marks an empty slot), so a key's place
+// in the merge of its list a with the partner list b is its index in a plus
+// the number of b's keys above it (a binary search in the descending list b);
+// places at or past K are dropped. log2(lists) levels of one search per key,
+// against the value histogram's dozen barriers. Same output, key for key.
+constexpr int kMergeSortedMaxS = 8;
+#ifndef DARTREE_MERGE_NT
+#define DARTREE_MERGE_NT 1024
+#endif
+constexpr int kMergeT = DARTREE_MERGE_NT;
+__global__ __launch_bounds__(kMergeT) void merge_sorted_kernel(const uint64_t* __restrict__ lists, int S, int K,
+                                                               bool bf16, int32_t* __restrict__ cand_ids,
+                                                               float* __restrict__ cand_logit) {
+  extern __shared__ __align__(16) char smem_raw[];
+  int P = 1;
+  while (P < S) P <<= 1;
+  LDS uint64_t* buf0 = (LDS uint64_t*)smem_raw;
+  LDS uint64_t* buf1 = buf0 + (size_t)P * K;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const uint64_t* Lr = lists + (size_t)row * S * K;
+  for (int i = tid; i < P * K; i += kMergeT) buf0[i] = i < S * K ? Lr[i] : 0ull;
+  __syncthreads();
+  LDS uint64_t* cur = buf0;
+  LDS uint64_t* nxt = buf1;
+  for (int n = P; n > 1; n >>= 1) {
+    for (int i = tid; i < (n >> 1) * K; i += kMergeT) nxt[i] = 0ull;
+    __syncthreads();
+    for (int i = tid; i < n * K; i += kMergeT) {
+      const uint64_t x = cur[i];
+      if (x == 0ull) continue;
+      const int l = i / K, j = i - l * K;
+      const LDS uint64_t* b = cur + (size_t)(l ^ 1) * K;
+      int lo = 0, hi = K;   // first place in b whose key is below x = b's keys above x
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (b[mid] > x) lo = mid + 1;
+        else hi = mid;
+      }
+      const int r = j + lo;
+      if (r < K) nxt[(size_t)(l >> 1) * K + r] = x;
+    }
+    __syncthreads();
+    LDS uint64_t* t = cur;
+    cur = nxt;
+    nxt = t;
+  }
+  for (int i = tid; i < K; i += kMergeT) {
+    const uint64_t x = cur[i];
+    cand_ids[(size_t)row * K + i] = x ? (int32_t)(0xFFFFFFFFu - (uint32_t)x) : -1;
+    cand_logit[(size_t)row * K + i] =
+        x ? (bf16 ? bf16_key_to_f32((uint32_t)(x >> 32)) : key_to_f32((uint32_t)(x >> 32))) : -__builtin_huge_valf();
+  }
+}
+
 __global__ __launch_bounds__(256) void head_valu_f32(const float* __restrict__ H, const float* __restrict__ Pt,
                                                      float* __restrict__ h, int M, int D, int r) {
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -971,6 +1027,19 @@ hipError_t launch_scan(const ScanPlan& p, bool bf16, const ScanArgs& args_in, hi
 hipError_t launch_merge(const ScanPlan& p, int rows, int K, bool bf16, const uint64_t* lists, int32_t* cand_ids,
                         float* cand_logit, hipStream_t s) {
   if (p.S <= 1) return hipSuccess;
+  if (p.S <= kMergeSortedMaxS) {
+    int P = 1;
+    while (P < p.S) P <<= 1;
+    const size_t lds = (size_t)2 * P * K * sizeof(uint64_t);
+    if (lds <= 64 * 1024) {
+      hipError_t e = hipFuncSetAttribute((const void*)merge_sorted_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(merge_sorted_kernel, dim3(rows), dim3(kMergeT), lds, s, lists, p.S, K, bf16, cand_ids,
+                         cand_logit);
+      return hipGetLastError();
+    }
+  }
   if (p.merge_ept == 8)
     hipLaunchKernelGGL((merge_kernel<8>), dim3(rows), dim3(kT), 0, s, lists, p.S, K, bf16, cand_ids, cand_logit);
   else
