@@ -738,6 +738,20 @@ def test_topk_small_and_ragged_rows():
         CK.check_candidates(ids, vals, I.bf16_bits_to_f32(bits).astype(np.float64), K, where=f"V={V}")
 
 
+def test_topk_merge_of_several_slices():
+    """Rows long enough to span 3, 4, 5 and 7 vocabulary slices with K > 64, so
+    the slice lists go through the separate merge (lists padded to a power of
+    two: 3 -> 4, 5 and 7 -> 8), up to the largest vocabulary the ABI takes
+    (2^18), with tie-heavy values (steps of 0.5) and K not a power of two."""
+    rng = np.random.default_rng(11)
+    for V, K in [(100000, 128), (140000, 65), (200000, 333), (262144, 200)]:
+        x = (np.round(rng.normal(0, 1, (3, V)) * 2) / 2).astype(np.float32)
+        bits = I.f32_to_bf16_bits(x)
+        say(f"case topk merge V={V} K={K}")
+        ids, vals = _topk_rows(bits, K)
+        CK.check_candidates(ids, vals, I.bf16_bits_to_f32(bits).astype(np.float64), K, where=f"V={V}")
+
+
 def test_tree_mask_on_handmade_parents():
     B = 130
     rng = np.random.default_rng(3)
