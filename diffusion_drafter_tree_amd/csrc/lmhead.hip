@@ -193,35 +193,150 @@ __global__ __launch_bounds__(kLT) void lmhead_topk_kernel(LmArgs a) {
 }
 
 // The S sorted lists of each row (K <= 64 keys each, descending, zero
-// padded) merged into the row's K best, one workgroup a row: wave w merges
-// lists w, w + 16, ... pairwise in registers (the elementwise maximum of one
-// descending list and the other reversed holds the 64 best of both as a
-// bitonic sequence, which six half-cleaner stages sort descending), the 16
-// waves' results meet in LDS, and wave 0 merges those the same way.
+// padded) merged into the row's K best, one workgroup a row; wave w holds
+// lists w, w + 16, ... (16 at most), all loaded at once.
+//
+// Pruned path: T, the K-th largest value word (the key's high 32 bits) among
+// the S list maxima, is reached by K distinct keys, so the row's K-th best
+// key has a value word >= T and so has every key of the result. Only the keys
+// whose value word is >= T (about K of them when the row's best keys are
+// spread over many slabs) are gathered into LDS and ranked by counting. When more than kSurvCap keys reach T (ties across slabs, a head
+// whose logits repeat), the lists are merged in full instead: pairwise in a
+// tree per wave (the elementwise maximum of one descending list and the other
+// reversed holds the K best of both as a bitonic sequence, which six
+// half-cleaner stages sort descending), then the 16 waves' results by wave
+// 0 the same way. Keys are distinct (each carries its column), so both paths
+// give the same K keys in the same order.
 constexpr int kMT = 1024, kMW = kMT / kWave;
+constexpr int kMPer = kMaxSlabs / kMW;   // lists a wave
+constexpr int kSurvCap = kMT;            // survivors the pruned path ranks (one a thread)
+static_assert(kMPer == 16, "the merge tree below takes 16 lists a wave");
+
+// K best of 16 sorted lists, one a register pair per lane; the result in
+// (h[0], l[0]).
+__device__ __forceinline__ void merge_tree16(uint32_t (&h)[16], uint32_t (&l)[16]) {
+#pragma unroll
+  for (int st = 1; st < 16; st *= 2)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2 * st) wave_merge_desc(h[i], l[i], ((uint64_t)h[i + st] << 32) | l[i + st]);
+}
 
 __global__ __launch_bounds__(kMT) void lmhead_merge_kernel(const uint64_t* __restrict__ lists, int S, int K,
                                                            int32_t* __restrict__ cand_ids,
                                                            float* __restrict__ cand_logit) {
-  __shared__ uint64_t part[kMW][kWave];
-  const int row = blockIdx.x, lane = lane_id(), w = threadIdx.x / kWave;
+  __shared__ __align__(16) uint32_t mx[kMaxSlabs];   // value words of the list maxima (zero: absent list)
+  __shared__ uint64_t sv[kSurvCap];                     // keys whose value word is >= T
+  __shared__ uint64_t part[kMW][kWave];                 // full merge: the waves' results
+  __shared__ uint32_t thr;
+  __shared__ int nsv;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const uint64_t* L = lists + (size_t)row * S * K;
   const bool v = lane < K;
-  uint32_t ah = 0u, al = 0u;
-  if (w < S) {
-    const uint64_t k0 = v ? L[(size_t)w * K + lane] : 0ull;
-    ah = (uint32_t)(k0 >> 32);
-    al = (uint32_t)k0;
-    for (int sl = w + kMW; sl < S; sl += kMW) wave_merge_desc(ah, al, v ? L[(size_t)sl * K + lane] : 0ull);
+  // addresses clamped into the row's lists (every load is issued), the
+  // slots past S and the lanes past K zeroed after
+  const int ln = min(lane, K - 1);
+  uint64_t kk[kMPer];
+#pragma unroll
+  for (int i = 0; i < kMPer; ++i) kk[i] = L[(size_t)min(w + i * kMW, S - 1) * K + ln];
+  if (tid == 0) {
+    thr = 0u;
+    nsv = 0;
   }
-  part[w][lane] = ((uint64_t)ah << 32) | al;
+  uint32_t h[kMPer], l[kMPer];
+#pragma unroll
+  for (int i = 0; i < kMPer; ++i) {
+    const uint64_t x = (v && w + i * kMW < S) ? kk[i] : 0ull;
+    h[i] = (uint32_t)(x >> 32);
+    l[i] = (uint32_t)x;
+    if (lane == 0) mx[w + i * kMW] = h[i];
+  }
+  __syncthreads();
+  {
+    // T: the value word m of a maximum with fewer than K maxima above it and
+    // at least K at or above it (one value, possibly held by several
+    // maxima); four threads a maximum, each counting over a quarter. With
+    // fewer than K non-zero maxima it is zero: nothing is pruned.
+    const int x = tid >> 2, q4 = tid & 3;
+    const uint32_t me = mx[x];
+    uint32_t gt = 0u, ge = 0u;
+    const LDS u32x4_t* m4 = reinterpret_cast<const LDS u32x4_t*>((const LDS uint32_t*)mx) + q4 * (kMaxSlabs / 16);
+#pragma unroll
+    for (int j = 0; j < kMaxSlabs / 16; ++j) {
+      const u32x4_t y = m4[j];
+      gt += (y.x > me) + (y.y > me) + (y.z > me) + (y.w > me);
+      ge += (y.x >= me) + (y.y >= me) + (y.z >= me) + (y.w >= me);
+    }
+    gt += dpp<kDppXor1>(gt);
+    gt += dpp<kDppXor2>(gt);
+    ge += dpp<kDppXor1>(ge);
+    ge += dpp<kDppXor2>(ge);
+    if (q4 == 0 && (int)gt < K && (int)ge >= K) thr = me;
+  }
+  __syncthreads();
+  const uint32_t T = thr;
+  {
+    // keys whose value word is >= T (non-zero) gathered into sv, one LDS
+    // atomic a wave
+    uint64_t bal[kMPer];
+    int tot = 0;
+#pragma unroll
+    for (int i = 0; i < kMPer; ++i) {
+      bal[i] = __ballot((h[i] | l[i]) != 0u && h[i] >= T);
+      tot += __popcll(bal[i]);
+    }
+    int base = 0;
+    if (lane == 0 && tot) base = lds_add((LDS int*)&nsv, tot);
+    base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+    for (int i = 0; i < kMPer; ++i) {
+      const int pos = base + (int)mbcnt64(bal[i]);
+      if (((bal[i] >> lane) & 1ull) && pos < kSurvCap) sv[pos] = ((uint64_t)h[i] << 32) | l[i];
+      base += __popcll(bal[i]);
+    }
+  }
+  __syncthreads();
+  const int ns = nsv;
+  if (ns <= kSurvCap) {
+    // rank by counting: a key's place is the number of larger survivors
+    if (tid < ns) {
+      const uint64_t me = sv[tid];
+      uint32_t r = 0u;
+      int j = 0;
+      for (; j + 4 <= ns; j += 4) {
+        uint64_t k4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) k4[e] = sv[j + e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r += k4[e] > me ? 1u : 0u;
+      }
+      for (; j < ns; ++j) r += sv[j] > me ? 1u : 0u;
+      if ((int)r < K) {
+        cand_ids[(size_t)row * K + r] = (int32_t)(0xFFFFFFFFu - (uint32_t)me);
+        cand_logit[(size_t)row * K + r] = key_to_f32((uint32_t)(me >> 32));
+      }
+    }
+    // fewer than K keys in the row: the places past them are empty
+    if (tid >= ns && tid < K) {
+      cand_ids[(size_t)row * K + tid] = -1;
+      cand_logit[(size_t)row * K + tid] = -__builtin_huge_valf();
+    }
+    return;
+  }
+  merge_tree16(h, l);
+  part[w][lane] = ((uint64_t)h[0] << 32) | l[0];
   __syncthreads();
   if (w == 0) {
-    for (int i = 1; i < kMW; ++i) wave_merge_desc(ah, al, part[i][lane]);
+#pragma unroll
+    for (int i = 0; i < kMW; ++i) {
+      const uint64_t x = part[i][lane];
+      h[i] = (uint32_t)(x >> 32);
+      l[i] = (uint32_t)x;
+    }
+    merge_tree16(h, l);
     if (v) {
-      const bool ok = (ah | al) != 0u;
-      cand_ids[(size_t)row * K + lane] = ok ? (int32_t)(0xFFFFFFFFu - al) : -1;
-      cand_logit[(size_t)row * K + lane] = ok ? key_to_f32(ah) : -__builtin_huge_valf();
+      const bool ok = (h[0] | l[0]) != 0u;
+      cand_ids[(size_t)row * K + lane] = ok ? (int32_t)(0xFFFFFFFFu - l[0]) : -1;
+      cand_logit[(size_t)row * K + lane] = ok ? key_to_f32(h[0]) : -__builtin_huge_valf();
     }
   }
 }

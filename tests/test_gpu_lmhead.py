@@ -76,3 +76,35 @@ def test_lmhead_exact_ties_at_the_cut_take_the_lower_id():
     rep = CK.check_lmhead_topk(ids, vals, Xf, Wf2, cfg.K, tol=TOL, where="ties")
     PP.log_case("lmhead exact ties", rep, rows=rows)
     assert rep.tie_events_level == 0, rep.tie_log
+
+
+def test_lmhead_all_logits_equal_takes_the_lowest_ids():
+    """Zero hidden states: every logit is exactly 0, so the K best are the K
+    lowest token ids. Far more than K keys of the slab lists reach the
+    K-th largest slab maximum here, which sends the merge down its full
+    (unpruned) path."""
+    cfg = I.small_variant("qwen3_4b", name="lmhead_flat", n_req=1, L=3, V=151936, D=256, K=64)
+    W = I.make_lmhead(cfg, 5)
+    rows = cfg.n_req * cfg.L
+    X = np.zeros((rows, cfg.D), dtype=np.uint16)
+    ids, vals = run_lmhead(cfg, X, W)
+    assert (ids == np.arange(cfg.K, dtype=np.int32)[None, :]).all()
+    assert (vals == 0.0).all()
+    rep = CK.check_lmhead_topk(ids, vals, O.widen(X, "bf16"), O.widen(W, "bf16"), cfg.K, tol=TOL, where="flat")
+    PP.log_case("lmhead all logits equal", rep, rows=rows)
+
+
+@pytest.mark.parametrize("period", [97, 1009])
+def test_lmhead_periodic_head_rows(period):
+    """Head rows repeating with a period: each logit value recurs V / period
+    times, spread over every slab, so the keys that reach the pruning bound
+    are many bit-equal logits across slabs, ranked by token id."""
+    cfg = I.small_variant("qwen3_4b", name=f"lmhead_period{period}", n_req=1, L=4, V=151936, D=512, K=64)
+    W = I.make_lmhead(cfg, 6)
+    W = W[np.arange(cfg.V) % period].copy()
+    X = I.make_lmhead_states(cfg, W, 6, 0)
+    rows = cfg.n_req * cfg.L
+    ids, vals = run_lmhead(cfg, X, W)
+    rep = CK.check_lmhead_topk(ids, vals, O.widen(X.reshape(rows, cfg.D), "bf16"), O.widen(W, "bf16"), cfg.K,
+                               tol=TOL, where=f"period{period}")
+    PP.log_case(f"lmhead periodic head rows {period}", rep, rows=rows)
