@@ -225,7 +225,8 @@ def main():
                       "hbm_frac": round(gbs / HBM_PEAK, 5), "alg_flops": alg[k]["flops"]}
     dom = max(kernels, key=lambda k: kernels[k]["us"])
     traffic = measured_traffic(cfg.name)
-    roofline = tree_issue_roofline(cfg, kernels, traffic) if dom == "tree_kernel" else None
+    cu_read = measure_cu_read_peak()
+    roofline = tree_issue_roofline(cfg, kernels, traffic, cu_read) if dom == "tree_kernel" else None
     if roofline is None:
         dk = kernels[dom]
         roofline = {"kernel": dom, "bound": "hbm", "achieved": dk["GB_s"], "peak": HBM_PEAK, "unit": "GB/s",
@@ -297,6 +298,7 @@ def main():
         "roofline": roofline,
         "roofline_scan": roofline_scan,
         "read_peak": read_peak,
+        "cu_read_peak": cu_read,
         "roofline_scan_stress": scan_stress,
         "roofline_head_stress": head_stress,
         "serial_heap": serial,
@@ -614,6 +616,32 @@ def measure_read_peak(gib=2, n_timed=10):
             "probe": "dartree_stream_read: one read-only pass, 16-byte loads, 256 x 512 threads"}
 
 
+def measure_cu_read_peak(mib=8, n_timed=10):
+    """The rate one CU pulls from the memory system: dartree_cu_read (one
+    workgroup of 1024 threads, 16-byte loads) over an 8 MiB buffer, timed
+    with torch events around n_timed passes."""
+    import torch
+
+    from diffusion_drafter_tree_amd import ops
+
+    buf = torch.ones((mib << 20) // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        ops.cu_read(buf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n_timed):
+        ops.cu_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / n_timed
+    nbytes = buf.numel() * 4
+    del buf
+    return {"GB_s": round(nbytes / (us * 1e-6) / 1e9, 2), "bytes": nbytes, "us": round(us, 2),
+            "probe": "dartree_cu_read: one read-only pass by one workgroup of 1024 threads, 16-byte loads"}
+
+
 ISSUE_SOURCES = KERNEL_SOURCES
 
 
@@ -640,14 +668,16 @@ def measured_issue(cfg_name):
     return rec["tree_kernel"]
 
 
-def tree_issue_roofline(cfg, kernels, traffic):
+def tree_issue_roofline(cfg, kernels, traffic, cu_read=None):
     """The tree kernel against its issue bound. One request's whole round
     (16 dependent depths) runs in one workgroup on one CU, so the CUs a
     launch occupies are n_req; each issues at most one wave64 VALU
     instruction a cycle (four 16-lane SIMDs, four cycles an instruction) at
     2.4 GHz. achieved = the launch's VALU instructions (rocprofv3
     SQ_INSTS_VALU, from the committed counter summary) / its measured time.
-    frac_chip relates the same rate to all 256 CUs."""
+    frac_chip relates the same rate to all 256 CUs. pull: the second bound of
+    a one-workgroup kernel, the bytes it moves (algorithmic, and counted)
+    against the rate one CU reads at (dartree_cu_read)."""
     rec = measured_issue(cfg.name)
     if rec is None:
         return None
@@ -661,7 +691,26 @@ def tree_issue_roofline(cfg, kernels, traffic):
             "valu_per_launch": rec["valu_per_launch"], "mfma_per_launch": rec.get("mfma_per_launch"),
             "hbm_frac": kernels["tree_kernel"]["hbm_frac"], "traffic": traffic.get("tree_kernel"),
             "model": "issue: one request's dependent depths run on one CU; peak = one VALU wave64 instruction "
-                     "a cycle per CU at 2.4 GHz"}
+                     "a cycle per CU at 2.4 GHz",
+            "pull": tree_pull_bound(cfg, kernels, traffic, cu_read)}
+
+
+def tree_pull_bound(cfg, kernels, traffic, cu_read):
+    """Bytes a launch moves per microsecond against what its CUs can pull
+    (one CU a request, each at the measured dartree_cu_read rate)."""
+    if not cu_read:
+        return None
+    us = kernels["tree_kernel"]["us"]
+    peak = cu_read["GB_s"] * cfg.n_req
+    alg = kernels["tree_kernel"]["alg_bytes"] / (us * 1e-6) / 1e9
+    out = {"cu_read_GB_s": cu_read["GB_s"], "cus": cfg.n_req, "peak_GB_s": round(peak, 2),
+           "alg_GB_s": round(alg, 2), "alg_frac": round(alg / peak, 4)}
+    t = traffic.get("tree_kernel")
+    if t:
+        tb = t["read"] + t["written"] if isinstance(t, dict) else t
+        out["traffic_GB_s"] = round(tb / (us * 1e-6) / 1e9, 2)
+        out["traffic_frac"] = round(out["traffic_GB_s"] / peak, 4)
+    return out
 
 
 def other_config_round(name, hbm_peak, read_peak, steps=256, warmup=16, G=16):

@@ -77,6 +77,7 @@ SIGNATURES = {
     "dartree_lmhead_workspace_size": (c_int32, [PD, POINTER(c_size_t)]),
     "dartree_lmhead_topk": (c_int32, [PD, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "dartree_stream_read": (c_int32, [c_void_p, c_size_t, c_void_p, c_void_p]),
+    "dartree_cu_read": (c_int32, [c_void_p, c_size_t, c_void_p, c_void_p]),
     "dartree_set_stage_events": (c_int32, [POINTER(c_void_p), c_int32]),
     "dartree_set_split_wait": (c_int32, [c_int32]),
     "dartree_serial_workspace_size": (c_int32, [PD, POINTER(c_size_t)]),

@@ -10,6 +10,13 @@
 
 #include "../../include/dartree.h"
 #include "kernels.h"
+
+namespace dartree {
+// measurement utility (lmhead.hip, beside the HBM read probe): one read of
+// bytes (a multiple of 16) at buf by a single workgroup
+hipError_t launch_cu_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
+}  // namespace dartree
+
 #include "api_internal.h"
 
 namespace {
@@ -337,6 +344,16 @@ dartree_status dartree_stream_read(const void* buf, size_t bytes, uint32_t* sink
   if (bytes == 0 || bytes % 16 != 0) return fail(DARTREE_ERR_INVALID_ARGUMENT, "bytes=%zu: a positive multiple of 16", bytes);
   hipError_t e = dartree::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "stream read launch");
+  return DARTREE_OK;
+}
+
+dartree_status dartree_cu_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  g_err[0] = 0;
+  REQ_PTR(buf, 16);
+  REQ_PTR(sink, 4);
+  if (bytes == 0 || bytes % 16 != 0) return fail(DARTREE_ERR_INVALID_ARGUMENT, "bytes=%zu: a positive multiple of 16", bytes);
+  hipError_t e = dartree::launch_cu_read(buf, bytes, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cu read launch");
   return DARTREE_OK;
 }
 

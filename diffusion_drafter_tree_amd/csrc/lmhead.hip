@@ -362,7 +362,34 @@ __global__ __launch_bounds__(512) void stream_read_kernel(const u32x4_t* __restr
   if (acc == 0x9E3779B9u && threadIdx.x == 0x3FF) sink[0] = acc;
 }
 
+// Measurement utility (not a step of the method): one workgroup of 1024
+// threads reads n 16-byte vectors once, eight loads in flight a thread: the
+// rate at which one CU pulls data from the memory system, the bound of a
+// kernel that runs a request's whole round in one workgroup.
+__global__ __launch_bounds__(1024) void cu_read_kernel(const u32x4_t* __restrict__ p, size_t n, uint32_t* sink) {
+  constexpr size_t T = 1024;
+  size_t i = threadIdx.x;
+  uint32_t acc = 0u;
+  for (; i + 7 * T < n; i += 8 * T) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[i + u * T];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n; i += T) {
+    const u32x4_t v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u && threadIdx.x == 0x3FF) sink[0] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_cu_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s) {
+  hipLaunchKernelGGL(cu_read_kernel, dim3(1), dim3(1024), 0, s, static_cast<const u32x4_t*>(buf), bytes / 16, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s) {
   hipLaunchKernelGGL(stream_read_kernel, dim3(256), dim3(512), 0, s, static_cast<const u32x4_t*>(buf), bytes / 16,

@@ -314,3 +314,9 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
     nbytes = (buf.numel() * buf.element_size()) // 16 * 16
     _check(C.load().dartree_stream_read(_p(buf), nbytes, _p(sink), _stream(stream)), "stream_read")
 
+
+
+def cu_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Measurement utility: the same read by one workgroup (dartree_cu_read)."""
+    nbytes = (buf.numel() * buf.element_size()) // 16 * 16
+    _check(C.load().dartree_cu_read(_p(buf), nbytes, _p(sink), _stream(stream)), "cu_read")

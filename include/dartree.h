@@ -365,6 +365,13 @@ dartree_status dartree_verify_tree(const dartree_dims* dims, const int32_t* n_se
  * with. sink is a device word the kernel may write (never in practice). */
 dartree_status dartree_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/* Measurement utility (not part of a round's computation): the same read as
+ * dartree_stream_read by a single workgroup of 1024 threads, eight 16-byte
+ * loads in flight a thread: the rate one CU pulls from the memory system,
+ * which bounds the block-decoding tree kernel (one workgroup a request).
+ * Same arguments and errors as dartree_stream_read. */
+dartree_status dartree_cu_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Profiling hook (not part of a round's computation). When set, every
  * following dartree_build_round on this thread records events[0] before its
  * first launch, events[1] after the logits scan (with the head tiles),
