@@ -132,6 +132,55 @@ def test_step_entry_points_match_fused_round(name):
         assert np.array_equal(a[k], c[k]), k
 
 
+@pytest.mark.parametrize("name", ["fast_K64_W12_L6", "fast_K16_W16_L31_B100", "bf16_ragged_odd_V"])
+def test_select_on_stored_levels_out_of_order(name):
+    """select_topB on a supertree whose stored levels are not in the order the
+    expansion writes them (each level's filled slots permuted, the next
+    level's parent slots remapped to match). The top-B ranking compares every
+    node's key with every other, so it must not depend on slot order: the
+    tree must be the same, with each emitted slot mapped through the
+    permutation."""
+    cfg = SMALL[name].with_(name=name)
+    hd, dhd = device_head(cfg)
+    rnd = I.make_round(cfg, 0, 0)
+    say(f"case {name}: select on permuted levels")
+    rb = ops.RoundBuffers(cfg)
+    ops.build_round(rb.dims, dhd, ops.to_device(rnd.logits), ops.to_device(rnd.H if cfg.D > 0 else rnd.h), rb)
+    torch.cuda.synchronize()
+    ref = rb.numpy()
+    n, L, W = cfg.n_req, cfg.L, cfg.W
+    cnt = ref["st_count"]
+    arrs = {k: ref[k].copy() for k in ("st_tok", "st_parent", "st_cum", "st_sbeta")}
+    rng = np.random.default_rng(11)
+    new_of_old = np.tile(np.arange(W), (n, L, 1))
+    moved = 0
+    for q in range(n):
+        for d in range(L):
+            c = int(cnt[q, d])
+            perm = np.arange(W)
+            perm[:c] = rng.permutation(c)   # new slot j holds old slot perm[j]
+            moved += int((perm[:c] != np.arange(c)).sum())
+            for a in arrs.values():
+                a[q, d] = a[q, d][perm]
+            new_of_old[q, d][perm] = np.arange(W)
+    for q in range(n):
+        for d in range(1, L):
+            c = int(cnt[q, d])
+            arrs["st_parent"][q, d, :c] = new_of_old[q, d - 1][arrs["st_parent"][q, d, :c]]
+    assert moved > 0
+    for k, a in arrs.items():
+        getattr(rb, k).copy_(torch.from_numpy(a))
+    ops.select_topB(rb.dims, rb)
+    torch.cuda.synchronize()
+    out = rb.numpy()
+    for k in ("n_sel", "tok", "depth", "parent", "score"):
+        assert np.array_equal(out[k], ref[k]), k
+    for q in range(n):
+        for e in range(int(ref["n_sel"][q])):
+            d, sl = int(ref["depth"][q, e]), int(ref["slot"][q, e])
+            assert out["slot"][q, e] == new_of_old[q, d - 1][sl]
+
+
 SPLIT_EXTRA = {
     # W (K + r) near the 16384 limit with parts' block ranges that round up:
     # more exchanged vectors than three a thread
