@@ -117,6 +117,21 @@ def test_null_and_misaligned_pointers_rejected_before_any_launch(lib):
     assert lib.dartree_tree_mask(ctypes.byref(d), fake, fake, ctypes.c_void_p(0x10004), s) == C.ERR_INVALID_ARGUMENT
 
 
+def test_read_probes_validate_on_host(lib):
+    """The two measurement utilities reject NULL or misaligned buffers and byte
+    counts that are zero or not a multiple of 16 before any launch."""
+    fake = ctypes.c_void_p(0x10000)      # never dereferenced: validation fails first
+    s = ctypes.c_void_p(None)
+    for fn in (lib.dartree_stream_read, lib.dartree_cu_read):
+        assert fn(None, 1024, fake, s) == C.ERR_INVALID_ARGUMENT
+        assert fn(ctypes.c_void_p(0x10008), 1024, fake, s) == C.ERR_INVALID_ARGUMENT
+        assert "aligned" in C.last_error()
+        assert fn(fake, 1024, None, s) == C.ERR_INVALID_ARGUMENT
+        for nbytes in (0, 15, 1000):
+            assert fn(fake, nbytes, fake, s) == C.ERR_INVALID_ARGUMENT
+            assert "multiple of 16" in C.last_error()
+
+
 def test_expand_depth_order_is_enforced(lib):
     d = dims()
     fake = 0x10000
