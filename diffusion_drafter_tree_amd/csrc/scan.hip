@@ -192,14 +192,18 @@ __device__ void rank_select(ScanSmem& sm, int ns, int K) {
 // in the slice: slices are shorter than 65,536 elements, so the keys are
 // distinct and in the same order as the 64-bit ones). A group of G threads
 // ranks two survivors (x and x + ceil(ns / 2)) against one segment of the
-// keys, read 32 at a time and all in flight at once; keys past ns are zero,
-// so segments are read in whole steps. The output is the 64-bit form.
+// keys, read eight at a time (the segments are as short as the group
+// allows: every lane of a wave pays for its busiest lane's compares); keys
+// past ns are zero, so segments are read in whole steps. The output is the
+// 64-bit form.
+static_assert(kT * 8 * kMaxNV <= 65536 && kWideT * 8 * kMaxNV <= 65536,
+              "a bf16 slice must fit the 16-bit offset of its 32-bit survivor keys");
 __device__ void rank_select32(ScanSmem& sm, int ns, int K, int s0) {
   const int tid = threadIdx.x;
   const int ng = (ns + 1) >> 1;
   int G = 16;
   while (G > 1 && ng * G > kT) G >>= 1;
-  const int per = (((ns + G - 1) / G) + 31) & ~31;   // multiple of 32
+  const int per = (((ns + G - 1) / G) + 7) & ~7;   // multiple of 8
   auto out64 = [&](uint32_t k) {
     const uint32_t idx = (uint32_t)s0 + 0xFFFFu - (k & 0xFFFFu);
     return ((uint64_t)(k >> 16) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
@@ -212,12 +216,12 @@ __device__ void rank_select32(ScanSmem& sm, int ns, int K, int s0) {
       ka = sm.key32[g];
       kb = sm.key32[xb];   // xb <= ns: the zero pad when ns is odd (unused)
       const int y1 = min(ns, (seg + 1) * per);
-      for (int y = seg * per; y < y1; y += 32) {
-        u32x4_t k4[8];
+      for (int y = seg * per; y < y1; y += 8) {
+        u32x4_t k4[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) k4[e] = *reinterpret_cast<const u32x4_t*>(&sm.key32[y + 4 * e]);
+        for (int e = 0; e < 2; ++e) k4[e] = *reinterpret_cast<const u32x4_t*>(&sm.key32[y + 4 * e]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 2; ++e) {
           ca += (k4[e].x > ka ? 1u : 0u) + (k4[e].y > ka ? 1u : 0u) + (k4[e].z > ka ? 1u : 0u) + (k4[e].w > ka ? 1u : 0u);
           cb += (k4[e].x > kb ? 1u : 0u) + (k4[e].y > kb ? 1u : 0u) + (k4[e].z > kb ? 1u : 0u) + (k4[e].w > kb ? 1u : 0u);
         }
@@ -558,7 +562,7 @@ __device__ void scan_block(const ScanArgs& a, Smem& sm, int blk, const u32x4_t (
     ns = sm.misc[3];
     if constexpr (BF16) {
       // keys of the overflowed pass may remain past ns: the ranking reads up
-      // to 32 keys beyond ns and needs zeros there
+      // to 7 keys beyond ns and needs zeros there
       if (tid < 32) sm.key32[ns + tid] = 0u;
       __syncthreads();
     }
@@ -635,11 +639,12 @@ __device__ void head_block(const ScanArgs& a, HeadSmem& sm, int tile) {
   const int nt = tile % ntn, mt = tile / ntn;
   const int KS = a.D / 32;
   const int k0 = (KS * w) / kWaves, k1 = (KS * (w + 1)) / kWaves;
-  const int m = mt * 16 + (lane & 15);
-  const int n = nt * 16 + (lane & 15);
-  const int sub = (lane >> 4) * 8;
-  const uint16_t* hrow = a.H + (size_t)(m < a.M ? m : 0) * a.D + sub;
-  const uint16_t* prow = a.Pt + (size_t)n * a.D + sub;
+  const int m = mt * 16 + (lane & 15);   // this lane's operand row of H
+  // rows read coalesced (four adjacent lanes on one 64-byte segment), then
+  // permuted to the operand lanes
+  const int mc = mt * 16 + coal_row(lane), nc = nt * 16 + coal_row(lane);
+  const uint16_t* hrow = a.H + (size_t)(mc < a.M ? mc : 0) * a.D + coal_col(lane);
+  const uint16_t* prow = a.Pt + (size_t)nc * a.D + coal_col(lane);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   for (int kb = k0; kb < k1; kb += G) {
     u16x8_t av[G], bv[G];
@@ -653,8 +658,9 @@ __device__ void head_block(const ScanArgs& a, HeadSmem& sm, int tile) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       if (kb + g < k1) {
-        if (m >= a.M) av[g] = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        acc = mfma_bf16(av[g], bv[g], acc);
+        u16x8_t x = to_mfma_lanes(av[g], lane);
+        if (m >= a.M) x = u16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        acc = mfma_bf16(x, to_mfma_lanes(bv[g], lane), acc);
       }
     }
   }
