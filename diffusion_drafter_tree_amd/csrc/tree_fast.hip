@@ -28,7 +28,8 @@
 //       same state fragments (A resident in registers).
 //   P2  one wave per parent: log-softmax over its K candidates, cum, s_beta,
 //       64-bit keys; the slot-0 parent's wave sorts its high words and takes
-//       the W-th as the bound T (its W best children alone reach T); the
+//       the W-th as the bound T (its W best children alone reach T), and the
+//       least of the parents' best children is a second bound; the
 //       previous level's path ranks; the rest of A S^T.
 //   P3a keys with high word >= T compacted into LDS.
 //   P3b survivors ranked by counting; the W smallest ranks are the level, in
@@ -131,7 +132,7 @@ struct FLay {
   LDS float* cumK;     // [16][KC]
   LDS uint64_t* sk;    // [kSkCap + 4] survivor keys
   LDS uint64_t* win;   // [16] the depth's survivors by rank
-  LDS int* misc;       // [32]: bounds and survivor counts by depth parity; 16..31 level keys
+  LDS int* misc;       // [32]: by depth parity, bounds (0, 1 and 4, 5) and survivor counts (2, 3); 16..31 level keys
   LDS int* cid;        // [L][KC]
   LDS float* clog;     // [L][KC]
   LDS int* lv_tok;     // [L][W]
@@ -559,6 +560,15 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       if (v) s.cumK[p * KC + lane] = cum;
       kh = v ? f32_key(cum + bd) : 0u;
       kl = v ? ~(((uint32_t)tok << 10) | ((uint32_t)p << 6) | (uint32_t)lane) : 0u;
+      if (Wp >= Wq && lane == 0) {
+        // Second bound: with at least Wq parents, each parent's best child is
+        // a distinct key, so the least of those reaches the Wq-th largest.
+        // The best child's key is this parent's maximum logit through the
+        // same operations as the lanes' keys; the least is taken by an LDS
+        // maximum of complements (the slot starts at 0 every depth).
+        const uint32_t kmax = f32_key((cp + fminf(m - lse, 0.f)) + bd);
+        lds_max((LDS unsigned*)&s.misc[4 + par], ~kmax);
+      }
       if (p == 0) {
         // Bound T: the W-th largest high word among the children of the
         // level's first parent (the one with the best score, its W best
@@ -590,7 +600,8 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
 
     // P3: survivors (high word >= T) compacted, then ranked by counting
     if (w < Wp) {
-      const uint32_t T = (uint32_t)s.misc[par];
+      // the larger of the two bounds (both at most the Wq-th largest key)
+      const uint32_t T = max((uint32_t)s.misc[par], Wp >= Wq ? ~(uint32_t)s.misc[4 + par] : 0u);
       const bool sv = lane < KC && kh >= T;
       const uint64_t bal = __ballot(sv);
       int base = 0;
@@ -602,14 +613,14 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
     lds_sync();
     const int nk = min(Wq, Wp * KC);
     {
-      // G = 2^lg threads per survivor (up to 16), as many as eight waves hold:
-      // every instruction a wave executes takes its SIMD's issue cycles, so a
-      // few busy waves (two per SIMD) rank faster than all sixteen. Ranking
-      // threads start at wave 4 (wave 0 finishes its A*S meanwhile); past 768
-      // survivors they wrap around to waves 0..3.
+      // G = 2^lg threads per survivor (up to 16), as many as waves 4..15 hold
+      // (wave 0 finishes its A*S meanwhile); past 768 survivors they wrap
+      // around to waves 0..3. A thread's compares are a chain of dependent
+      // LDS reads, so the more threads share a survivor the shorter the
+      // phase: capped at eight waves the launch took 1.45 us longer.
       const int ns = min(__builtin_amdgcn_readfirstlane(s.misc[2 + par]), kSkCap);
       int lg = 4;
-      while (lg > 0 && (ns << lg) > 8 * kWave) --lg;
+      while (lg > 0 && (ns << lg) > 12 * kWave) --lg;
       const int G = 1 << lg;
       const int per = (ns + G - 1) >> lg;
       const int rt = (tid + kT - 4 * kWave) & (kT - 1);
@@ -641,8 +652,8 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
         s.lv_sb[row] = cum + bd;
       }
       if (tid == 0) s.lv_cnt[d - 1] = nk;
-      // the other parity's bound and count are free again (read one depth ago)
-      if (tid < 2) s.misc[(par ^ 1) + 2 * tid] = 0;
+      // the other parity's bounds and count are free again (read one depth ago)
+      if (tid < 3) s.misc[(par ^ 1) + 2 * tid] = 0;
     }
     if (need_state && !markov && w == 0) as_finish();
     // this depth's staged E/h rows into LDS, then the next depth's first E share
