@@ -454,7 +454,6 @@ __device__ __forceinline__ f32x4_t mfma_bf16(const u16x8_t& a, const u16x8_t& b,
 struct SelSmem {
   LDS uint64_t* key;      // [cap]
   LDS int* pay;           // [cap]
-  LDS int* rank;          // [cap]
   LDS uint64_t* out_key;  // [>= K]
   LDS int* out_pay;       // [>= K]
   LDS int* misc;          // [8]
@@ -548,40 +547,52 @@ __device__ __forceinline__ int select_exact(const uint64_t (&k)[EPT], const int 
 }
 
 // Ranks ns (<= cap) compacted keys and scatters the K largest, descending, to
-// out_key/out_pay; zero-fills out_key[n..K). sm.rank[0..ns) must be zero.
-// Leaves misc zeroed and rank zeroed for the next selection.
+// out_key/out_pay; zero-fills out_key[n..K). Keys are distinct. A key's rank
+// is the number of larger keys, counted by a group of G = 2^lg threads (up to
+// 16, as many as the block holds) over segments of the keys and summed across
+// the group's lanes by DPP; the group's first thread writes the key at its
+// rank. Leaves misc zeroed for the next selection.
 __device__ __forceinline__ int select_rank(int ns, int K, const SelSmem& sm) {
   const int tid = threadIdx.x, nthr = blockDim.x;
   if (ns > 0) {
-    int nseg = nthr / ns;
-    if (nseg < 1) nseg = 1;
-    const int seg = (ns + nseg - 1) / nseg;
-    for (int t = tid; t < ns * nseg; t += nthr) {
-      const int i = t % ns, s = t / ns;
-      const uint64_t x = sm.key[i];
-      const int j0 = s * seg, j1 = min(ns, j0 + seg);
-      int r = 0;
-      for (int j = j0; j < j1; ++j) r += sm.key[j] > x;
-      if (r) lds_add(&sm.rank[i], r);
+    int lg = 4;
+    while (lg > 0 && (ns << lg) > nthr) --lg;
+    const int G = 1 << lg;
+    const int per = (ns + G - 1) >> lg;
+    // passes of nthr threads (more than one only when ns > nthr, G = 1); the
+    // trip count is the block's, so every lane reaches the group sum
+    for (int t0 = 0; t0 < (ns << lg); t0 += nthr) {
+      const int t = t0 + tid;
+      const int x = t >> lg, seg = t & (G - 1);
+      uint64_t kx = 0ull;
+      uint32_t c = 0u;
+      if (x < ns) {
+        kx = sm.key[x];
+        const int y0 = seg * per, y1 = min(ns, y0 + per);
+        int y = y0;
+        for (; y + 4 <= y1; y += 4) {
+          const uint64_t k0 = sm.key[y], k1 = sm.key[y + 1], k2 = sm.key[y + 2], k3 = sm.key[y + 3];
+          c += (k0 > kx ? 1u : 0u) + (k1 > kx ? 1u : 0u) + (k2 > kx ? 1u : 0u) + (k3 > kx ? 1u : 0u);
+        }
+        for (; y < y1; ++y) c += sm.key[y] > kx ? 1u : 0u;
+      }
+      if (G >= 2) c += lane_xor<1>(c);
+      if (G >= 4) c += lane_xor<2>(c);
+      if (G >= 8) c += lane_xor<4>(c);
+      if (G >= 16) c += lane_xor<8>(c);
+      if (x < ns && seg == 0 && (int)c < K) {
+        sm.out_key[c] = kx;
+        sm.out_pay[c] = sm.pay[x];
+      }
     }
   }
-  __syncthreads();
   const int n_out = min(ns, K);
-  for (int i = tid; i < ns; i += nthr) {
-    const int r = sm.rank[i];
-    if (r < K) {
-      sm.out_key[r] = sm.key[i];
-      sm.out_pay[r] = sm.pay[i];
-    }
-    sm.rank[i] = 0;
-  }
   for (int i = n_out + tid; i < K; i += nthr) sm.out_key[i] = 0ull;
   if (tid < 8) sm.misc[tid] = 0;
   __syncthreads();
   return n_out;
 }
 
-// Full selection from register-held keys. sm.rank[0..cap) must be zero.
 template <int EPT>
 __device__ __forceinline__ int block_select(const uint64_t (&k)[EPT], const int (&p)[EPT], int K, int hi_bits, const SelSmem& sm) {
   const int lane = lane_id();

@@ -856,14 +856,12 @@ __global__ __launch_bounds__(kT) void merge_kernel(const uint64_t* __restrict__ 
                                                    int32_t* __restrict__ cand_ids, float* __restrict__ cand_logit) {
   __shared__ uint64_t s_key[kScanCap];
   __shared__ int s_pay[kScanCap];
-  __shared__ int s_rank[kScanCap];
   __shared__ uint64_t s_out[1024];
   __shared__ int s_outp[1024];
   __shared__ int s_misc[8];
   __shared__ int s_hist[256], s_cursor[256], s_base[256], s_hmisc[2];
   const int row = blockIdx.x, tid = threadIdx.x;
   if (tid < 8) s_misc[tid] = 0;
-  for (int i = tid; i < kScanCap; i += kT) s_rank[i] = 0;
   for (int i = tid; i < 256; i += kT) {
     s_hist[i] = 0;
     s_cursor[i] = 0;
@@ -886,7 +884,7 @@ __global__ __launch_bounds__(kT) void merge_kernel(const uint64_t* __restrict__ 
   HistSmem hs{(LDS int*)s_hist, (LDS int*)s_cursor, (LDS int*)s_base, (LDS int*)s_hmisc, (LDS uint64_t*)s_key,
               (LDS uint64_t*)s_out, kScanCap};
   if (!hist_topk<EPT>(k, lo_v, hi_v, K, hs)) {
-    SelSmem sm{(LDS uint64_t*)s_key, (LDS int*)s_pay, (LDS int*)s_rank, (LDS uint64_t*)s_out, (LDS int*)s_outp,
+    SelSmem sm{(LDS uint64_t*)s_key, (LDS int*)s_pay, (LDS uint64_t*)s_out, (LDS int*)s_outp,
                (LDS int*)s_misc, kScanCap};
     block_select<EPT>(k, p, K, bf16 ? 16 : 32, sm);
   }

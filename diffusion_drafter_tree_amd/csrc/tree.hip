@@ -76,7 +76,6 @@ struct Lay {
   LDS float* hb;      // mode 2: [2][r]
   LDS uint64_t* skey; // [kSelCap]
   LDS int* spay;
-  LDS int* srank;
   LDS uint64_t* okey; // [max(W, B)]
   LDS int* opay;
   LDS int* misc;      // [16]
@@ -90,7 +89,7 @@ struct Lay {
 };
 
 struct LayOff {
-  size_t cid, clog, sf, sh, sm, sl, zp, as, cp, tok, ps, lex, k, cum, sb, cnt, ec, hb, sk, sp, sr, ok, op, misc, eidx,
+  size_t cid, clog, sf, sh, sm, sl, zp, as, cp, tok, ps, lex, k, cum, sb, cnt, ec, hb, sk, sp, ok, op, misc, eidx,
       eord, nd, base, epar, mb, ab, total;
 };
 
@@ -132,7 +131,6 @@ __host__ __device__ inline LayOff lay_off(int L, int K, int W, int B, int r, int
   o.hb = mode == 2 ? take(4ul * 2 * r) : 0;
   o.sk = take(8ul * kSelCap);
   o.sp = take(4ul * kSelCap);
-  o.sr = take(4ul * kSelCap);
   o.ok = take(8 * outn);
   o.op = take(4 * outn);
   o.misc = take(4 * 16);
@@ -171,7 +169,6 @@ __device__ __forceinline__ Lay make_lay(const LayOff& o) {
   s.hb = (LDS float*)(b + o.hb);
   s.skey = (LDS uint64_t*)(b + o.sk);
   s.spay = (LDS int*)(b + o.sp);
-  s.srank = (LDS int*)(b + o.sr);
   s.okey = (LDS uint64_t*)(b + o.ok);
   s.opay = (LDS int*)(b + o.op);
   s.misc = (LDS int*)(b + o.misc);
@@ -366,11 +363,10 @@ __global__ __launch_bounds__(kT) void tree_kernel(TreeArgs a, int KQ) {
   const float* hq = a.h + (size_t)q * L * r;
   const int32_t* cid_g = a.cand_ids + (size_t)q * L * K;
   const float* clog_g = a.cand_logit + (size_t)q * L * K;
-  SelSmem sel{s.skey, s.spay, s.srank, s.okey, s.opay, s.misc, kSelCap};
+  SelSmem sel{s.skey, s.spay, s.okey, s.opay, s.misc, kSelCap};
   const bool expand = a.d0 <= a.d1;
 
   if (tid < 16) s.misc[tid] = 0;
-  for (int i = tid; i < kSelCap; i += kT) s.srank[i] = 0;
   for (int d = tid; d < 32; d += kT) s.lv_cnt[d] = d < L ? min(max(a.st_count[(size_t)q * L + d], 0), W) : 0;
   // levels this launch does not expand come from global memory
   for (int i = tid; i < L * W; i += kT) {
