@@ -55,8 +55,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(requests shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(requests would shard across GPUs with no exchange between them)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -98,9 +98,9 @@ def _check_cut(chosen, score_of, tol: float, where: str, what: str):
     """A chosen subset of a pool is a valid top-n under tolerance ``tol`` iff
     no excluded member outscores a chosen one by more than ``tol``:
     min over chosen of the oracle score >= max over excluded - tol. This is
-    the near-tie rule of the benchmark spec's parity bar, applied to both sides
-    of the cut (a set that keeps near-tied nodes but drops a clearly better
-    one is invalid)."""
+    the near-tie rule of the parity bar, applied to both sides of the cut (a
+    set that keeps near-tied nodes but drops a clearly better one is
+    invalid)."""
     lo_key = min(chosen, key=lambda k: score_of[k])
     excluded = [k for k in score_of if k not in chosen]
     if not excluded:
