@@ -583,8 +583,10 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
     }
     if (w == 0) __builtin_amdgcn_s_setprio(0);
     // the level before this one: its path ranks, by a wave without a parent
-    // (the state update of the level, one depth ago, had no spare wave)
+    // (the state update of the level, one depth ago, had no spare wave), at
+    // raised issue priority too: it is the last wave to reach the barrier
     if (a.do_select && a.d0 == 1 && d >= 2 && w == kWaves - 1) {
+      __builtin_amdgcn_s_setprio(2);
       uint32_t tk = 0u;
       int ps = 0;
       if (lane < Wp) {
@@ -595,6 +597,7 @@ __global__ __launch_bounds__(kT) void tree_fast_kernel(TreeArgs a) {
       level_lex_wave(s, d - 1, W, Wp, tk, ps);
     }
     if (need_state && !markov && w != 0) as_finish();
+    if (w == kWaves - 1) __builtin_amdgcn_s_setprio(0);
     load_u1(min(d + 1, a.d1), 0);
     lds_sync();
 
